@@ -1,0 +1,122 @@
+"""Exact softmax attention, O = softmax(s * Q K^T) V, in plain float64 NumPy.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU baseline leg, never by the library or its binding.
+
+What it computes, and where the pages define it:
+  * FastVideo wan22_vae_decode attn.cu, header comment: per latent frame one head
+    of softmax(q k^T / 32) v over the H*W positions, C channels, no mask; and
+    stage 3, the row softmax exp(S * scale - max) / sum.
+  * same page, row_softmax_kernel: scale the row, take its max, exponentiate the
+    difference, sum, multiply by the reciprocal of the sum.
+  * cuDNN native_sparse_attention fmha.py (Blackwell FMHA example), module
+    docstring and softmax_step: Q*K^T, a numerically stable softmax (row max
+    subtracted before the exponential, then normalised by the row sum), times V,
+    with an optional causal mask that removes keys after the query.
+
+The method reaches exactly the plain definition (up to rounding order), so this
+oracle is that definition written out, one step per function, in the pages'
+order: logits, mask, row softmax, weighted sum of value rows.  Inputs are the
+exact bf16 values as float64 arrays; the result is float64 and never rounded.
+
+Readings where the pages leave a step open (each listed in the design notes):
+  * the scale is the caller's, applied to the logits before the row max (the
+    attn.cu softmax scales the row first); any finite value, including 0 and
+    negative values, is allowed;
+  * causal means key j is allowed for query i iff j <= i (square attention, so
+    top-left and bottom-right alignment coincide);
+  * a row with every key masked cannot occur (the diagonal is always allowed);
+    the oracle asserts it rather than inventing an output.
+
+Pins (tests/test_oracle.py): brute-force loops with math.fsum on tiny inputs,
+closed forms (constant V, equal keys, causal row 0, scale 0, L = 1, a one-hot
+limit with huge logits, a hand-worked example in tests/golden), invariants
+(rows of P sum to 1, key-shift invariance, permutation equivariance, linearity
+in V) and a cross-check against torch's CPU float64 attention.  No function
+here is unpinned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def logits(Q: np.ndarray, K: np.ndarray, scale: float) -> np.ndarray:
+    """Z = s * Q K^T for one head: Q [n, d], K [L, d] -> Z [n, L]."""
+    return float(scale) * (Q @ K.T)
+
+
+def causal_mask(Z: np.ndarray, query_index: np.ndarray) -> np.ndarray:
+    """Set Z[r, j] = -inf where key j comes after the query at position query_index[r]."""
+    Z = Z.copy()
+    keys = np.arange(Z.shape[1])
+    Z[keys[None, :] > np.asarray(query_index)[:, None]] = -np.inf
+    return Z
+
+
+def softmax_rows(Z: np.ndarray) -> np.ndarray:
+    """Numerically stable row softmax: exp(Z - rowmax) / rowsum."""
+    m = Z.max(axis=1, keepdims=True)
+    assert np.all(np.isfinite(m)), "a row with every key masked"
+    E = np.exp(Z - m)
+    return E / E.sum(axis=1, keepdims=True)
+
+
+def weighted_values(P: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """O = P V: each output row is the P-weighted sum of the value rows."""
+    return P @ V
+
+
+def _head(x, b: int, h: int) -> np.ndarray:
+    """One (batch, head) slice as float64 (exact for bf16 or float32 inputs)."""
+    return np.asarray(x[b, h], dtype=np.float64)
+
+
+def _dims(q, k, v):
+    if not (len(np.shape(q)) == 4 and np.shape(q) == np.shape(k)
+            and np.shape(k)[:3] == np.shape(v)[:3]):
+        raise ValueError("q, k, v must be [B, H, L, d] sharing B, H, L (q, k share d)")
+    return np.shape(q)[:3]
+
+
+def probabilities(q, k, scale: float, causal: bool = False) -> np.ndarray:
+    """P = softmax(s * Q K^T) (masked when causal), shape [B, H, L, L]."""
+    B, H, L = _dims(q, k, k)
+    P = np.empty((B, H, L, L), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            Z = logits(_head(q, b, h), _head(k, b, h), scale)
+            if causal:
+                Z = causal_mask(Z, np.arange(L))
+            P[b, h] = softmax_rows(Z)
+    return P
+
+
+def attention(q, k, v, scale: float, causal: bool = False) -> np.ndarray:
+    """O = softmax(s * Q K^T) V for every (batch, head); float64 [B, H, L, d]."""
+    B, H, L = _dims(q, k, v)
+    O = np.empty(tuple(np.shape(v)), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            Z = logits(_head(q, b, h), _head(k, b, h), scale)
+            if causal:
+                Z = causal_mask(Z, np.arange(L))
+            O[b, h] = weighted_values(softmax_rows(Z), _head(v, b, h))
+    return O
+
+
+def attention_rows(q, k, v, scale: float, causal: bool, rows) -> np.ndarray:
+    """The same definition evaluated only at the output rows listed in ``rows``.
+
+    ``rows`` is a sequence of (b, h, i); returns float64 [len(rows), d].  Used to
+    check full-size runs on a sample of rows the oracle can afford one by one.
+    """
+    out = np.empty((len(rows), np.shape(v)[-1]), dtype=np.float64)
+    for r, (b, h, i) in enumerate(rows):
+        Q = np.asarray(q[b, h, i : i + 1], dtype=np.float64)
+        K = np.asarray(k[b, h], dtype=np.float64)
+        V = np.asarray(v[b, h], dtype=np.float64)
+        Z = logits(Q, K, scale)
+        if causal:
+            Z = causal_mask(Z, np.array([i]))
+        out[r] = weighted_values(softmax_rows(Z), V)[0]
+    return out

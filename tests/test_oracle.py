@@ -1,0 +1,274 @@
+"""Pins for the CPU float64 oracle, independent of the oracle itself.
+
+Each test fixes the oracle against something the pages or the mathematics
+determine: brute-force loops with math.fsum on tiny inputs, closed forms,
+invariants, hand-derived worked examples (tests/golden) and torch's CPU float64
+attention as a library special case.  The mutation tests at the end plant a
+plausible mistake in one oracle step at a time and check that these pins catch
+it.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.exact as oa
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+REL = 1e-12
+
+
+def brute_force(q, k, v, scale, causal):
+    """softmax(s q k^T) v with scalar loops and math.fsum (exactly rounded sums)."""
+    B, H, L, d = q.shape
+    dv = v.shape[-1]
+    out = np.zeros((B, H, L, dv))
+    for b in range(B):
+        for h in range(H):
+            for i in range(L):
+                keys = range(i + 1) if causal else range(L)
+                z = [scale * math.fsum(q[b, h, i, c] * k[b, h, j, c] for c in range(d)) for j in keys]
+                m = max(z)
+                e = [math.exp(x - m) for x in z]
+                tot = math.fsum(e)
+                for c in range(dv):
+                    out[b, h, i, c] = math.fsum(e[jj] * v[b, h, j, c] for jj, j in enumerate(keys)) / tot
+    return out
+
+
+def rnd(shape, seed, s=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * s
+
+
+def close(a, b, rel=REL):
+    a, b = np.asarray(a), np.asarray(b)
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    return float(np.max(np.abs(a - b))) <= rel * scale
+
+
+TINY = [
+    (1, 1, 1, 1, 0.5, False),
+    (1, 1, 5, 3, 0.7, False),
+    (2, 2, 7, 4, 0.5, True),
+    (1, 3, 9, 8, 1 / math.sqrt(8), False),
+    (2, 1, 9, 8, 1 / math.sqrt(8), True),
+    (1, 1, 6, 2, 0.0, True),
+    (1, 2, 8, 5, -1.3, False),
+    (1, 1, 9, 8, 3.0, True),
+]
+
+
+@pytest.mark.parametrize("B,H,L,d,scale,causal", TINY)
+def test_brute_force_tiny(B, H, L, d, scale, causal):
+    q, k, v = rnd((B, H, L, d), 1), rnd((B, H, L, d), 2), rnd((B, H, L, d), 3)
+    assert close(oracle.attention(q, k, v, scale, causal), brute_force(q, k, v, scale, causal))
+
+
+def test_brute_force_value_dim_differs():
+    q, k, v = rnd((1, 2, 6, 4), 4), rnd((1, 2, 6, 4), 5), rnd((1, 2, 6, 3), 6)
+    for causal in (False, True):
+        assert close(oracle.attention(q, k, v, 0.4, causal), brute_force(q, k, v, 0.4, causal))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_match_full(causal):
+    q, k, v = rnd((2, 2, 13, 8), 7), rnd((2, 2, 13, 8), 8), rnd((2, 2, 13, 8), 9)
+    full = oracle.attention(q, k, v, 0.3, causal)
+    rows = [(0, 0, 0), (1, 1, 12), (0, 1, 6), (1, 0, 3)]
+    got = oracle.attention_rows(q, k, v, 0.3, causal, rows)
+    want = np.stack([full[b, h, i] for b, h, i in rows])
+    assert close(got, want, 1e-14)
+    # and against the brute force, independently of attention()
+    bf = brute_force(q, k, v, 0.3, causal)
+    assert close(got, np.stack([bf[b, h, i] for b, h, i in rows]))
+
+
+def test_golden_worked_examples():
+    doc = json.load(open(GOLDEN))
+    assert len(doc["cases"]) >= 5
+    for case in doc["cases"]:
+        got = oracle.attention(np.array(case["q"]), np.array(case["k"]), np.array(case["v"]),
+                               case["scale"], case["causal"])
+        assert close(got, np.array(case["expected"]), 1e-14), case["name"]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_torch_cpu_float64_sdpa(causal):
+    q, k, v = rnd((2, 3, 33, 16), 10), rnd((2, 3, 33, 16), 11), rnd((2, 3, 33, 16), 12)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), scale=0.37, is_causal=causal
+    ).numpy()
+    assert close(oracle.attention(q, k, v, 0.37, causal), ref)
+
+
+# ---- closed forms ---------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v_gives_v(causal):
+    q, k = rnd((2, 2, 11, 6), 13, 3.0), rnd((2, 2, 11, 6), 14, 3.0)
+    row = rnd((6,), 15)
+    v = np.broadcast_to(row, (2, 2, 11, 6)).copy()
+    assert close(oracle.attention(q, k, v, 0.5, causal), v)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_equal_keys_give_mean_or_prefix_mean(causal):
+    q = rnd((1, 2, 10, 5), 16)
+    k = np.broadcast_to(rnd((5,), 17), (1, 2, 10, 5)).copy()
+    v = rnd((1, 2, 10, 5), 18)
+    o = oracle.attention(q, k, v, 0.9, causal)
+    if causal:
+        want = np.cumsum(v, axis=2) / np.arange(1, 11)[None, None, :, None]
+    else:
+        want = np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+    assert close(o, want)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_scale_zero_is_uniform(causal):
+    q, k, v = rnd((1, 1, 12, 4), 19, 50.0), rnd((1, 1, 12, 4), 20, 50.0), rnd((1, 1, 12, 4), 21)
+    o = oracle.attention(q, k, v, 0.0, causal)
+    if causal:
+        want = np.cumsum(v, axis=2) / np.arange(1, 13)[None, None, :, None]
+    else:
+        want = np.broadcast_to(v.mean(axis=2, keepdims=True), v.shape)
+    assert close(o, want)
+
+
+def test_causal_row0_is_v0():
+    q, k, v = rnd((2, 2, 9, 4), 22, 4.0), rnd((2, 2, 9, 4), 23, 4.0), rnd((2, 2, 9, 4), 24)
+    o = oracle.attention(q, k, v, 1.0, True)
+    assert np.array_equal(o[:, :, 0], v[:, :, 0])
+
+
+def test_single_position_is_v():
+    q, k, v = rnd((3, 2, 1, 8), 25), rnd((3, 2, 1, 8), 26), rnd((3, 2, 1, 8), 27)
+    for causal in (False, True):
+        assert np.array_equal(oracle.attention(q, k, v, 0.7, causal), v)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_huge_logits_select_argmax(causal):
+    """Logit gaps of >= 1000 make the softmax one-hot in float64 (exp(-1000) == 0).
+
+    A version that exponentiates before subtracting the row max overflows here.
+    """
+    L, d = 6, 6
+    k = 40.0 * np.eye(L, d)[None, None]                      # k_j = 40 e_j
+    target = np.array([0, 0, 2, 1, 4, 3])                    # the key each query aligns with
+    q = (40.0 * np.eye(d)[target])[None, None]               # q_i = 40 e_target(i)
+    v = rnd((1, 1, L, d), 28)
+    o = oracle.attention(q, k, v, 1.0, causal)               # logits 1600 vs 0
+    assert np.array_equal(o[0, 0], v[0, 0, target])
+
+
+# ---- invariants -------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows(causal):
+    q, k = rnd((2, 2, 17, 8), 29, 2.0), rnd((2, 2, 17, 8), 30, 2.0)
+    P = oracle.probabilities(q, k, 0.6, causal)
+    assert np.all(P >= 0)
+    assert np.max(np.abs(P.sum(-1) - 1.0)) <= 1e-12
+    if causal:
+        assert np.all(np.triu(P[0, 0], 1) == 0)
+        assert np.all(np.diagonal(P, axis1=2, axis2=3) > 0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_shift_invariance(causal):
+    """Adding one vector to every key adds a per-query constant to each logit row."""
+    q, k, v = rnd((1, 2, 14, 6), 31), rnd((1, 2, 14, 6), 32), rnd((1, 2, 14, 6), 33)
+    c = rnd((6,), 34, 3.0)
+    assert close(oracle.attention(q, k + c, v, 0.8, causal), oracle.attention(q, k, v, 0.8, causal), 1e-11)
+
+
+def test_permutation_equivariance():
+    q, k, v = rnd((1, 1, 15, 7), 35), rnd((1, 1, 15, 7), 36), rnd((1, 1, 15, 7), 37)
+    perm = np.random.default_rng(38).permutation(15)
+    o = oracle.attention(q, k, v, 0.5)
+    assert close(oracle.attention(q, k[:, :, perm], v[:, :, perm], 0.5), o)
+    assert close(oracle.attention(q[:, :, perm], k, v, 0.5), o[:, :, perm])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_linear_in_v(causal):
+    q, k = rnd((1, 2, 10, 4), 39), rnd((1, 2, 10, 4), 40)
+    v1, v2 = rnd((1, 2, 10, 4), 41), rnd((1, 2, 10, 4), 42)
+    lhs = oracle.attention(q, k, 2.5 * v1 - 0.75 * v2, 0.5, causal)
+    rhs = 2.5 * oracle.attention(q, k, v1, 0.5, causal) - 0.75 * oracle.attention(q, k, v2, 0.5, causal)
+    assert close(lhs, rhs)
+
+
+def test_dimension_errors():
+    with pytest.raises(ValueError):
+        oracle.attention(np.zeros((1, 1, 3, 2)), np.zeros((1, 1, 4, 2)), np.zeros((1, 1, 3, 2)), 1.0)
+
+
+# ---- planted mistakes: the pins above must catch each one -------------------
+
+def _pins_pass():
+    """A compact run of the pins; False if any fails or raises."""
+    try:
+        for B, H, L, d, scale, causal in [(1, 2, 7, 4, 0.5, True), (1, 1, 6, 3, 0.7, False)]:
+            q, k, v = rnd((B, H, L, d), 50), rnd((B, H, L, d), 51), rnd((B, H, L, d), 52)
+            if not close(oracle.attention(q, k, v, scale, causal), brute_force(q, k, v, scale, causal)):
+                return False
+        for case in json.load(open(GOLDEN))["cases"]:
+            got = oracle.attention(np.array(case["q"]), np.array(case["k"]), np.array(case["v"]),
+                                   case["scale"], case["causal"])
+            if not close(got, np.array(case["expected"]), 1e-14):
+                return False
+        L = 6
+        k = 40.0 * np.eye(L)[None, None]
+        t = np.array([0, 0, 2, 1, 4, 3])
+        q = (40.0 * np.eye(L)[t])[None, None]
+        v = rnd((1, 1, L, L), 53)
+        with np.errstate(all="ignore"):
+            o = oracle.attention(q, k, v, 1.0, False)
+        if not np.array_equal(o[0, 0], v[0, 0, t]):
+            return False
+        return True
+    except (AssertionError, ValueError, FloatingPointError):
+        return False
+
+
+def test_pins_pass_unmutated():
+    assert _pins_pass()
+
+
+MUTANTS = {
+    "transposed_logits": ("logits", lambda Q, K, s: float(s) * (K @ Q.T) if Q.shape == K.shape else float(s) * (Q @ K.T)),
+    "scale_dropped": ("logits", lambda Q, K, s: Q @ K.T),
+    "scale_squared": ("logits", lambda Q, K, s: float(s) ** 2 * (Q @ K.T)),
+    "causal_excludes_diagonal": ("causal_mask", lambda Z, qi: _mask_ge(Z, qi)),
+    "causal_one_late": ("causal_mask", lambda Z, qi: _mask_gt(Z, np.asarray(qi) + 1)),
+    "softmax_over_queries": ("softmax_rows", lambda Z: np.exp(Z - Z.max(0, keepdims=True)) / np.exp(Z - Z.max(0, keepdims=True)).sum(0, keepdims=True)),
+    "softmax_unnormalised": ("softmax_rows", lambda Z: np.exp(Z - Z.max(1, keepdims=True))),
+    "softmax_no_max_shift": ("softmax_rows", lambda Z: np.exp(Z) / np.exp(Z).sum(1, keepdims=True)),
+    "softmax_sign_flip": ("softmax_rows", lambda Z: np.exp(-(Z - Z.max(1, keepdims=True))) / np.exp(-(Z - Z.max(1, keepdims=True))).sum(1, keepdims=True)),
+    "values_transposed_weights": ("weighted_values", lambda P, V: P.T @ V),
+}
+
+
+def _mask_gt(Z, qi):
+    Z = Z.copy()
+    Z[np.arange(Z.shape[1])[None, :] > np.asarray(qi)[:, None]] = -np.inf
+    return Z
+
+
+def _mask_ge(Z, qi):
+    Z = Z.copy()
+    Z[np.arange(Z.shape[1])[None, :] >= np.asarray(qi)[:, None]] = -np.inf
+    return Z
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    attr, bad = MUTANTS[name]
+    monkeypatch.setattr(oa, attr, bad)
+    assert not _pins_pass(), f"pins did not catch mutant {name}"

@@ -1,0 +1,254 @@
+// attn_api.cpp -- the C ABI: argument checks, path choice, workspace, timing.
+//
+// The pages' host entry points (FastVideo wan22_vae_decode attn.cu,
+// attn_forward; cuDNN fmha.py, __call__) check shapes and raise; this library
+// returns status codes instead and makes every check before any HIP call, so
+// each error path can be exercised without a GPU.
+#include "../../include/attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+bool head_dim_supported(int64_t d) {
+  return d == 32 || d == 64 || d == 128 || (d > 128 && d <= 1024 && d % 64 == 0);
+}
+
+// Heads per two-pass chunk: enough to fill the chip, capped near 2 GiB of workspace.
+constexpr int64_t kChunkBudget = int64_t(2) << 30;
+
+int64_t heads_per_chunk(int64_t BH, int64_t head_bytes) {
+  int64_t n = kChunkBudget / (head_bytes > 0 ? head_bytes : 1);
+  if (n < 1) n = 1;
+  return n < BH ? n : BH;
+}
+
+bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
+}
+
+// ---- stream-ordered workspace: one pool per device, memory kept between calls.
+std::mutex g_pool_mu;
+std::map<int, hipMemPool_t> g_pools;
+
+hipError_t device_pool(hipStream_t stream, hipMemPool_t* pool) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  auto it = g_pools.find(dev);
+  if (it != g_pools.end()) {
+    *pool = it->second;
+    return hipSuccess;
+  }
+  hipMemPoolProps props = {};
+  props.allocType = hipMemAllocationTypePinned;
+  props.handleTypes = hipMemHandleTypeNone;
+  props.location.type = hipMemLocationTypeDevice;
+  props.location.id = dev;
+  hipMemPool_t p = nullptr;
+  e = hipMemPoolCreate(&p, &props);
+  if (e != hipSuccess) return e;
+  uint64_t keep = UINT64_MAX;
+  e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+  if (e != hipSuccess) {
+    (void)hipMemPoolDestroy(p);
+    return e;
+  }
+  g_pools[dev] = p;
+  *pool = p;
+  return hipSuccess;
+}
+
+// ---- kernel timing (benchmarks only).
+struct TimingRecord {
+  int id;
+  hipEvent_t start, stop;
+};
+std::mutex g_timing_mu;
+bool g_timing = false;
+std::vector<TimingRecord> g_records;
+
+bool timing_on() {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  return g_timing;
+}
+
+template <class F>
+hipError_t timed(int id, hipStream_t s, bool on, F&& launch) {
+  if (!on) return launch();
+  TimingRecord r{id, nullptr, nullptr};
+  hipError_t e = hipEventCreate(&r.start);
+  if (e == hipSuccess) e = hipEventCreate(&r.stop);
+  if (e == hipSuccess) e = hipEventRecord(r.start, s);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(r.stop, s);
+  if (e != hipSuccess) {
+    if (r.start) (void)hipEventDestroy(r.start);
+    if (r.stop) (void)hipEventDestroy(r.stop);
+    return e;
+  }
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_records.push_back(r);
+  return hipSuccess;
+}
+
+int run_two_pass(const void* q, const void* k, const void* v, void* out, int64_t BH, int64_t L,
+                 int64_t d, float sl2, bool causal, hipStream_t stream) {
+  const attn::TwoPassDims t = attn::two_pass_dims(L, d);
+  const int64_t per_head = attn::two_pass_head_bytes(t);
+  const int64_t chunk = heads_per_chunk(BH, per_head);
+  const bool on = timing_on();
+
+  hipMemPool_t pool = nullptr;
+  if (device_pool(stream, &pool) != hipSuccess) return ATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (hipMallocFromPoolAsync(&ws, (size_t)(per_head * chunk), pool, stream) != hipSuccess)
+    return ATTN_ERR_WORKSPACE;
+
+  auto r256 = [](int64_t x) { return (x + 255) / 256 * 256; };
+  const int64_t e_bytes = r256((int64_t)t.L * t.Ls * 2) * chunk;
+  const int64_t vt_bytes = r256((int64_t)t.d * t.Lk * 2) * chunk;
+  const int64_t st_bytes = r256((int64_t)t.T * t.L * 4) * chunk;
+  char* base = (char*)ws;
+  void* E = base;
+  void* vt = base + e_bytes;
+  float* mref = (float*)(base + e_bytes + vt_bytes);
+  float* psum = (float*)(base + e_bytes + vt_bytes + st_bytes);
+
+  const int64_t head_elems = L * d;
+  hipError_t err = hipSuccess;
+  for (int64_t h0 = 0; h0 < BH && err == hipSuccess; h0 += chunk) {
+    const int n = (int)((BH - h0) < chunk ? (BH - h0) : chunk);
+    const uint16_t* qc = (const uint16_t*)q + h0 * head_elems;
+    const uint16_t* kc = (const uint16_t*)k + h0 * head_elems;
+    const uint16_t* vc = (const uint16_t*)v + h0 * head_elems;
+    uint16_t* oc = (uint16_t*)out + h0 * head_elems;
+    err = timed(ATTN_KERNEL_V_TRANSPOSE, stream, on,
+                [&] { return attn::launch_v_transpose(vc, vt, n, t, stream); });
+    if (err == hipSuccess)
+      err = timed(ATTN_KERNEL_SCORES, stream, on, [&] {
+        return attn::launch_scores(qc, kc, E, mref, psum, n, t, sl2, causal, stream);
+      });
+    if (err == hipSuccess)
+      err = timed(ATTN_KERNEL_VALUES, stream, on, [&] {
+        return attn::launch_values(vt, E, mref, psum, oc, n, t, causal, stream);
+      });
+  }
+  const hipError_t ferr = hipFreeAsync(ws, stream);
+  if (err != hipSuccess || ferr != hipSuccess) return ATTN_ERR_HIP;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_NULL_PTR: return "a tensor pointer is NULL";
+    case ATTN_ERR_BAD_SHAPE: return "a size is negative or the byte sizes overflow";
+    case ATTN_ERR_UNSUPPORTED_HEAD_DIM:
+      return "unsupported head dimension: need 32, 64, 128, or a multiple of 64 in (128, 1024]";
+    case ATTN_ERR_BAD_SCALE: return "scale is not finite";
+    case ATTN_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
+    case ATTN_ERR_ALIAS: return "out overlaps q, k or v";
+    case ATTN_ERR_WORKSPACE: return "workspace allocation failed";
+    case ATTN_ERR_HIP: return "a HIP launch or runtime call failed";
+    case ATTN_ERR_TOO_LARGE: return "one head is too large for 32-bit byte offsets";
+    default: return "unknown status";
+  }
+}
+
+int attn_path_for_head_dim(int64_t d) {
+  if (d == 32 || d == 64 || d == 128) return ATTN_PATH_ONLINE;
+  if (head_dim_supported(d)) return ATTN_PATH_TWO_PASS;
+  return ATTN_PATH_NONE;
+}
+
+int64_t attn_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int causal) {
+  (void)causal;
+  if (B < 0 || H < 0 || L < 0 || attn_path_for_head_dim(d) != ATTN_PATH_TWO_PASS) return 0;
+  if (B == 0 || H == 0 || L == 0) return 0;
+  if (L > (int64_t)1 << 20) return 0;
+  const attn::TwoPassDims t = attn::two_pass_dims(L, d);
+  const int64_t per_head = attn::two_pass_head_bytes(t);
+  return per_head * heads_per_chunk(B * H, per_head);
+}
+
+int attn_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
+                 int64_t L, int64_t d, float scale, int causal, hipStream_t stream) {
+  if (B < 0 || H < 0 || L < 0 || d < 0) return ATTN_ERR_BAD_SHAPE;
+  int64_t bh = 0, rows = 0, elems = 0, bytes = 0;
+  if (__builtin_mul_overflow(B, H, &bh) || __builtin_mul_overflow(bh, L, &rows) ||
+      __builtin_mul_overflow(rows, d, &elems) || __builtin_mul_overflow(elems, (int64_t)2, &bytes))
+    return ATTN_ERR_BAD_SHAPE;
+  if (!head_dim_supported(d)) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+  if (rows == 0) return ATTN_OK;
+  if (!q || !k || !v || !out) return ATTN_ERR_NULL_PTR;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return ATTN_ERR_MISALIGNED;
+  if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+    return ATTN_ERR_ALIAS;
+
+  // Kernels address one head with 32-bit byte offsets and count heads in int.
+  const int64_t head_bytes = L * d * 2;
+  if (head_bytes + (int64_t)256 * d * 2 >= ((int64_t)1 << 31) || bh >= ((int64_t)1 << 31) / 1024)
+    return ATTN_ERR_TOO_LARGE;
+  const float sl2 = scale * 1.4426950408889634f;
+  const bool c = causal != 0;
+
+  if (attn_path_for_head_dim(d) == ATTN_PATH_ONLINE) {
+    const int64_t nqb = (L + 127) / 128;
+    if (nqb * bh >= ((int64_t)1 << 31)) return ATTN_ERR_TOO_LARGE;
+    const hipError_t e = timed(ATTN_KERNEL_ONLINE, stream, timing_on(), [&] {
+      return attn::launch_online(q, k, v, out, (int)bh, (int)L, (int)d, sl2, c, stream);
+    });
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  }
+  const attn::TwoPassDims t = attn::two_pass_dims(L, d);
+  // E rows are addressed up to (L + 255) * Ls * 2 bytes inside a head.
+  if ((int64_t)(t.L + 256) * t.Ls * 2 >= ((int64_t)1 << 32) - 1 ||
+      (int64_t)t.T * t.T * bh >= ((int64_t)1 << 31))
+    return ATTN_ERR_TOO_LARGE;
+  return run_two_pass(q, k, v, out, bh, L, d, sl2, c, stream);
+}
+
+int attn_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing = enable != 0;
+  return ATTN_OK;
+}
+
+int attn_timing_collect(double* sum_ms, int64_t* launches, int n) {
+  std::vector<TimingRecord> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    recs.swap(g_records);
+  }
+  int status = ATTN_OK;
+  for (const TimingRecord& r : recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      status = ATTN_ERR_HIP;
+    else if (r.id >= 0 && r.id < n) {
+      if (sum_ms) sum_ms[r.id] += ms;
+      if (launches) launches[r.id] += 1;
+    }
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  return status;
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// device.h -- gfx950 building blocks shared by the attention kernels.
+//
+// bf16 MFMA (v_mfma_f32_32x32x16_bf16), buffer-resource loads with hardware
+// zero-fill past the end of a tensor, direct global->LDS loads, and the
+// conversions the softmax needs.  Nothing here is specific to one kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Buffer resource over [base, base + bytes).  Loads past `bytes` return zero,
+// which is how every kernel here pads the ragged tail of a tile.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes from byte offset `voff` into registers (zero when out of range).
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+}
+
+// 16 bytes from byte offset `voff` straight into LDS.  `dst` is wave-uniform;
+// lane i's 16 bytes land at dst + 16 * i.
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)dst, 16, (int)voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// D = A * B + C with A 32x16, B 16x32, C/D 32x32 fp32.  Lane l supplies
+// A[l % 32][8 * (l / 32) + e] and B[8 * (l / 32) + e][l % 32], e = 0..7, and
+// holds D[8 * (j / 4) + 4 * (l / 32) + j % 4][l % 32] in element j.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two floats -> two bf16 (round to nearest even), packed lo | hi << 16.
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Multiply both bf16 halves of a word by 2^-s (s <= 255) exactly: a saturating
+// subtract on the exponent field; values that would drop below the smallest
+// normal become zero.  `s2` is s << 7 | s << 23.  Inputs must be >= 0.
+__device__ __forceinline__ unsigned scale_pow2_down(unsigned w, unsigned s2) {
+  u16x2 a = __builtin_bit_cast(u16x2, w);
+  u16x2 b = __builtin_bit_cast(u16x2, s2);
+  return __builtin_bit_cast(unsigned, __builtin_elementwise_sub_sat(a, b));
+}
+
+__device__ __forceinline__ float wave_swap32_max(float x) {
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+__device__ __forceinline__ float wave_swap32_sum(float x) {
+  return x + __shfl_xor(x, 32, 64);
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs.  Renumber them so that a run
+// of consecutive logical ids sits on one XCD (sharing its L2): physical id p
+// runs on XCD p % 8; logical ids [x*per, (x+1)*per) go to XCD x.
+__device__ __forceinline__ uint32_t xcd_logical_id(uint32_t p, uint32_t n) {
+  const uint32_t per = n / 8, rem = n % 8;
+  const uint32_t x = p % 8, slot = p / 8;
+  // XCDs 0..rem-1 get per+1 logical ids, the rest get per.
+  const uint32_t base = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  return base + slot;
+}
+
+}  // namespace attn

@@ -1,0 +1,42 @@
+// internal.h -- launchers the C ABI dispatches to (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Sizes of the two-pass path's per-head staging, all in elements.
+struct TwoPassDims {
+  int L;   // sequence length
+  int d;   // head dimension
+  int T;   // number of 256-key score tiles: ceil(L / 256)
+  int Ls;  // row stride of the exponent matrix E: T * 256
+  int Lk;  // row stride of V^T: ceil(L / 64) * 64
+};
+
+TwoPassDims two_pass_dims(int64_t L, int64_t d);
+
+// Bytes of workspace one head needs on the two-pass path: E, V^T, and the
+// per-(tile, query) exponent reference and partial sum.
+int64_t two_pass_head_bytes(const TwoPassDims& t);
+
+// Fused online-softmax kernel, d in {32, 64, 128}.  sl2 = scale * log2(e).
+hipError_t launch_online(const void* q, const void* k, const void* v, void* out, int BH, int L,
+                         int d, float sl2, bool causal, hipStream_t s);
+
+// V [BH, L, d] -> V^T [BH, d, Lk], zero past L.
+hipError_t launch_v_transpose(const void* v, void* vt, int BH, const TwoPassDims& t,
+                              hipStream_t s);
+
+// Scores pass: per 256x256 (key, query) tile, E = bf16(2^(y - m)) with
+// y = sl2 * q.k, m = ceil(max over the tile's keys of y) per query, plus m and
+// the sum of the stored E per (tile, query).
+hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, float* psum, int BH,
+                         const TwoPassDims& t, float sl2, bool causal, hipStream_t s);
+
+// Values pass: O = (sum over tiles of 2^(m_t - M) E_t V_t) / (sum_t 2^(m_t - M) psum_t).
+hipError_t launch_values(const void* vt, const void* E, const float* mref, const float* psum,
+                         void* out, int BH, const TwoPassDims& t, bool causal, hipStream_t s);
+
+}  // namespace attn

@@ -1,0 +1,112 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) exact softmax attention library.
+ *
+ * The operation (FastVideo wan22_vae_decode attn.cu, header comment and
+ * row_softmax_kernel; cuDNN native_sparse_attention fmha.py, module docstring
+ * and softmax_step): for every batch b and head h,
+ *
+ *     O[b,h] = softmax( scale * Q[b,h] K[b,h]^T ) V[b,h]
+ *
+ * where the softmax runs over keys with the row maximum subtracted first, and,
+ * when causal is nonzero, key j is allowed for query i only if j <= i.  Both
+ * contractions accumulate in fp32; the result is rounded once to bf16.
+ *
+ * Conventions shared by every entry point:
+ *   - q, k, v, out are device pointers to bf16 values (raw 16-bit patterns),
+ *     each a row-major contiguous [B, H, L, d] tensor; q, k, v share L and d.
+ *   - The caller owns all four buffers and keeps them alive until the work
+ *     queued on `stream` has finished.  `out` is written, never read, and must
+ *     not overlap q, k or v.  The library keeps no reference to them.
+ *   - Work is queued asynchronously on `stream` (0 = the null stream); no
+ *     entry point synchronises the device.
+ *   - Every argument is checked on the host before any HIP call; a failed check
+ *     returns its status code and queues nothing.  No exception crosses the ABI.
+ *   - Thread safety: any number of host threads may call concurrently.  Calls on
+ *     different streams are independent: workspace comes from a stream-ordered
+ *     pool, so two calls never share scratch memory.
+ */
+#ifndef ATTN_MI355X_ATTN_H
+#define ATTN_MI355X_ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (the pages' host code throws on bad shapes -- attn.cu's
+ * attn_forward checks, fmha.py's __call__ type errors; here they are returns). */
+enum {
+  ATTN_OK = 0,                       /* success; also B*H*L == 0 (nothing queued) */
+  ATTN_ERR_NULL_PTR = 1,             /* q, k, v or out is NULL (with B*H*L > 0)   */
+  ATTN_ERR_BAD_SHAPE = 2,            /* a negative size, or byte sizes overflow   */
+  ATTN_ERR_UNSUPPORTED_HEAD_DIM = 3, /* d not in {32,64,128} nor 128<d<=1024, d%64==0 */
+  ATTN_ERR_BAD_SCALE = 4,            /* scale is NaN or infinite                  */
+  ATTN_ERR_MISALIGNED = 5,           /* a pointer is not 16-byte aligned          */
+  ATTN_ERR_ALIAS = 6,                /* out overlaps q, k or v                    */
+  ATTN_ERR_WORKSPACE = 7,            /* the stream-ordered workspace allocation failed */
+  ATTN_ERR_HIP = 8,                  /* a HIP launch or runtime call failed       */
+  ATTN_ERR_TOO_LARGE = 9             /* one head exceeds the kernels' 32-bit byte offsets */
+};
+
+/* Kernel paths chosen by head dimension. */
+enum {
+  ATTN_PATH_NONE = -1,
+  ATTN_PATH_ONLINE = 0,   /* d in {32, 64, 128}: one fused online-softmax kernel  */
+  ATTN_PATH_TWO_PASS = 1  /* 128 < d <= 1024, d % 64 == 0: scores pass + values pass */
+};
+
+/*
+ * attn_forward -- O = softmax(scale * Q K^T) V on bf16 [B,H,L,d] tensors.
+ *
+ *   q, k, v : const device pointers, bf16 [B,H,L,d] contiguous, 16-byte aligned.
+ *   out     : device pointer, bf16 [B,H,L,d] contiguous, 16-byte aligned.
+ *   B, H, L : batch, heads, sequence length (>= 0; B*H*L == 0 queues nothing).
+ *   d       : head dimension: 32, 64, 128, or a multiple of 64 in (128, 1024].
+ *   scale   : finite logit scale (any sign, 0 allowed); callers usually pass 1/sqrt(d).
+ *   causal  : 0 = no mask; nonzero = key j allowed for query i iff j <= i.
+ *   stream  : HIP stream the kernels are queued on.
+ *
+ * Returns ATTN_OK or one of the codes above.  For d > 128 the call draws a
+ * workspace from a per-device stream-ordered pool and returns it on `stream`
+ * after the last kernel (about 2*L*ceil(L/256)*256 + 2*d*ceil(L/64)*64 bytes
+ * per head, heads processed in chunks of at most 2 GiB).
+ */
+int attn_forward(const void* q, const void* k, const void* v, void* out,
+                 int64_t B, int64_t H, int64_t L, int64_t d,
+                 float scale, int causal, hipStream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/* The kernel path attn_forward uses for head dimension d, or ATTN_PATH_NONE.
+ * Host-only; makes no HIP call. */
+int attn_path_for_head_dim(int64_t d);
+
+/* Workspace bytes attn_forward draws for one chunk of this problem (0 on the
+ * online path or for an invalid shape).  Host-only; makes no HIP call. */
+int64_t attn_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int causal);
+
+/*
+ * Kernel timing, for benchmarks.  While enabled, attn_forward records a pair of
+ * HIP events around every kernel it queues (on the caller's stream).
+ * attn_timing_collect waits for those events, adds each kernel's elapsed
+ * milliseconds and launch count into sum_ms[id] / launches[id] for
+ * id < n (ids below), and forgets the records.  Returns a status code.
+ */
+enum {
+  ATTN_KERNEL_ONLINE = 0,      /* fused online-softmax kernel (d <= 128)        */
+  ATTN_KERNEL_V_TRANSPOSE = 1, /* two-pass path: V -> V^T staging              */
+  ATTN_KERNEL_SCORES = 2,      /* two-pass path: S = QK^T tiles -> bf16 exp + stats */
+  ATTN_KERNEL_VALUES = 3,      /* two-pass path: O = P V with the row normalisation */
+  ATTN_KERNEL_COUNT = 4
+};
+int attn_timing_enable(int enable);
+int attn_timing_collect(double* sum_ms, int64_t* launches, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_ATTN_H */

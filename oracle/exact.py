@@ -111,11 +111,13 @@ def attention_rows(q, k, v, scale: float, causal: bool, rows) -> np.ndarray:
     check full-size runs on a sample of rows the oracle can afford one by one.
     """
     out = np.empty((len(rows), np.shape(v)[-1]), dtype=np.float64)
+    cache = {}
     for r, (b, h, i) in enumerate(rows):
-        Q = np.asarray(q[b, h, i : i + 1], dtype=np.float64)
-        K = np.asarray(k[b, h], dtype=np.float64)
-        V = np.asarray(v[b, h], dtype=np.float64)
-        Z = logits(Q, K, scale)
+        if (b, h) not in cache:
+            cache.clear()  # one head's K and V in float64 at a time
+            cache[(b, h)] = (_head(k, b, h), _head(v, b, h))
+        K, V = cache[(b, h)]
+        Z = logits(np.asarray(q[b, h, i : i + 1], dtype=np.float64), K, scale)
         if causal:
             Z = causal_mask(Z, np.array([i]))
         out[r] = weighted_values(softmax_rows(Z), V)[0]

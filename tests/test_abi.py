@@ -1,0 +1,158 @@
+"""The C ABI on the host: exported symbols, argument checks, path choice.
+
+Every check in attn_forward runs before any HIP call, so these calls use fake
+(never dereferenced) addresses and need no GPU.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_softmax_attention_bf16_amd as eab
+from exact_softmax_attention_bf16_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+A = 0x7F0000000000          # fake, 16-byte aligned device addresses (never touched)
+MB = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(attn_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def fwd(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, B=1, H=1, L=16, d=64,
+        scale=0.125, causal=0):
+    return _lib.load().attn_forward(q, k, v, out, B, H, L, d, scale, causal, None)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["attn_forward", "attn_status_string", "attn_path_for_head_dim",
+                            "attn_workspace_bytes", "attn_timing_enable", "attn_timing_collect"])
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True)
+    exported = set(re.findall(r"\sT\s(attn_\w+)", out.stdout))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings():
+    for code in range(10):
+        s = eab.status_string(code)
+        assert s and s != "unknown status"
+    assert eab.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("d,path", [(32, 0), (64, 0), (128, 0), (192, 1), (256, 1), (320, 1),
+                                    (1024, 1), (0, -1), (16, -1), (48, -1), (96, -1), (160, -1),
+                                    (1088, -1), (2048, -1), (-64, -1)])
+def test_path_for_head_dim(d, path):
+    assert eab.path_for_head_dim(d) == path
+
+
+def test_workspace_bytes():
+    # per head: E (L x ceil(L/256)*256 bf16), V^T (d x ceil(L/64)*64 bf16), two fp32 [T, L] tables
+    L, d, T = 3432, 1024, 14
+    r = lambda x: (x + 255) // 256 * 256
+    per_head = r(L * T * 256 * 2) + r(d * 3456 * 2) + 2 * r(T * L * 4)
+    assert eab.workspace_bytes(1, 1, L, d) == per_head
+    assert eab.workspace_bytes(31, 1, L, d) == 31 * per_head
+    assert eab.workspace_bytes(4, 8, 1024, 64) == 0       # online path: none
+    assert eab.workspace_bytes(0, 1, L, d) == 0
+    big = eab.workspace_bytes(1000, 1, L, d)              # chunked under ~2 GiB
+    assert per_head <= big <= (2 << 30)
+
+
+def test_valid_empty_problem_queues_nothing():
+    assert fwd(q=None, k=None, v=None, out=None, L=0) == _lib.ATTN_OK
+    assert fwd(B=0) == _lib.ATTN_OK
+    assert fwd(H=0, d=1024) == _lib.ATTN_OK
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "out"])
+def test_null_pointer(which):
+    assert fwd(**{which: None}) == _lib.ATTN_ERR_NULL_PTR
+
+
+@pytest.mark.parametrize("dims", [dict(B=-1), dict(H=-2), dict(L=-5), dict(d=-64),
+                                  dict(B=1 << 40, H=1 << 20, L=1 << 10)])
+def test_bad_shape(dims):
+    assert fwd(**dims) == _lib.ATTN_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("d", [0, 16, 48, 96, 100, 160, 1088, 2048])
+def test_unsupported_head_dim(d):
+    assert fwd(d=d) == _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM
+
+
+@pytest.mark.parametrize("scale", [float("nan"), float("inf"), float("-inf")])
+def test_bad_scale(scale):
+    assert fwd(scale=scale) == _lib.ATTN_ERR_BAD_SCALE
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "out"])
+def test_misaligned(which):
+    base = {"q": A, "k": A + 64 * MB, "v": A + 128 * MB, "out": A + 192 * MB}[which]
+    assert fwd(**{which: base + 8}) == _lib.ATTN_ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v"])
+def test_out_overlapping_an_input(which):
+    base = {"q": A, "k": A + 64 * MB, "v": A + 128 * MB}[which]
+    nbytes = 2 * 3 * 5 * 100 * 64 * 2
+    assert fwd(out=base, B=2, H=3, L=500) == _lib.ATTN_ERR_ALIAS
+    assert fwd(out=base + nbytes - 16, B=2, H=3, L=500) == _lib.ATTN_ERR_ALIAS
+
+
+def test_adjacent_buffers_do_not_alias():
+    # out starts exactly where q ends: allowed (checked, then it would launch, so
+    # only the alias predicate is exercised through a too-large shape error path)
+    L, d = 1 << 21, 1024  # one head of 4 GiB: rejected after the alias check
+    nbytes = L * d * 2
+    assert fwd(q=A, k=A + nbytes, v=A + 2 * nbytes, out=A + 3 * nbytes, L=L, d=d) == _lib.ATTN_ERR_TOO_LARGE
+
+
+def test_too_large_two_pass_head():
+    # E for one head would need more than 2^32 bytes of offsets
+    L, d = 50000, 256
+    n = L * d * 2
+    assert fwd(q=A, k=A + n, v=A + 2 * n, out=A + 3 * n, L=L, d=d) == _lib.ATTN_ERR_TOO_LARGE
+
+
+def test_check_order_is_documented():
+    # shape before head dim before scale before emptiness before pointers
+    assert fwd(B=-1, d=48) == _lib.ATTN_ERR_BAD_SHAPE
+    assert fwd(d=48, scale=float("nan")) == _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM
+    assert fwd(scale=float("nan"), q=None) == _lib.ATTN_ERR_BAD_SCALE
+    assert fwd(q=None, out=A + 8) == _lib.ATTN_ERR_NULL_PTR
+    assert fwd(out=A + 8, k=A) == _lib.ATTN_ERR_MISALIGNED
+
+
+def test_timing_collect_without_records():
+    lib = _lib.load()
+    n = 4
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    assert lib.attn_timing_collect(ms, cnt, n) == _lib.ATTN_OK
+    assert list(cnt) == [0] * n
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    from exact_softmax_attention_bf16_amd import attention
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):          # CPU tensors never reach the library
+        attention(x, x, x)
+    with pytest.raises(TypeError):
+        attention(x.float(), x, x)

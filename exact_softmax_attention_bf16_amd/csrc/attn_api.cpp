@@ -165,7 +165,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_ALIAS: return "out overlaps q, k or v";
     case ATTN_ERR_WORKSPACE: return "workspace allocation failed";
     case ATTN_ERR_HIP: return "a HIP launch or runtime call failed";
-    case ATTN_ERR_TOO_LARGE: return "one head is too large for 32-bit byte offsets";
+    case ATTN_ERR_TOO_LARGE: return "problem too large: one head exceeds 32-bit byte offsets, or L > 31744 with d > 128";
     default: return "unknown status";
   }
 }
@@ -218,7 +218,7 @@ int attn_forward(const void* q, const void* k, const void* v, void* out, int64_t
   }
   const attn::TwoPassDims t = attn::two_pass_dims(L, d);
   // E rows are addressed up to (L + 255) * Ls * 2 bytes inside a head.
-  if ((int64_t)(t.L + 256) * t.Ls * 2 >= ((int64_t)1 << 32) - 1 ||
+  if (t.T > attn::kTwoPassMaxTiles || (int64_t)(t.L + 256) * t.Ls * 2 >= ((int64_t)1 << 32) - 1 ||
       (int64_t)t.T * t.T * bh >= ((int64_t)1 << 31))
     return ATTN_ERR_TOO_LARGE;
   return run_two_pass(q, k, v, out, bh, L, d, sl2, c, stream);

@@ -4,12 +4,18 @@
 // B = Q rows, K = d) and the values pass (A = V^T rows, B = E rows, K = keys).
 //
 // Workgroup: 4 waves in a 2x2 grid, each wave owning a 128x128 block of C as
-// 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 registers per lane).
-// The K loop runs in 64-wide steps through two LDS stages (2 x 64 KB); the next
-// step's A and B tiles are fetched straight into LDS with buffer loads while
-// the current stage feeds the MFMAs.  Each 128-byte LDS row holds eight
-// 16-byte chunks stored at chunk ^ (row % 8), so the eight lanes that read one
-// column of chunks in a fragment load hit eight different bank groups.
+// 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 registers per lane, held
+// in AGPRs).  The K loop runs in 64-wide steps through two LDS stages
+// (2 x 64 KB) filled by direct buffer->LDS loads.  Each 128-byte LDS row holds
+// eight 16-byte chunks stored at chunk ^ (row % 8), so the lanes that read one
+// column of chunks in a fragment load hit different bank groups.
+//
+// Schedule per 64-wide step (4 sub-steps of k = 16, 16 MFMAs each): the
+// fragments of sub-step s + 1 are read from LDS while the MFMAs of sub-step s
+// run.  In the last sub-step the wave waits for its own loads of the next
+// stage, the workgroup meets at one barrier (next stage complete everywhere,
+// current stage no longer read), the loads two steps ahead are issued into
+// the stage just drained, and the first fragments of the next step are read.
 #pragma once
 
 #include "device.h"
@@ -25,18 +31,28 @@ struct GemmSmem {
   char b[2][kStageBytes];
 };
 
-// Copy rows [r0, r0 + 256) x columns [k0, k0 + 64) of a row-major bf16 matrix
-// (row stride `ld` elements) into one LDS stage; 8 direct loads per lane.
-__device__ __forceinline__ void gemm_load_tile(__amdgpu_buffer_rsrc_t r, uint32_t ld, int r0,
-                                               int k0, char* stage, int wave, int lane) {
+// Per-lane byte offsets of the 8 chunks this lane copies for one operand, at k = 0.
+struct TileLoader {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t off[8];
+
+  __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t rsrc, uint32_t ld, int r0, int wave,
+                                       int lane) {
+    r = rsrc;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int P = (wave * 8 + j) * 64 + lane;  // 16-byte chunk slot in the stage
-    const int row = P >> 3, pc = P & 7, lc = pc ^ (row & 7);
-    const uint32_t voff = ((uint32_t)(r0 + row) * ld + (uint32_t)(k0 + lc * 8)) * 2u;
-    load16_to_lds(r, stage + (wave * 8 + j) * 1024, voff);
+    for (int j = 0; j < 8; ++j) {
+      const int P = (wave * 8 + j) * 64 + lane;  // 16-byte chunk slot in the stage
+      const int row = P >> 3, pc = P & 7, lc = pc ^ (row & 7);
+      off[j] = ((uint32_t)(r0 + row) * ld + (uint32_t)(lc * 8)) * 2u;
+    }
   }
-}
+  // Rows [r0, r0 + 256) x columns [k0, k0 + 64) into `stage`.
+  __device__ __forceinline__ void issue(int k0, char* stage, int wave) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      load16_to_lds(r, stage + (wave * 8 + j) * 1024, off[j] + (uint32_t)k0 * 2u);
+  }
+};
 
 __device__ __forceinline__ bf16x8 gemm_frag(const char* stage, int row, int lc) {
   return *(const bf16x8*)(stage + row * 128 + ((lc ^ (row & 7)) << 4));
@@ -47,8 +63,56 @@ struct NoTransform {
   __device__ __forceinline__ bf16x8 operator()(bf16x8 f, int) const { return f; }
 };
 
-// acc[i][j] += A[m0 + 128 wm + 32 i + .., :] . B[n0 + 128 wn + 32 j + .., :] over nk steps.
-// `bx.step(kt)` runs at the top of step kt; `bx(frag, j)` may rewrite each B fragment.
+struct Frags {
+  bf16x8 a[4], b[4];
+};
+
+__device__ __forceinline__ void read_frags(Frags& f, const char* sa, const char* sb, int wm, int wn,
+                                           int c32, int h, int ss) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = gemm_frag(sa, wm * 128 + i * 32 + c32, 2 * ss + h);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.b[j] = gemm_frag(sb, wn * 128 + j * 32 + c32, 2 * ss + h);
+}
+
+template <class BX>
+__device__ __forceinline__ void mma_substep(f32x16 (&acc)[4][4], const Frags& f, const BX& bx) {
+  bf16x8 b[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = bx(f.b[j], j);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(f.a[i], b[j], acc[i][j]);
+}
+
+// Interleave 16 MFMAs with 8 LDS reads (and optionally 16 buffer loads).
+__device__ __forceinline__ void sched_substep(bool with_vmem) {
+  if (with_vmem) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // 2 VMEM reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    }
+  }
+}
+
+__device__ __forceinline__ void block_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
+  __builtin_amdgcn_s_barrier();
+}
+
+// acc[i][j] = A[m0 + 128 wm + 32 i + .., 0:64 nk] . B[n0 + 128 wn + 32 j + .., 0:64 nk].
+// `bx.step(kt)` runs before step kt's MFMAs; `bx(frag, j)` may rewrite each B fragment.
 template <class BX>
 __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_rsrc_t ra,
                                           uint32_t lda, int m0, __amdgpu_buffer_rsrc_t rb,
@@ -61,32 +125,45 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  gemm_load_tile(ra, lda, m0, 0, sm.a[0], wave, lane);
-  gemm_load_tile(rb, ldb, n0, 0, sm.b[0], wave, lane);
+  TileLoader la, lb;
+  la.init(ra, lda, m0, wave, lane);
+  lb.init(rb, ldb, n0, wave, lane);
+
+  // Stage 0 <- step 0; stage 1 <- step 1 (a harmless reload of step 0 when nk == 1).
+  la.issue(0, sm.a[0], wave);
+  lb.issue(0, sm.b[0], wave);
+  wait_vmem();
+  block_sync();
+  const int k1 = nk > 1 ? kStepK : 0;
+  la.issue(k1, sm.a[1], wave);
+  lb.issue(k1, sm.b[1], wave);
+
+  Frags cur, nxt;
+  read_frags(cur, sm.a[0], sm.b[0], wm, wn, c32, h, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    wait_vmem();
-    __syncthreads();  // stage st landed; every wave is done reading stage st ^ 1
-    if (kt + 1 < nk) {
-      gemm_load_tile(ra, lda, m0, (kt + 1) * kStepK, sm.a[st ^ 1], wave, lane);
-      gemm_load_tile(rb, ldb, n0, (kt + 1) * kStepK, sm.b[st ^ 1], wave, lane);
-    }
-    bx.step(kt);
     const char* sa = sm.a[st];
     const char* sb = sm.b[st];
+    bx.step(kt);
 #pragma unroll
-    for (int ss = 0; ss < 4; ++ss) {
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = gemm_frag(sa, wm * 128 + i * 32 + c32, 2 * ss + h);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = bx(gemm_frag(sb, wn * 128 + j * 32 + c32, 2 * ss + h), j);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
+    for (int ss = 0; ss < 3; ++ss) {
+      read_frags(nxt, sa, sb, wm, wn, c32, h, ss + 1);
+      mma_substep(acc, cur, bx);
+      sched_substep(false);
+      cur = nxt;
     }
+    // Last sub-step: next stage complete everywhere, this stage drained.
+    wait_vmem();
+    block_sync();
+    const int k2 = (kt + 2 < nk ? kt + 2 : nk - 1) * kStepK;  // past the end: reload, unused
+    la.issue(k2, sm.a[st], wave);
+    lb.issue(k2, sm.b[st], wave);
+    read_frags(nxt, sm.a[st ^ 1], sm.b[st ^ 1], wm, wn, c32, h, 0);
+    mma_substep(acc, cur, bx);
+    sched_substep(true);
+    cur = nxt;
   }
+  wait_vmem();  // no LDS writes in flight past the loop
 }
 
 }  // namespace attn

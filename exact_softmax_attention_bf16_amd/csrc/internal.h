@@ -17,6 +17,10 @@ struct TwoPassDims {
 
 TwoPassDims two_pass_dims(int64_t L, int64_t d);
 
+// The values pass keeps one byte per (score tile, query) of its query tile in
+// LDS next to the 128 KB GEMM stages, which caps L at 124 * 256 = 31744 there.
+constexpr int kTwoPassMaxTiles = 124;
+
 // Bytes of workspace one head needs on the two-pass path: E, V^T, and the
 // per-(tile, query) exponent reference and partial sum.
 int64_t two_pass_head_bytes(const TwoPassDims& t);

@@ -113,27 +113,49 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
   const int wm = wave >> 1, wn = wave & 1, c32 = lane & 31, h = lane >> 5;
   const int key0 = kt * kTile + wm * 128;
 
-  // Scale, mask and the per-query maximum over this wave's 128 keys.
+  // Per-query maximum of y = sl2 * s over this wave's 128 keys.  Interior tiles
+  // (no key past L, no key after a query) take it on the raw accumulator; edge
+  // tiles scale and mask each element.  The accumulator is only read here.
+  const bool need_mask = (kt + 1) * kTile > L || (causal && kt >= qt);
+  auto masked = [&](int bi, int bj, int j) {
+    const int key = key0 + bi * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+    const int query = qt * kTile + wn * 128 + bj * 32 + c32;
+    return key >= L || (causal && key > query);
+  };
+  float wmax[4];
 #pragma unroll
   for (int bj = 0; bj < 4; ++bj) {
-    const int query = qt * kTile + wn * 128 + bj * 32 + c32;
-    float wmax = -INFINITY;
+    float mx = -INFINITY;
+    if (!need_mask) {
+      float hi = -INFINITY, lo = INFINITY;
+      if (sl2 >= 0.f) {
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
+        for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = key0 + bi * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-        float y = acc[bi][bj][j] * sl2;
-        if (key >= L || (causal && key > query)) y = -INFINITY;
-        acc[bi][bj][j] = y;
-        wmax = fmaxf(wmax, y);
+          for (int j = 0; j < 16; ++j) hi = fmaxf(hi, acc[bi][bj][j]);
+        mx = hi * sl2;
+      } else {
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) lo = fminf(lo, acc[bi][bj][j]);
+        mx = lo * sl2;
       }
+    } else {
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          mx = fmaxf(mx, masked(bi, bj, j) ? -INFINITY : acc[bi][bj][j] * sl2);
     }
-    wmax = wave_swap32_max(wmax);
-    if (h == 0) red[wm][wn * 128 + bj * 32 + c32] = wmax;
+    wmax[bj] = wave_swap32_max(mx);
   }
+#pragma unroll
+  for (int bj = 0; bj < 4; ++bj)
+    if (h == 0) red[wm][wn * 128 + bj * 32 + c32] = wmax[bj];
   __syncthreads();
 
+  // E = bf16(2^(y - m)) with m = ceil(tile max of y): at most 1, at least 1/2 at the max.
   float mt[4], ps[4];
   uint16_t* Eh = E + (size_t)bh * L * Ls;
 #pragma unroll
@@ -142,17 +164,21 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
     const int query = qt * kTile + ql;
     const float tmax = fmaxf(red[0][ql], red[1][ql]);
     const float m2 = tmax == -INFINITY ? -INFINITY : ceilf(tmax);
-    const float muse = tmax == -INFINITY ? 0.f : m2;
+    const float add = tmax == -INFINITY ? 0.f : -m2;
     float s = 0.f;
     uint16_t* erow = Eh + (size_t)query * Ls + key0 + 4 * h;
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const unsigned w0 = pack_bf16x2(exp2_fast(acc[bi][bj][4 * i] - muse),
-                                        exp2_fast(acc[bi][bj][4 * i + 1] - muse));
-        const unsigned w1 = pack_bf16x2(exp2_fast(acc[bi][bj][4 * i + 2] - muse),
-                                        exp2_fast(acc[bi][bj][4 * i + 3] - muse));
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e[r] = exp2_fast(fmaf(acc[bi][bj][4 * i + r], sl2, add));
+          if (need_mask && masked(bi, bj, 4 * i + r)) e[r] = 0.f;
+        }
+        const unsigned w0 = pack_bf16x2(e[0], e[1]);
+        const unsigned w1 = pack_bf16x2(e[2], e[3]);
         s += (bf16_lo(w0) + bf16_hi(w0)) + (bf16_lo(w1) + bf16_hi(w1));
         if (query < L) *(u32x2*)(erow + bi * 32 + 8 * i) = u32x2{w0, w1};
       }
@@ -186,27 +212,19 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
 // Each lane owns four queries (one per 32-column block j); before each group
 // of four steps (one 256-key score tile t) it turns M - m_t into the exponent
 // shift for those queries, fetched one tile ahead.
+constexpr int kMaxTiles = kTwoPassMaxTiles;
+
 struct PowerOfTwoShift {
-  const float* mref;  // this head's reference exponents, [T][L]
-  int L;
-  int q[4];           // this lane's queries, clamped into [0, L)
-  float M[4];         // per-query maximum of m_t over the tiles used
-  float next[4];      // m_{t+1}, loaded during tile t
-  unsigned sw[4];     // current shift words (s << 7 | s << 23)
-  int tiles;          // tiles used by this query block
+  const uint8_t (*tab)[kTile];  // [t][query in tile]: M - m_t, capped at 255
+  int col[4];                   // this lane's four query columns in the tile
+  unsigned sw[4];               // current shift words (s << 7 | s << 23)
 
   __device__ __forceinline__ void step(int kt) {
     if ((kt & 3) == 0) {
-      const int t = kt >> 2;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float diff = fminf(M[j] - next[j], 255.f);  // m_t = -inf -> 255 -> zero
-        const unsigned s = (unsigned)diff;
+        const unsigned s = tab[kt >> 2][col[j]];
         sw[j] = (s << 7) | (s << 23);
-      }
-      if (t + 1 < tiles) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) next[j] = mref[(size_t)(t + 1) * L + q[j]];
       }
     }
   }
@@ -225,6 +243,8 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
                                                      uint16_t* __restrict__ out, int L, int d,
                                                      int T, int Ls, int Lk, int causal, int ncb) {
   __shared__ GemmSmem sm;
+  __shared__ uint8_t shift_tab[kMaxTiles][kTile];
+  __shared__ float inv_l[kTile];
 
   const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int per_head = T * ncb;
@@ -239,27 +259,31 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
   const int kend = causal ? min(Lk, (qt + 1) * kTile) : Lk;
   const int nk = kend / kStepK;
 
-  const float* mh = mref + (size_t)bh * T * L;
-  const float* ph = psum + (size_t)bh * T * L;
+  // Thread tid owns query qt*256 + tid: M = max_t m_t, l = sum_t 2^(m_t - M) psum_t,
+  // and the shift M - m_t of each tile (a nonnegative integer; -inf tiles -> 255).
+  {
+    const float* mh = mref + (size_t)bh * T * L;
+    const float* ph = psum + (size_t)bh * T * L;
+    const int qc = min(qt * kTile + tid, L - 1);
+    float M = -INFINITY;
+    for (int t = 0; t < tiles; ++t) M = fmaxf(M, mh[(size_t)t * L + qc]);
+    float l = 0.f;
+    for (int t = 0; t < tiles; ++t) {
+      const float mt = mh[(size_t)t * L + qc];
+      l += ph[(size_t)t * L + qc] * exp2_fast(mt - M);
+      shift_tab[t][tid] = (uint8_t)fminf(M - mt, 255.f);
+    }
+    inv_l[tid] = 1.f / l;
+  }
+  __syncthreads();
+
   PowerOfTwoShift sh;
-  sh.mref = mh;
-  sh.L = L;
-  sh.tiles = tiles;
+  sh.tab = shift_tab;
   float invl[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int query = qt * kTile + wn * 128 + j * 32 + c32;
-    sh.q[j] = min(query, L - 1);
-    float M = -INFINITY;
-    for (int t = 0; t < tiles; ++t) M = fmaxf(M, mh[(size_t)t * L + sh.q[j]]);
-    float l = 0.f;
-    for (int t = 0; t < tiles; ++t) {
-      const float mt = mh[(size_t)t * L + sh.q[j]];
-      l += ph[(size_t)t * L + sh.q[j]] * exp2_fast(mt - M);
-    }
-    sh.M[j] = M;
-    sh.next[j] = mh[sh.q[j]];
-    invl[j] = 1.f / l;
+    sh.col[j] = wn * 128 + j * 32 + c32;
+    invl[j] = inv_l[sh.col[j]];
   }
 
   const auto ra = make_rsrc(vt + (size_t)bh * d * Lk, (uint32_t)d * Lk * 2);

@@ -58,6 +58,12 @@ __device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s + lo + hi of a packed bf16 pair, in fp32 (one v_dot2 against (1, 1)).
+__device__ __forceinline__ float add_bf16x2(unsigned w, float s) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), s, false);
+}
+
 // Multiply both bf16 halves of a word by 2^-s (s <= 255) exactly: a saturating
 // subtract on the exponent field; values that would drop below the smallest
 // normal become zero.  `s2` is s << 7 | s << 23.  Inputs must be >= 0.

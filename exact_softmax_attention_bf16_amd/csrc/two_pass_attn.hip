@@ -85,6 +85,140 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __rest
 // Scores pass.  Tile (kt, qt) of head bh: keys [256 kt, +256) on the M side,
 // queries [256 qt, +256) on the N side, so each lane of the accumulator owns a
 // query and holds 4 runs of 4 consecutive keys per 32x32 block.
+//
+// Epilogue, per query: m = ceil(max over the tile's keys of y), y = sl2 * s;
+// E = bf16(2^(y - m)) (so 1/2 < max E <= 1); psum = sum of the stored E.
+// MASK selects the edge-tile version (keys past L, keys after the query); it is
+// a template flag so that the per-element test compiles to selects, not branches.
+// The E tile (256 queries x 256 keys) is staged through the drained GEMM stages
+// in LDS so that the global stores write whole 512-byte row segments.
+template <bool MASK>
+__device__ __forceinline__ void scores_epilogue(const f32x16 (&acc)[4][4], float (&red)[2][kTile],
+                                                char* __restrict__ stage,
+                                                uint16_t* __restrict__ Eh,
+                                                float* __restrict__ mref_t,
+                                                float* __restrict__ psum_t, int L, int Ls,
+                                                int kt, int qt, float sl2, int causal) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, c32 = lane & 31, h = lane >> 5;
+  const int key0 = kt * kTile + wm * 128;
+  // Key key0 + 4h + c (c = 32 bi + 8 (j / 4) + j % 4, a constant) is allowed for
+  // query column bj iff c < lim[bj].
+  int lim[4];
+#pragma unroll
+  for (int bj = 0; bj < 4; ++bj) {
+    const int query = qt * kTile + wn * 128 + bj * 32 + c32;
+    lim[bj] = (causal ? min(L, query + 1) : L) - (key0 + 4 * h);
+  }
+  auto masked = [&](int bi, int bj, int j) { return bi * 32 + 8 * (j >> 2) + (j & 3) >= lim[bj]; };
+
+  // Per-query maximum of y over this wave's 128 keys (interior tiles: on the
+  // raw accumulator, then scaled; the sign of sl2 picks max or min).
+  float wmax[4];
+  if (!MASK && sl2 >= 0.f) {
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      float hi = acc[0][bj][0];
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) hi = fmaxf(hi, acc[bi][bj][j]);
+      wmax[bj] = hi * sl2;
+    }
+  } else if (!MASK) {
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      float lo = acc[0][bj][0];
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) lo = fminf(lo, acc[bi][bj][j]);
+      wmax[bj] = lo * sl2;
+    }
+  } else {
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          mx = fmaxf(mx, masked(bi, bj, j) ? -INFINITY : acc[bi][bj][j] * sl2);
+      wmax[bj] = mx;
+    }
+  }
+#pragma unroll
+  for (int bj = 0; bj < 4; ++bj) {
+    const float m = wave_swap32_max(wmax[bj]);
+    if (h == 0) red[wm][wn * 128 + bj * 32 + c32] = m;
+  }
+  __syncthreads();  // red complete; every wave is past its GEMM (the stages are free)
+  // Recompute the mask below instead of keeping 256 mask bits alive across the
+  // barrier (the compiler would otherwise hold them in scalar registers).
+#pragma unroll
+  for (int bj = 0; bj < 4; ++bj) asm volatile("" : "+v"(lim[bj]));
+
+  // E into LDS as [query][key] rows of 512 bytes; 16-byte chunk c of row r is
+  // stored at chunk c ^ (r % 32).
+  float mt[4], ps[4];
+#pragma unroll
+  for (int bj = 0; bj < 4; ++bj) {
+    const int ql = wn * 128 + bj * 32 + c32;
+    const float tmax = fmaxf(red[0][ql], red[1][ql]);
+    const float m2 = tmax == -INFINITY ? -INFINITY : ceilf(tmax);
+    const float add = tmax == -INFINITY ? 0.f : -m2;
+    float s = 0.f;
+    char* row = stage + ql * 512 + 8 * h;
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float e[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e[r] = exp2_fast(fmaf(acc[bi][bj][4 * i + r], sl2, add));
+          if (MASK) e[r] = masked(bi, bj, 4 * i + r) ? 0.f : e[r];
+        }
+        const unsigned w0 = pack_bf16x2(e[0], e[1]), w1 = pack_bf16x2(e[2], e[3]);
+        // the normaliser sums exactly the rounded values the values pass multiplies
+        s = add_bf16x2(w1, add_bf16x2(w0, s));
+        const int chunk = wm * 16 + bi * 4 + i;
+        *(u32x2*)(row + ((chunk ^ c32) << 4)) = u32x2{w0, w1};
+      }
+    }
+    mt[bj] = m2;
+    ps[bj] = wave_swap32_sum(s);
+  }
+  __syncthreads();  // E tile complete in LDS; red no longer read
+  if (h == 0) {
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) red[wm][wn * 128 + bj * 32 + c32] = ps[bj];
+  }
+  // Whole-row stores: thread t writes chunk t % 32 of rows t / 32 + 8 j.
+  {
+    const int c = tid & 31;
+    uint16_t* base = Eh + (size_t)(qt * kTile) * Ls + kt * kTile + 8 * c;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) {
+      const int r = (tid >> 5) + 8 * j;
+      if (qt * kTile + r < L)
+        *(u32x4*)(base + (size_t)r * Ls) = *(const u32x4*)(stage + r * 512 + ((c ^ (r & 31)) << 4));
+    }
+  }
+  __syncthreads();  // partial sums complete
+  if (wm == 0 && h == 0) {
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const int ql = wn * 128 + bj * 32 + c32;
+      const int query = qt * kTile + ql;
+      if (query < L) {
+        mref_t[query] = mt[bj];
+        psum_t[query] = red[0][ql] + red[1][ql];
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict__ q,
                                                      const uint16_t* __restrict__ k,
                                                      uint16_t* __restrict__ E,
@@ -109,101 +243,15 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
   NoTransform nx;
   gemm_tile(acc, rk, (uint32_t)d, kt * kTile, rq, (uint32_t)d, qt * kTile, d / kStepK, sm, nx);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, c32 = lane & 31, h = lane >> 5;
-  const int key0 = kt * kTile + wm * 128;
-
-  // Per-query maximum of y = sl2 * s over this wave's 128 keys.  Interior tiles
-  // (no key past L, no key after a query) take it on the raw accumulator; edge
-  // tiles scale and mask each element.  The accumulator is only read here.
-  const bool need_mask = (kt + 1) * kTile > L || (causal && kt >= qt);
-  auto masked = [&](int bi, int bj, int j) {
-    const int key = key0 + bi * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-    const int query = qt * kTile + wn * 128 + bj * 32 + c32;
-    return key >= L || (causal && key > query);
-  };
-  float wmax[4];
-#pragma unroll
-  for (int bj = 0; bj < 4; ++bj) {
-    float mx = -INFINITY;
-    if (!need_mask) {
-      float hi = -INFINITY, lo = INFINITY;
-      if (sl2 >= 0.f) {
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) hi = fmaxf(hi, acc[bi][bj][j]);
-        mx = hi * sl2;
-      } else {
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) lo = fminf(lo, acc[bi][bj][j]);
-        mx = lo * sl2;
-      }
-    } else {
-#pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          mx = fmaxf(mx, masked(bi, bj, j) ? -INFINITY : acc[bi][bj][j] * sl2);
-    }
-    wmax[bj] = wave_swap32_max(mx);
-  }
-#pragma unroll
-  for (int bj = 0; bj < 4; ++bj)
-    if (h == 0) red[wm][wn * 128 + bj * 32 + c32] = wmax[bj];
-  __syncthreads();
-
-  // E = bf16(2^(y - m)) with m = ceil(tile max of y): at most 1, at least 1/2 at the max.
-  float mt[4], ps[4];
   uint16_t* Eh = E + (size_t)bh * L * Ls;
-#pragma unroll
-  for (int bj = 0; bj < 4; ++bj) {
-    const int ql = wn * 128 + bj * 32 + c32;
-    const int query = qt * kTile + ql;
-    const float tmax = fmaxf(red[0][ql], red[1][ql]);
-    const float m2 = tmax == -INFINITY ? -INFINITY : ceilf(tmax);
-    const float add = tmax == -INFINITY ? 0.f : -m2;
-    float s = 0.f;
-    uint16_t* erow = Eh + (size_t)query * Ls + key0 + 4 * h;
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float e[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          e[r] = exp2_fast(fmaf(acc[bi][bj][4 * i + r], sl2, add));
-          if (need_mask && masked(bi, bj, 4 * i + r)) e[r] = 0.f;
-        }
-        const unsigned w0 = pack_bf16x2(e[0], e[1]);
-        const unsigned w1 = pack_bf16x2(e[2], e[3]);
-        s += (bf16_lo(w0) + bf16_hi(w0)) + (bf16_lo(w1) + bf16_hi(w1));
-        if (query < L) *(u32x2*)(erow + bi * 32 + 8 * i) = u32x2{w0, w1};
-      }
-    }
-    mt[bj] = m2;
-    ps[bj] = wave_swap32_sum(s);
-  }
-  __syncthreads();
-  if (h == 0) {
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj) red[wm][wn * 128 + bj * 32 + c32] = ps[bj];
-  }
-  __syncthreads();
-  if (wm == 0 && h == 0) {
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
-      const int ql = wn * 128 + bj * 32 + c32;
-      const int query = qt * kTile + ql;
-      if (query < L) {
-        const size_t at = ((size_t)bh * T + kt) * L + query;
-        mref[at] = mt[bj];
-        psum[at] = red[0][ql] + red[1][ql];
-      }
-    }
-  }
+  float* mref_t = mref + ((size_t)bh * T + kt) * L;
+  float* psum_t = psum + ((size_t)bh * T + kt) * L;
+  const bool need_mask = (kt + 1) * kTile > L || (causal && kt >= qt);
+  char* stage = sm.a[0];  // 128 KB of drained GEMM stages hold the E tile
+  if (need_mask)
+    scores_epilogue<true>(acc, red, stage, Eh, mref_t, psum_t, L, Ls, kt, qt, sl2, causal);
+  else
+    scores_epilogue<false>(acc, red, stage, Eh, mref_t, psum_t, L, Ls, kt, qt, sl2, causal);
 }
 
 // ---------------------------------------------------------------------------
@@ -261,17 +309,37 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
 
   // Thread tid owns query qt*256 + tid: M = max_t m_t, l = sum_t 2^(m_t - M) psum_t,
   // and the shift M - m_t of each tile (a nonnegative integer; -inf tiles -> 255).
+  // The stats are read in batches of 16 tiles so their latencies overlap.
   {
     const float* mh = mref + (size_t)bh * T * L;
     const float* ph = psum + (size_t)bh * T * L;
     const int qc = min(qt * kTile + tid, L - 1);
-    float M = -INFINITY;
-    for (int t = 0; t < tiles; ++t) M = fmaxf(M, mh[(size_t)t * L + qc]);
-    float l = 0.f;
-    for (int t = 0; t < tiles; ++t) {
-      const float mt = mh[(size_t)t * L + qc];
-      l += ph[(size_t)t * L + qc] * exp2_fast(mt - M);
-      shift_tab[t][tid] = (uint8_t)fminf(M - mt, 255.f);
+    float M = -INFINITY, l = 0.f;
+    for (int t0 = 0; t0 < tiles; t0 += 16) {
+      float mt[16], pt[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int t = min(t0 + u, tiles - 1);
+        mt[u] = mh[(size_t)t * L + qc];
+        pt[u] = ph[(size_t)t * L + qc];
+      }
+      float Mn = M;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) Mn = fmaxf(Mn, mt[u]);
+      l = M == -INFINITY ? 0.f : l * exp2_fast(M - Mn);
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (t0 + u < tiles) l += pt[u] * exp2_fast(mt[u] - Mn);
+      M = Mn;
+    }
+    // The shifts need the final M: a second pass over the (now cached) stats.
+    for (int t0 = 0; t0 < tiles; t0 += 16) {
+      float mt[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) mt[u] = mh[(size_t)min(t0 + u, tiles - 1) * L + qc];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (t0 + u < tiles) shift_tab[t0 + u][tid] = (uint8_t)fminf(M - mt[u], 255.f);
     }
     inv_l[tid] = 1.f / l;
   }

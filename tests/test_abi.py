@@ -130,6 +130,13 @@ def test_too_large_two_pass_head():
     assert fwd(q=A, k=A + n, v=A + 2 * n, out=A + 3 * n, L=L, d=d) == _lib.ATTN_ERR_TOO_LARGE
 
 
+def test_two_pass_length_cap():
+    # the values pass keeps a byte per (256-key tile, query) in LDS: L <= 124 * 256 when d > 128
+    L, d = 124 * 256 + 1, 192
+    n = L * d * 2
+    assert fwd(q=A, k=A + n, v=A + 2 * n, out=A + 3 * n, L=L, d=d) == _lib.ATTN_ERR_TOO_LARGE
+
+
 def test_check_order_is_documented():
     # shape before head dim before scale before emptiness before pointers
     assert fwd(B=-1, d=48) == _lib.ATTN_ERR_BAD_SHAPE

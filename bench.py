@@ -100,7 +100,22 @@ def main() -> int:
     ap.add_argument("--workload", default="wan_31frame")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only copy 256 MiB device-to-device three times (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        import torch
+        n = 256 << 20
+        src = torch.empty(n // 2, dtype=torch.bfloat16, device="cuda:0").normal_()
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 3 copies of {n} bytes")
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

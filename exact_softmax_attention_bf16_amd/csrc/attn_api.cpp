@@ -117,7 +117,7 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, int64_t
 
   auto r256 = [](int64_t x) { return (x + 255) / 256 * 256; };
   const int64_t e_bytes = r256((int64_t)t.L * t.Ls * 2) * chunk;
-  const int64_t vt_bytes = r256((int64_t)t.d * t.Lk * 2) * chunk;
+  const int64_t vt_bytes = r256((int64_t)t.d * t.Ls * 2) * chunk;
   const int64_t st_bytes = r256((int64_t)t.T * t.L * 4) * chunk;
   char* base = (char*)ws;
   void* E = base;

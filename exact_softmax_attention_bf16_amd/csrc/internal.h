@@ -11,8 +11,9 @@ struct TwoPassDims {
   int L;   // sequence length
   int d;   // head dimension
   int T;   // number of 256-key score tiles: ceil(L / 256)
-  int Ls;  // row stride of the exponent matrix E: T * 256
-  int Lk;  // row stride of V^T: ceil(L / 64) * 64
+  int Ls;  // row stride of E and of V^T: 256 T + 128 (an odd multiple of 256 bytes,
+           // which spreads a tile's rows over the memory channels)
+  int Lk;  // keys the values pass iterates over: ceil(L / 64) * 64 (<= Ls)
 };
 
 TwoPassDims two_pass_dims(int64_t L, int64_t d);

@@ -34,7 +34,7 @@ TwoPassDims two_pass_dims(int64_t L, int64_t d) {
   t.L = (int)L;
   t.d = (int)d;
   t.T = (int)((L + kTile - 1) / kTile);
-  t.Ls = t.T * kTile;
+  t.Ls = t.T * kTile + kTile / 2;
   t.Lk = (int)((L + 63) / 64 * 64);
   return t;
 }
@@ -42,17 +42,17 @@ TwoPassDims two_pass_dims(int64_t L, int64_t d) {
 static int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
 int64_t two_pass_head_bytes(const TwoPassDims& t) {
-  return round256((int64_t)t.L * t.Ls * 2) + round256((int64_t)t.d * t.Lk * 2) +
+  return round256((int64_t)t.L * t.Ls * 2) + round256((int64_t)t.d * t.Ls * 2) +
          2 * round256((int64_t)t.T * t.L * 4);
 }
 
 namespace {
 
 // ---------------------------------------------------------------------------
-// V [BH, L, d] -> V^T [BH, d, Lk] through a 64x64 LDS tile; keys >= L read as 0.
+// V [BH, L, d] -> V^T [BH, d, ldv] (keys [0, 64 nkb), zero past L) through a 64x64 LDS tile.
 __global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __restrict__ v,
                                                           uint16_t* __restrict__ vt, int L, int d,
-                                                          int Lk, int nkb, int ncb) {
+                                                          int ldv, int nkb, int ncb) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
   const int tid = threadIdx.x;
   const int per_head = nkb * ncb;
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __rest
     *(u32x4*)&tile[row][col8 * 8] = x;
   }
   __syncthreads();
-  uint16_t* dst = vt + (size_t)bh * d * Lk;
+  uint16_t* dst = vt + (size_t)bh * d * ldv;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int c = tid + 256 * i;
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __rest
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       w[e] = (unsigned)tile[8 * g + 2 * e][ch] | ((unsigned)tile[8 * g + 2 * e + 1][ch] << 16);
-    *(u32x4*)(dst + (size_t)(cb * 64 + ch) * Lk + kb * 64 + 8 * g) = w;
+    *(u32x4*)(dst + (size_t)(cb * 64 + ch) * ldv + kb * 64 + 8 * g) = w;
   }
 }
 
@@ -354,10 +354,10 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
     invl[j] = inv_l[sh.col[j]];
   }
 
-  const auto ra = make_rsrc(vt + (size_t)bh * d * Lk, (uint32_t)d * Lk * 2);
+  const auto ra = make_rsrc(vt + (size_t)bh * d * Ls, (uint32_t)d * Ls * 2);
   const auto rb = make_rsrc(E + (size_t)bh * L * Ls, (uint32_t)L * Ls * 2);
   f32x16 acc[4][4];
-  gemm_tile(acc, ra, (uint32_t)Lk, ct * kTile, rb, (uint32_t)Ls, qt * kTile, nk, sm, sh);
+  gemm_tile(acc, ra, (uint32_t)Ls, ct * kTile, rb, (uint32_t)Ls, qt * kTile, nk, sm, sh);
 
   // O[query][ch] = acc / l, rounded once to bf16; lane holds 4 consecutive channels per run.
   uint16_t* oh = out + (size_t)bh * L * d;
@@ -388,8 +388,8 @@ hipError_t launch_v_transpose(const void* v, void* vt, int BH, const TwoPassDims
   const int nkb = t.Lk / 64, ncb = t.d / 64;
   const uint16_t* vp = (const uint16_t*)v;
   uint16_t* vtp = (uint16_t*)vt;
-  int L = t.L, d = t.d, Lk = t.Lk;
-  void* args[] = {&vp, &vtp, &L, &d, &Lk, (void*)&nkb, (void*)&ncb};
+  int L = t.L, d = t.d, ldv = t.Ls;
+  void* args[] = {&vp, &vtp, &L, &d, &ldv, (void*)&nkb, (void*)&ncb};
   return hipLaunchKernel((const void*)&v_transpose_kernel, dim3((unsigned)(BH * nkb * ncb)),
                          dim3(256), args, 0, s);
 }

@@ -53,7 +53,7 @@ def kernel_flops(name: str, w) -> int:
     pairs = w.L * (w.L + 1) // 2 if w.causal else w.L * w.L
     per_contraction = 2 * w.B * w.H * pairs * w.d
     return {"online": 2 * per_contraction, "scores": per_contraction,
-            "values": per_contraction, "v_transpose": 0}[name]
+            "values": per_contraction}[name]
 
 
 def measured_traffic(kernel: str, workload: str, launches_per_step: float):

@@ -117,13 +117,11 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, int64_t
 
   auto r256 = [](int64_t x) { return (x + 255) / 256 * 256; };
   const int64_t e_bytes = r256((int64_t)t.L * t.Ls * 2) * chunk;
-  const int64_t vt_bytes = r256((int64_t)t.d * t.Ls * 2) * chunk;
   const int64_t st_bytes = r256((int64_t)t.T * t.L * 4) * chunk;
   char* base = (char*)ws;
   void* E = base;
-  void* vt = base + e_bytes;
-  float* mref = (float*)(base + e_bytes + vt_bytes);
-  float* psum = (float*)(base + e_bytes + vt_bytes + st_bytes);
+  float* mref = (float*)(base + e_bytes);
+  float* psum = (float*)(base + e_bytes + st_bytes);
 
   const int64_t head_elems = L * d;
   hipError_t err = hipSuccess;
@@ -133,15 +131,12 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, int64_t
     const uint16_t* kc = (const uint16_t*)k + h0 * head_elems;
     const uint16_t* vc = (const uint16_t*)v + h0 * head_elems;
     uint16_t* oc = (uint16_t*)out + h0 * head_elems;
-    err = timed(ATTN_KERNEL_V_TRANSPOSE, stream, on,
-                [&] { return attn::launch_v_transpose(vc, vt, n, t, stream); });
-    if (err == hipSuccess)
-      err = timed(ATTN_KERNEL_SCORES, stream, on, [&] {
-        return attn::launch_scores(qc, kc, E, mref, psum, n, t, sl2, causal, stream);
-      });
+    err = timed(ATTN_KERNEL_SCORES, stream, on, [&] {
+      return attn::launch_scores(qc, kc, E, mref, psum, n, t, sl2, causal, stream);
+    });
     if (err == hipSuccess)
       err = timed(ATTN_KERNEL_VALUES, stream, on, [&] {
-        return attn::launch_values(vt, E, mref, psum, oc, n, t, causal, stream);
+        return attn::launch_values(vc, E, mref, psum, oc, n, t, causal, stream);
       });
   }
   const hipError_t ferr = hipFreeAsync(ws, stream);

@@ -15,7 +15,8 @@
 // run.  In the last sub-step the wave waits for its own loads of the next
 // stage, the workgroup meets at one barrier (next stage complete everywhere,
 // current stage no longer read), the loads two steps ahead are issued into
-// the stage just drained, and the first fragments of the next step are read.
+// the stage just drained in one burst (measured faster than spreading them
+// between the MFMAs), and the first fragments of the next step are read.
 #pragma once
 
 #include "device.h"
@@ -31,8 +32,11 @@ struct GemmSmem {
   char b[2][kStageBytes];
 };
 
-// Per-lane byte offsets of the 8 chunks this lane copies for one operand, at k = 0.
-struct TileLoader {
+// Operand stored K-contiguous in global memory (row r, K index k at r * ld + k).
+// Its stage holds 256 rows x 64 K values; each 128-byte LDS row keeps eight
+// 16-byte chunks at chunk ^ (row % 8).  Per-lane byte offsets of the 8 chunks
+// this lane copies, at k = 0.
+struct KContiguous {
   __amdgpu_buffer_rsrc_t r;
   uint32_t off[8];
 
@@ -52,11 +56,53 @@ struct TileLoader {
     for (int j = 0; j < 8; ++j)
       load16_to_lds(r, stage + (wave * 8 + j) * 1024, off[j] + (uint32_t)k0 * 2u);
   }
+  // MFMA fragment: lane supplies row rbase + lane % 32, K values 16 ss + 8 (lane / 32) .. + 8.
+  __device__ __forceinline__ bf16x8 frag(const char* stage, int rbase, int ss, int lane) const {
+    const int row = rbase + (lane & 31), lc = 2 * ss + (lane >> 5);
+    return *(const bf16x8*)(stage + row * 128 + ((lc ^ (row & 7)) << 4));
+  }
 };
 
-__device__ __forceinline__ bf16x8 gemm_frag(const char* stage, int row, int lc) {
-  return *(const bf16x8*)(stage + row * 128 + ((lc ^ (row & 7)) << 4));
-}
+// Operand A stored with K as the outer index (A[m][k] at k * ld + m), e.g. V read
+// as the A operand of O^T = V^T E^T.  Its stage holds 64 K rows x 256 m values
+// (512 bytes per row, 16-byte chunk c at c ^ 4 (row % 4)).  Fragments are built
+// with two ds_read_b64_tr_b16: in each 16-lane group, lane L reads the 4 values
+// A[m0 + 4 (L % 4) ..][k0 + L / 4] and the hardware hands lane i the 4 K values
+// of column m0 + i.
+struct KOuter {
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t off[8];
+  uint32_t ld2;  // bytes per K row
+
+  __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t rsrc, uint32_t ld, int m0, int wave,
+                                       int lane) {
+    r = rsrc;
+    ld2 = ld * 2u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int P = (wave * 8 + j) * 64 + lane;  // 16-byte chunk slot in the stage
+      const int row = P >> 5, pc = P & 31, lc = pc ^ ((row & 3) << 2);
+      off[j] = (uint32_t)row * ld2 + (uint32_t)(m0 + lc * 8) * 2u;
+    }
+  }
+  __device__ __forceinline__ void issue(int k0, char* stage, int wave) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      load16_to_lds(r, stage + (wave * 8 + j) * 1024, off[j] + (uint32_t)k0 * ld2);
+  }
+  __device__ __forceinline__ bf16x8 frag(const char* stage, int mbase, int ss, int lane) const {
+    const int g = lane >> 4, L = lane & 15;
+    const int m = mbase + (g & 1) * 16 + 4 * (L & 3);
+    const int row = 16 * ss + 8 * (g >> 1) + (L >> 2);
+    auto at = [&](int rr) {
+      return (short4_lds*)(stage + rr * 512 + (((m >> 3) ^ ((rr & 3) << 2)) << 4) + (m & 7) * 2);
+    };
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(row));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(row + 4));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
 
 struct NoTransform {
   __device__ __forceinline__ void step(int) {}
@@ -67,12 +113,13 @@ struct Frags {
   bf16x8 a[4], b[4];
 };
 
-__device__ __forceinline__ void read_frags(Frags& f, const char* sa, const char* sb, int wm, int wn,
-                                           int c32, int h, int ss) {
+template <class LA, class LB>
+__device__ __forceinline__ void read_frags(Frags& f, const LA& la, const LB& lb, const char* sa,
+                                           const char* sb, int wm, int wn, int lane, int ss) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = gemm_frag(sa, wm * 128 + i * 32 + c32, 2 * ss + h);
+  for (int i = 0; i < 4; ++i) f.a[i] = la.frag(sa, wm * 128 + i * 32, ss, lane);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = gemm_frag(sb, wn * 128 + j * 32 + c32, 2 * ss + h);
+  for (int j = 0; j < 4; ++j) f.b[j] = lb.frag(sb, wn * 128 + j * 32, ss, lane);
 }
 
 template <class BX>
@@ -112,20 +159,22 @@ __device__ __forceinline__ void block_sync() {
 }
 
 // acc[i][j] = A[m0 + 128 wm + 32 i + .., 0:64 nk] . B[n0 + 128 wn + 32 j + .., 0:64 nk].
+// LA is the layout policy of A (KContiguous or KOuter), B is K-contiguous.
 // `bx.step(kt)` runs before step kt's MFMAs; `bx(frag, j)` may rewrite each B fragment.
-template <class BX>
+template <class LA, class BX>
 __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_rsrc_t ra,
                                           uint32_t lda, int m0, __amdgpu_buffer_rsrc_t rb,
                                           uint32_t ldb, int n0, int nk, GemmSmem& sm, BX& bx) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, c32 = lane & 31, h = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-  TileLoader la, lb;
+  LA la;
+  KContiguous lb;
   la.init(ra, lda, m0, wave, lane);
   lb.init(rb, ldb, n0, wave, lane);
 
@@ -139,7 +188,7 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
   lb.issue(k1, sm.b[1], wave);
 
   Frags cur, nxt;
-  read_frags(cur, sm.a[0], sm.b[0], wm, wn, c32, h, 0);
+  read_frags(cur, la, lb, sm.a[0], sm.b[0], wm, wn, lane, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
     const char* sa = sm.a[st];
@@ -147,7 +196,7 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
     bx.step(kt);
 #pragma unroll
     for (int ss = 0; ss < 3; ++ss) {
-      read_frags(nxt, sa, sb, wm, wn, c32, h, ss + 1);
+      read_frags(nxt, la, lb, sa, sb, wm, wn, lane, ss + 1);
       mma_substep(acc, cur, bx);
       sched_substep(false);
       cur = nxt;
@@ -158,9 +207,10 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
     const int k2 = (kt + 2 < nk ? kt + 2 : nk - 1) * kStepK;  // past the end: reload, unused
     la.issue(k2, sm.a[st], wave);
     lb.issue(k2, sm.b[st], wave);
-    read_frags(nxt, sm.a[st ^ 1], sm.b[st ^ 1], wm, wn, c32, h, 0);
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out as one burst, ahead of the MFMAs
+    read_frags(nxt, la, lb, sm.a[st ^ 1], sm.b[st ^ 1], wm, wn, lane, 0);
     mma_substep(acc, cur, bx);
-    sched_substep(true);
+    sched_substep(false);
     cur = nxt;
   }
   wait_vmem();  // no LDS writes in flight past the loop

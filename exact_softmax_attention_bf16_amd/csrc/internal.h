@@ -11,8 +11,8 @@ struct TwoPassDims {
   int L;   // sequence length
   int d;   // head dimension
   int T;   // number of 256-key score tiles: ceil(L / 256)
-  int Ls;  // row stride of E and of V^T: 256 T + 128 (an odd multiple of 256 bytes,
-           // which spreads a tile's rows over the memory channels)
+  int Ls;  // row stride of E: 256 T + 128 (an odd multiple of 256 bytes, which
+           // spreads a tile's rows over the memory channels)
   int Lk;  // keys the values pass iterates over: ceil(L / 64) * 64 (<= Ls)
 };
 
@@ -22,17 +22,13 @@ TwoPassDims two_pass_dims(int64_t L, int64_t d);
 // LDS next to the 128 KB GEMM stages, which caps L at 124 * 256 = 31744 there.
 constexpr int kTwoPassMaxTiles = 124;
 
-// Bytes of workspace one head needs on the two-pass path: E, V^T, and the
+// Bytes of workspace one head needs on the two-pass path: E and the
 // per-(tile, query) exponent reference and partial sum.
 int64_t two_pass_head_bytes(const TwoPassDims& t);
 
 // Fused online-softmax kernel, d in {32, 64, 128}.  sl2 = scale * log2(e).
 hipError_t launch_online(const void* q, const void* k, const void* v, void* out, int BH, int L,
                          int d, float sl2, bool causal, hipStream_t s);
-
-// V [BH, L, d] -> V^T [BH, d, Lk], zero past L.
-hipError_t launch_v_transpose(const void* v, void* vt, int BH, const TwoPassDims& t,
-                              hipStream_t s);
 
 // Scores pass: per 256x256 (key, query) tile, E = bf16(2^(y - m)) with
 // y = sl2 * q.k, m = ceil(max over the tile's keys of y) per query, plus m and
@@ -41,7 +37,7 @@ hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, flo
                          const TwoPassDims& t, float sl2, bool causal, hipStream_t s);
 
 // Values pass: O = (sum over tiles of 2^(m_t - M) E_t V_t) / (sum_t 2^(m_t - M) psum_t).
-hipError_t launch_values(const void* vt, const void* E, const float* mref, const float* psum,
+hipError_t launch_values(const void* v, const void* E, const float* mref, const float* psum,
                          void* out, int BH, const TwoPassDims& t, bool causal, hipStream_t s);
 
 }  // namespace attn

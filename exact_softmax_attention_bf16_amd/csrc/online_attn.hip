@@ -31,6 +31,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // queries per workgroup
 constexpr int kBN = 64;           // keys per step
+constexpr float kLazy = 8.f;      // reference slack (log2 units) before O is rescaled
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void online_attn_kernel(const uint16_t* __restrict__ q,
@@ -145,44 +146,62 @@ __global__ __launch_bounds__(256) void online_attn_kernel(const uint16_t* __rest
           s[kb] = mfma32x32x16(a, qf[ss], s[kb]);
         }
       }
-      // Softmax update for this lane's query over its 32 of the 64 keys.
+      // Softmax update for this lane's query over its 32 of the 64 keys.  The
+      // maximum is taken on the raw scores (scaled afterwards; the sign of sl2
+      // picks max or min), and y - m is one FMA: p = 2^(s * sl2 - m).
       const bool need_mask = (kbase + kBN > L) || (CAUSAL && kbase + kBN - 1 > q0);
-      float tmax = -INFINITY;
+      float tmax;
+      if (need_mask) {
+        tmax = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float y = s[kb][j] * sl2;
-          if (need_mask) {
+          for (int j = 0; j < 16; ++j) {
             const int key = kbase + kb * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-            if (key >= L || (CAUSAL && key > myq)) y = -INFINITY;
+            const bool off = key >= L || (CAUSAL && key > myq);
+            s[kb][j] = off ? -INFINITY : s[kb][j] * sl2;
+            tmax = fmaxf(tmax, s[kb][j]);
           }
-          s[kb][j] = y;
-          tmax = fmaxf(tmax, y);
         }
+      } else {
+        float hi = s[0][0], lo = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            hi = fmaxf(hi, s[kb][j]);
+            lo = fminf(lo, s[kb][j]);
+          }
+        tmax = sl2 >= 0.f ? hi * sl2 : lo * sl2;
       }
       tmax = wave_swap32_max(tmax);
-      const float mnew = fmaxf(m, tmax);
-      const float muse = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2_fast(m - muse);
-      m = mnew;
+      // Lazy reference: m moves only when this block's maximum exceeds it by more
+      // than kLazy (log2 units), so most blocks skip the rescale of O.  P and l
+      // always use the same reference, so the result is unchanged; p <= 2^kLazy.
+      const bool grow = tmax > m + kLazy;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float mnew = grow ? tmax : m;
+        const float alpha = m == -INFINITY ? 0.f : exp2_fast(m - mnew);
+        m = mnew;
+        lsum *= alpha;
+#pragma unroll
+        for (int c = 0; c < NCB; ++c)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) o[c][j] *= alpha;
+      }
+      const float muse = m == -INFINITY ? 0.f : m;
+      const float mul = need_mask ? 1.f : sl2;
       unsigned pk[2][8];
-      float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int j = 0; j < 16; j += 2) {
-          const float p0 = exp2_fast(s[kb][j] - muse);
-          const float p1 = exp2_fast(s[kb][j + 1] - muse);
-          rs += p0 + p1;
+          const float p0 = exp2_fast(fmaf(s[kb][j], mul, -muse));
+          const float p1 = exp2_fast(fmaf(s[kb][j + 1], mul, -muse));
           pk[kb][j >> 1] = pack_bf16x2(p0, p1);
+          lsum = add_bf16x2(pk[kb][j >> 1], lsum);  // sum of the rounded P actually used
         }
       }
-      lsum = lsum * alpha + rs;
-#pragma unroll
-      for (int c = 0; c < NCB; ++c)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o[c][j] *= alpha;
       // O^T += V^T P^T.  MFMA (kb, u) covers keys kb*32 + 16u + {4h..4h+3, 8+4h..8+4h+3}
       // in lane half h: exactly the S^T registers 8u..8u+7 of block kb.
 #pragma unroll

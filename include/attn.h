@@ -70,8 +70,8 @@ enum {
  *
  * Returns ATTN_OK or one of the codes above.  For d > 128 the call draws a
  * workspace from a per-device stream-ordered pool and returns it on `stream`
- * after the last kernel (about 2*L*ceil(L/256)*256 + 2*d*ceil(L/64)*64 bytes
- * per head, heads processed in chunks of at most 2 GiB).
+ * after the last kernel (about 2*L*(256*ceil(L/256) + 128) + 8*L*ceil(L/256)
+ * bytes per head, heads processed in chunks of at most 2 GiB).
  */
 int attn_forward(const void* q, const void* k, const void* v, void* out,
                  int64_t B, int64_t H, int64_t L, int64_t d,
@@ -96,11 +96,10 @@ int64_t attn_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int cau
  * id < n (ids below), and forgets the records.  Returns a status code.
  */
 enum {
-  ATTN_KERNEL_ONLINE = 0,      /* fused online-softmax kernel (d <= 128)        */
-  ATTN_KERNEL_V_TRANSPOSE = 1, /* two-pass path: V -> V^T staging              */
-  ATTN_KERNEL_SCORES = 2,      /* two-pass path: S = QK^T tiles -> bf16 exp + stats */
-  ATTN_KERNEL_VALUES = 3,      /* two-pass path: O = P V with the row normalisation */
-  ATTN_KERNEL_COUNT = 4
+  ATTN_KERNEL_ONLINE = 0,  /* fused online-softmax kernel (d <= 128)              */
+  ATTN_KERNEL_SCORES = 1,  /* two-pass path: S = QK^T tiles -> bf16 exp + stats   */
+  ATTN_KERNEL_VALUES = 2,  /* two-pass path: O = P V with the row normalisation   */
+  ATTN_KERNEL_COUNT = 3
 };
 int attn_timing_enable(int enable);
 int attn_timing_collect(double* sum_ms, int64_t* launches, int n);

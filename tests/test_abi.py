@@ -62,12 +62,11 @@ def test_path_for_head_dim(d, path):
 
 
 def test_workspace_bytes():
-    # per head: E (L rows) and V^T (d rows), bf16, both with row stride 256*T + 128
-    # elements (T = ceil(L/256)), and two fp32 [T, L] tables
+    # per head: E (L rows of 256*T + 128 bf16, T = ceil(L/256)) and two fp32 [T, L] tables
     L, d, T = 3432, 1024, 14
     ls = 256 * T + 128
     r = lambda x: (x + 255) // 256 * 256
-    per_head = r(L * ls * 2) + r(d * ls * 2) + 2 * r(T * L * 4)
+    per_head = r(L * ls * 2) + 2 * r(T * L * 4)
     assert eab.workspace_bytes(1, 1, L, d) == per_head
     assert eab.workspace_bytes(31, 1, L, d) == 31 * per_head
     assert eab.workspace_bytes(4, 8, 1024, 64) == 0       # online path: none

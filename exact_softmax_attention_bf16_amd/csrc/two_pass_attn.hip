@@ -18,7 +18,9 @@
 //
 // So S never leaves the registers in fp32, E is written once in bf16 (the
 // pages' P rounding point), the normaliser sums exactly the values the second
-// contraction uses, and there is no extra pass over S or P.  The subtraction of
+// contraction uses, and there is no extra pass over S or P.  V is read in place:
+// the values pass stages V rows in LDS and builds its MFMA operand with the
+// gfx950 transpose read (ds_read_b64_tr_b16), so no V^T copy is made.  The subtraction of
 // a per-tile reference before the exponential is the stable softmax of the
 // attn.cu row_softmax_kernel and of the FMHA example's softmax_step; the
 // rescale by 2^(m_t - M) is that example's correction step, done once per
@@ -42,44 +44,10 @@ TwoPassDims two_pass_dims(int64_t L, int64_t d) {
 static int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
 int64_t two_pass_head_bytes(const TwoPassDims& t) {
-  return round256((int64_t)t.L * t.Ls * 2) + round256((int64_t)t.d * t.Ls * 2) +
-         2 * round256((int64_t)t.T * t.L * 4);
+  return round256((int64_t)t.L * t.Ls * 2) + 2 * round256((int64_t)t.T * t.L * 4);
 }
 
 namespace {
-
-// ---------------------------------------------------------------------------
-// V [BH, L, d] -> V^T [BH, d, ldv] (keys [0, 64 nkb), zero past L) through a 64x64 LDS tile.
-__global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __restrict__ v,
-                                                          uint16_t* __restrict__ vt, int L, int d,
-                                                          int ldv, int nkb, int ncb) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][72];
-  const int tid = threadIdx.x;
-  const int per_head = nkb * ncb;
-  const int bh = blockIdx.x / per_head;
-  const int r = blockIdx.x % per_head;
-  const int kb = r / ncb, cb = r % ncb;
-  const auto rv = make_rsrc(v + (size_t)bh * L * d, (uint32_t)L * d * 2);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i;
-    const int row = c >> 3, col8 = c & 7;
-    const u32x4 x = load16(rv, (uint32_t)((kb * 64 + row) * d + cb * 64 + col8 * 8) * 2);
-    *(u32x4*)&tile[row][col8 * 8] = x;
-  }
-  __syncthreads();
-  uint16_t* dst = vt + (size_t)bh * d * ldv;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = tid + 256 * i;
-    const int ch = c >> 3, g = c & 7;
-    u32x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = (unsigned)tile[8 * g + 2 * e][ch] | ((unsigned)tile[8 * g + 2 * e + 1][ch] << 16);
-    *(u32x4*)(dst + (size_t)(cb * 64 + ch) * ldv + kb * 64 + 8 * g) = w;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Scores pass.  Tile (kt, qt) of head bh: keys [256 kt, +256) on the M side,
@@ -241,7 +209,8 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
 
   f32x16 acc[4][4];
   NoTransform nx;
-  gemm_tile(acc, rk, (uint32_t)d, kt * kTile, rq, (uint32_t)d, qt * kTile, d / kStepK, sm, nx);
+  gemm_tile<KContiguous>(acc, rk, (uint32_t)d, kt * kTile, rq, (uint32_t)d, qt * kTile, d / kStepK,
+                         sm, nx);
 
   uint16_t* Eh = E + (size_t)bh * L * Ls;
   float* mref_t = mref + ((size_t)bh * T + kt) * L;
@@ -284,7 +253,7 @@ struct PowerOfTwoShift {
   }
 };
 
-__global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict__ vt,
+__global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict__ v,
                                                      const uint16_t* __restrict__ E,
                                                      const float* __restrict__ mref,
                                                      const float* __restrict__ psum,
@@ -354,45 +323,49 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
     invl[j] = inv_l[sh.col[j]];
   }
 
-  const auto ra = make_rsrc(vt + (size_t)bh * d * Ls, (uint32_t)d * Ls * 2);
+  const auto ra = make_rsrc(v + (size_t)bh * L * d, (uint32_t)L * d * 2);
   const auto rb = make_rsrc(E + (size_t)bh * L * Ls, (uint32_t)L * Ls * 2);
   f32x16 acc[4][4];
-  gemm_tile(acc, ra, (uint32_t)Ls, ct * kTile, rb, (uint32_t)Ls, qt * kTile, nk, sm, sh);
+  gemm_tile<KOuter>(acc, ra, (uint32_t)d, ct * kTile, rb, (uint32_t)Ls, qt * kTile, nk, sm, sh);
 
-  // O[query][ch] = acc / l, rounded once to bf16; lane holds 4 consecutive channels per run.
-  uint16_t* oh = out + (size_t)bh * L * d;
+  // O[query][ch] = acc / l, rounded once to bf16.  The tile goes through the
+  // drained GEMM stages as [query][256 channels] rows (16-byte chunk c of row r
+  // at c ^ (r % 32)) so that the global stores write whole row segments.
+  __syncthreads();  // every wave is past its GEMM: the stages are free
+  char* stage = sm.a[0];
 #pragma unroll
   for (int bj = 0; bj < 4; ++bj) {
-    const int query = qt * kTile + wn * 128 + bj * 32 + c32;
-    if (query >= L) continue;
+    const int ql = wn * 128 + bj * 32 + c32;
+    char* row = stage + ql * 512 + 8 * h;
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int ch = ct * kTile + wm * 128 + bi * 32 + 8 * i + 4 * h;
-        if (ch < d) {
-          const f32x16& a = acc[bi][bj];
-          u32x2 w = {pack_bf16x2(a[4 * i] * invl[bj], a[4 * i + 1] * invl[bj]),
-                     pack_bf16x2(a[4 * i + 2] * invl[bj], a[4 * i + 3] * invl[bj])};
-          *(u32x2*)(oh + (size_t)query * d + ch) = w;
-        }
+        const f32x16& a = acc[bi][bj];
+        const u32x2 w = {pack_bf16x2(a[4 * i] * invl[bj], a[4 * i + 1] * invl[bj]),
+                         pack_bf16x2(a[4 * i + 2] * invl[bj], a[4 * i + 3] * invl[bj])};
+        const int chunk = wm * 16 + bi * 4 + i;
+        *(u32x2*)(row + ((chunk ^ c32) << 4)) = w;
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const int c = tid & 31;
+    const int ch = ct * kTile + 8 * c;
+    if (ch < d) {
+      uint16_t* oh = out + (size_t)bh * L * d + (size_t)(qt * kTile) * d + ch;
+#pragma unroll 8
+      for (int j = 0; j < 32; ++j) {
+        const int r = (tid >> 5) + 8 * j;
+        if (qt * kTile + r < L)
+          *(u32x4*)(oh + (size_t)r * d) = *(const u32x4*)(stage + r * 512 + ((c ^ (r & 31)) << 4));
       }
     }
   }
 }
 
 }  // namespace
-
-hipError_t launch_v_transpose(const void* v, void* vt, int BH, const TwoPassDims& t,
-                              hipStream_t s) {
-  const int nkb = t.Lk / 64, ncb = t.d / 64;
-  const uint16_t* vp = (const uint16_t*)v;
-  uint16_t* vtp = (uint16_t*)vt;
-  int L = t.L, d = t.d, ldv = t.Ls;
-  void* args[] = {&vp, &vtp, &L, &d, &ldv, (void*)&nkb, (void*)&ncb};
-  return hipLaunchKernel((const void*)&v_transpose_kernel, dim3((unsigned)(BH * nkb * ncb)),
-                         dim3(256), args, 0, s);
-}
 
 hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, float* psum, int BH,
                          const TwoPassDims& t, float sl2, bool causal, hipStream_t s) {
@@ -405,9 +378,9 @@ hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, flo
                          args, 0, s);
 }
 
-hipError_t launch_values(const void* vt, const void* E, const float* mref, const float* psum,
+hipError_t launch_values(const void* v, const void* E, const float* mref, const float* psum,
                          void* out, int BH, const TwoPassDims& t, bool causal, hipStream_t s) {
-  const uint16_t* vtp = (const uint16_t*)vt;
+  const uint16_t* vtp = (const uint16_t*)v;
   const uint16_t* ep = (const uint16_t*)E;
   uint16_t* op = (uint16_t*)out;
   int L = t.L, d = t.d, T = t.T, Ls = t.Ls, Lk = t.Lk, c = causal ? 1 : 0;

@@ -6,9 +6,8 @@
 // Workgroup: 4 waves in a 2x2 grid, each wave owning a 128x128 block of C as
 // 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 registers per lane, held
 // in AGPRs).  The K loop runs in 64-wide steps through two LDS stages
-// (2 x 64 KB) filled by direct buffer->LDS loads.  Each 128-byte LDS row holds
-// eight 16-byte chunks stored at chunk ^ (row % 8), so the lanes that read one
-// column of chunks in a fragment load hit different bank groups.
+// (2 x 64 KB) filled by direct buffer->LDS loads, XOR-swizzled so that the
+// lanes that read one column of chunks in a fragment load hit different banks.
 //
 // Schedule per 64-wide step (4 sub-steps of k = 16, 16 MFMAs each): the
 // fragments of sub-step s + 1 are read from LDS while the MFMAs of sub-step s
@@ -34,8 +33,11 @@ struct GemmSmem {
 
 // Operand stored K-contiguous in global memory (row r, K index k at r * ld + k).
 // Its stage holds 256 rows x 64 K values; each 128-byte LDS row keeps eight
-// 16-byte chunks at chunk ^ (row % 8).  Per-lane byte offsets of the 8 chunks
-// this lane copies, at k = 0.
+// 16-byte chunks at chunk ^ swz(row), swz(row) = (row % 8) ^ ((row / 8) % 2):
+// the 8 or 16 consecutive rows one fragment read serves per LDS cycle then hit
+// distinct banks.  Per-lane byte offsets of the 8 chunks this lane copies, at k = 0.
+__device__ __forceinline__ int kc_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
 struct KContiguous {
   __amdgpu_buffer_rsrc_t r;
   uint32_t off[8];
@@ -46,7 +48,7 @@ struct KContiguous {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int P = (wave * 8 + j) * 64 + lane;  // 16-byte chunk slot in the stage
-      const int row = P >> 3, pc = P & 7, lc = pc ^ (row & 7);
+      const int row = P >> 3, pc = P & 7, lc = pc ^ kc_swz(row);
       off[j] = ((uint32_t)(r0 + row) * ld + (uint32_t)(lc * 8)) * 2u;
     }
   }
@@ -59,7 +61,7 @@ struct KContiguous {
   // MFMA fragment: lane supplies row rbase + lane % 32, K values 16 ss + 8 (lane / 32) .. + 8.
   __device__ __forceinline__ bf16x8 frag(const char* stage, int rbase, int ss, int lane) const {
     const int row = rbase + (lane & 31), lc = 2 * ss + (lane >> 5);
-    return *(const bf16x8*)(stage + row * 128 + ((lc ^ (row & 7)) << 4));
+    return *(const bf16x8*)(stage + row * 128 + ((lc ^ kc_swz(row)) << 4));
   }
 };
 

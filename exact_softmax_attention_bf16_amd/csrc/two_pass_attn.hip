@@ -49,6 +49,12 @@ int64_t two_pass_head_bytes(const TwoPassDims& t) {
 
 namespace {
 
+// A staged 16-byte chunk of tile row r holds its 8-byte halves swapped when
+// r % 32 >= 16; put them back in order.
+__device__ __forceinline__ u32x4 unswap_halves(u32x4 x, int r) {
+  return (r & 16) ? u32x4{x[2], x[3], x[0], x[1]} : x;
+}
+
 // ---------------------------------------------------------------------------
 // Scores pass.  Tile (kt, qt) of head bh: keys [256 kt, +256) on the M side,
 // queries [256 qt, +256) on the N side, so each lane of the accumulator owns a
@@ -127,7 +133,9 @@ __device__ __forceinline__ void scores_epilogue(const f32x16 (&acc)[4][4], float
   for (int bj = 0; bj < 4; ++bj) asm volatile("" : "+v"(lim[bj]));
 
   // E into LDS as [query][key] rows of 512 bytes; 16-byte chunk c of row r is
-  // stored at chunk c ^ (r % 32).
+  // stored at chunk c ^ (r % 32), with its two 8-byte halves swapped when
+  // r % 32 >= 16 (the 32 rows one write instruction touches then fill 32
+  // different bank pairs).
   float mt[4], ps[4];
 #pragma unroll
   for (int bj = 0; bj < 4; ++bj) {
@@ -136,7 +144,7 @@ __device__ __forceinline__ void scores_epilogue(const f32x16 (&acc)[4][4], float
     const float m2 = tmax == -INFINITY ? -INFINITY : ceilf(tmax);
     const float add = tmax == -INFINITY ? 0.f : -m2;
     float s = 0.f;
-    char* row = stage + ql * 512 + 8 * h;
+    char* row = stage + ql * 512 + 8 * (h ^ (c32 >> 4));
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
 #pragma unroll
@@ -170,7 +178,7 @@ __device__ __forceinline__ void scores_epilogue(const f32x16 (&acc)[4][4], float
     for (int j = 0; j < 32; ++j) {
       const int r = (tid >> 5) + 8 * j;
       if (qt * kTile + r < L)
-        *(u32x4*)(base + (size_t)r * Ls) = *(const u32x4*)(stage + r * 512 + ((c ^ (r & 31)) << 4));
+        *(u32x4*)(base + (size_t)r * Ls) = unswap_halves(*(const u32x4*)(stage + r * 512 + ((c ^ (r & 31)) << 4)), r);
     }
   }
   __syncthreads();  // partial sums complete
@@ -329,14 +337,14 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
   gemm_tile<KOuter>(acc, ra, (uint32_t)d, ct * kTile, rb, (uint32_t)Ls, qt * kTile, nk, sm, sh);
 
   // O[query][ch] = acc / l, rounded once to bf16.  The tile goes through the
-  // drained GEMM stages as [query][256 channels] rows (16-byte chunk c of row r
-  // at c ^ (r % 32)) so that the global stores write whole row segments.
+  // drained GEMM stages as [query][256 channels] rows (laid out like the E tile
+  // of the scores pass) so that the global stores write whole row segments.
   __syncthreads();  // every wave is past its GEMM: the stages are free
   char* stage = sm.a[0];
 #pragma unroll
   for (int bj = 0; bj < 4; ++bj) {
     const int ql = wn * 128 + bj * 32 + c32;
-    char* row = stage + ql * 512 + 8 * h;
+    char* row = stage + ql * 512 + 8 * (h ^ (c32 >> 4));
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
 #pragma unroll
@@ -359,7 +367,7 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
       for (int j = 0; j < 32; ++j) {
         const int r = (tid >> 5) + 8 * j;
         if (qt * kTile + r < L)
-          *(u32x4*)(oh + (size_t)r * d) = *(const u32x4*)(stage + r * 512 + ((c ^ (r & 31)) << 4));
+          *(u32x4*)(oh + (size_t)r * d) = unswap_halves(*(const u32x4*)(stage + r * 512 + ((c ^ (r & 31)) << 4)), r);
       }
     }
   }

@@ -16,6 +16,13 @@
 // current stage no longer read), the loads two steps ahead are issued into
 // the stage just drained in one burst (measured faster than spreading them
 // between the MFMAs), and the first fragments of the next step are read.
+//
+// The compiler guards LDS reads against direct-to-LDS loads still in flight:
+// a read it cannot prove disjoint from them gets a wait for all of them.
+// Ordinary reads of a kernel whose LDS is one object pass; the transpose
+// reads of the K-outer layout never do.  So for that layout all A fragments of
+// the next step are read before the burst is issued (held in registers for the
+// whole step), and no read after the burst is one the compiler would stall.
 #pragma once
 
 #include "device.h"
@@ -39,6 +46,7 @@ struct GemmSmem {
 __device__ __forceinline__ int kc_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 struct KContiguous {
+  static constexpr bool kWholeStepA = false;
   __amdgpu_buffer_rsrc_t r;
   uint32_t off[8];
 
@@ -72,6 +80,7 @@ struct KContiguous {
 // A[m0 + 4 (L % 4) ..][k0 + L / 4] and the hardware hands lane i the 4 K values
 // of column m0 + i.
 struct KOuter {
+  static constexpr bool kWholeStepA = true;  // fragments come from transpose reads
   __amdgpu_buffer_rsrc_t r;
   uint32_t off[8];
   uint32_t ld2;  // bytes per K row
@@ -160,6 +169,16 @@ __device__ __forceinline__ void block_sync() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Interleave 16 MFMAs with 4 LDS reads.
+__device__ __forceinline__ void sched_substep_b_only() {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
+  }
+}
+
 // acc[i][j] = A[m0 + 128 wm + 32 i + .., 0:64 nk] . B[n0 + 128 wn + 32 j + .., 0:64 nk].
 // LA is the layout policy of A (KContiguous or KOuter), B is K-contiguous.
 // `bx.step(kt)` runs before step kt's MFMAs; `bx(frag, j)` may rewrite each B fragment.
@@ -186,34 +205,74 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
   wait_vmem();
   block_sync();
   const int k1 = nk > 1 ? kStepK : 0;
-  la.issue(k1, sm.a[1], wave);
-  lb.issue(k1, sm.b[1], wave);
 
-  Frags cur, nxt;
-  read_frags(cur, la, lb, sm.a[0], sm.b[0], wm, wn, lane, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    const char* sa = sm.a[st];
-    const char* sb = sm.b[st];
-    bx.step(kt);
+  if constexpr (!LA::kWholeStepA) {
+    la.issue(k1, sm.a[1], wave);
+    lb.issue(k1, sm.b[1], wave);
+    Frags cur, nxt;
+    read_frags(cur, la, lb, sm.a[0], sm.b[0], wm, wn, lane, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & 1;
+      const char* sa = sm.a[st];
+      const char* sb = sm.b[st];
+      bx.step(kt);
 #pragma unroll
-    for (int ss = 0; ss < 3; ++ss) {
-      read_frags(nxt, la, lb, sa, sb, wm, wn, lane, ss + 1);
+      for (int ss = 0; ss < 3; ++ss) {
+        read_frags(nxt, la, lb, sa, sb, wm, wn, lane, ss + 1);
+        mma_substep(acc, cur, bx);
+        sched_substep(false);
+        cur = nxt;
+      }
+      // Last sub-step: next stage complete everywhere, this stage drained.
+      wait_vmem();
+      block_sync();
+      const int k2 = (kt + 2 < nk ? kt + 2 : nk - 1) * kStepK;  // past the end: reload, unused
+      la.issue(k2, sm.a[st], wave);
+      lb.issue(k2, sm.b[st], wave);
+      __builtin_amdgcn_sched_barrier(0);  // the loads go out as one burst, ahead of the MFMAs
+      read_frags(nxt, la, lb, sm.a[st ^ 1], sm.b[st ^ 1], wm, wn, lane, 0);
       mma_substep(acc, cur, bx);
       sched_substep(false);
       cur = nxt;
     }
-    // Last sub-step: next stage complete everywhere, this stage drained.
-    wait_vmem();
-    block_sync();
-    const int k2 = (kt + 2 < nk ? kt + 2 : nk - 1) * kStepK;  // past the end: reload, unused
-    la.issue(k2, sm.a[st], wave);
-    lb.issue(k2, sm.b[st], wave);
-    __builtin_amdgcn_sched_barrier(0);  // the loads go out as one burst, ahead of the MFMAs
-    read_frags(nxt, la, lb, sm.a[st ^ 1], sm.b[st ^ 1], wm, wn, lane, 0);
-    mma_substep(acc, cur, bx);
-    sched_substep(false);
-    cur = nxt;
+  } else {
+    // A fragments of a whole step in registers, read before each burst.
+    Frags f[4];  // f[ss].a: A of sub-step ss; f[ss].b: B of sub-step ss (as it arrives)
+    auto read_a_step = [&](Frags (&g)[4], const char* sa) {
+#pragma unroll
+      for (int ss = 0; ss < 4; ++ss)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g[ss].a[i] = la.frag(sa, wm * 128 + i * 32, ss, lane);
+    };
+    auto read_b = [&](bf16x8 (&b)[4], const char* sb, int ss) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = lb.frag(sb, wn * 128 + j * 32, ss, lane);
+    };
+    read_a_step(f, sm.a[0]);
+    read_b(f[0].b, sm.b[0], 0);
+    la.issue(k1, sm.a[1], wave);
+    lb.issue(k1, sm.b[1], wave);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & 1;
+      const char* sb = sm.b[st];
+      bx.step(kt);
+#pragma unroll
+      for (int ss = 0; ss < 3; ++ss) {
+        read_b(f[ss + 1].b, sb, ss + 1);
+        mma_substep(acc, f[ss], bx);
+        sched_substep_b_only();
+      }
+      const Frags last = f[3];
+      wait_vmem();
+      block_sync();
+      read_a_step(f, sm.a[st ^ 1]);
+      read_b(f[0].b, sm.b[st ^ 1], 0);
+      const int k2 = (kt + 2 < nk ? kt + 2 : nk - 1) * kStepK;  // past the end: reload, unused
+      la.issue(k2, sm.a[st], wave);
+      lb.issue(k2, sm.b[st], wave);
+      __builtin_amdgcn_sched_barrier(0);  // reads, then the burst, then the MFMAs
+      mma_substep(acc, last, bx);
+    }
   }
   wait_vmem();  // no LDS writes in flight past the loop
 }

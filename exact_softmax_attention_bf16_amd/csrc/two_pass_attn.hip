@@ -195,14 +195,26 @@ __device__ __forceinline__ void scores_epilogue(const f32x16 (&acc)[4][4], float
   }
 }
 
+// One LDS object per kernel: with a single object the compiler attaches no
+// alias scopes, and its LDS-DMA wait tracking then does not make the fragment
+// reads of one stage wait for the loads just issued into the other (with
+// several objects it does, and every K step stalls on the whole memory latency).
+// The stage protocol itself (wait for this wave's loads, then a barrier) is
+// explicit in the GEMM loop.
+struct ScoresSmem {
+  GemmSmem g;
+  float red[2][kTile];
+};
+
 __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict__ q,
                                                      const uint16_t* __restrict__ k,
                                                      uint16_t* __restrict__ E,
                                                      float* __restrict__ mref,
                                                      float* __restrict__ psum, int L, int d, int T,
                                                      int Ls, float sl2, int causal) {
-  __shared__ GemmSmem sm;
-  __shared__ float red[2][kTile];
+  __shared__ ScoresSmem smem;
+  GemmSmem& sm = smem.g;
+  float(&red)[2][kTile] = smem.red;
 
   const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int per_head = T * T;
@@ -261,15 +273,22 @@ struct PowerOfTwoShift {
   }
 };
 
+struct ValuesSmem {
+  GemmSmem g;
+  uint8_t shift_tab[kMaxTiles][kTile];
+  float inv_l[kTile];
+};
+
 __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict__ v,
                                                      const uint16_t* __restrict__ E,
                                                      const float* __restrict__ mref,
                                                      const float* __restrict__ psum,
                                                      uint16_t* __restrict__ out, int L, int d,
                                                      int T, int Ls, int Lk, int causal, int ncb) {
-  __shared__ GemmSmem sm;
-  __shared__ uint8_t shift_tab[kMaxTiles][kTile];
-  __shared__ float inv_l[kTile];
+  __shared__ ValuesSmem smem;
+  GemmSmem& sm = smem.g;
+  uint8_t(&shift_tab)[kMaxTiles][kTile] = smem.shift_tab;
+  float(&inv_l)[kTile] = smem.inv_l;
 
   const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int per_head = T * ncb;

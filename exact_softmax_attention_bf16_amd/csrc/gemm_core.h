@@ -62,9 +62,15 @@ struct KContiguous {
   }
   // Rows [r0, r0 + 256) x columns [k0, k0 + 64) into `stage`.
   __device__ __forceinline__ void issue(int k0, char* stage, int wave) const {
+    issue_from(r, k0, stage, wave);
+  }
+  // The same from another tensor of the same row stride (offsets as for r0 = 0
+  // when the resource starts at the tile's first row).
+  __device__ __forceinline__ void issue_from(__amdgpu_buffer_rsrc_t rs, int k0, char* stage,
+                                             int wave) const {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      load16_to_lds(r, stage + (wave * 8 + j) * 1024, off[j] + (uint32_t)k0 * 2u);
+      load16_to_lds(rs, stage + (wave * 8 + j) * 1024, off[j] + (uint32_t)k0 * 2u);
   }
   // MFMA fragment: lane supplies row rbase + lane % 32, K values 16 ss + 8 (lane / 32) .. + 8.
   __device__ __forceinline__ bf16x8 frag(const char* stage, int rbase, int ss, int lane) const {
@@ -75,10 +81,15 @@ struct KContiguous {
 
 // Operand A stored with K as the outer index (A[m][k] at k * ld + m), e.g. V read
 // as the A operand of O^T = V^T E^T.  Its stage holds 64 K rows x 256 m values
-// (512 bytes per row, 16-byte chunk c at c ^ 4 (row % 4)).  Fragments are built
-// with two ds_read_b64_tr_b16: in each 16-lane group, lane L reads the 4 values
+// (512 bytes per row, 16-byte chunk c at c ^ 4 (row % 4)).  Stage row r holds K
+// row k0 + kperm(r), kperm exchanging bits 2 and 3 of the index: the order the
+// scores pass gives the keys of each 32-key block of E, so that the B operand
+// (E, K-contiguous) and this one agree.  Fragments are built with two
+// ds_read_b64_tr_b16: in each 16-lane group, lane L reads the 4 values
 // A[m0 + 4 (L % 4) ..][k0 + L / 4] and the hardware hands lane i the 4 K values
 // of column m0 + i.
+__device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
 struct KOuter {
   static constexpr bool kWholeStepA = true;  // fragments come from transpose reads
   __amdgpu_buffer_rsrc_t r;
@@ -93,7 +104,7 @@ struct KOuter {
     for (int j = 0; j < 8; ++j) {
       const int P = (wave * 8 + j) * 64 + lane;  // 16-byte chunk slot in the stage
       const int row = P >> 5, pc = P & 31, lc = pc ^ ((row & 3) << 2);
-      off[j] = (uint32_t)row * ld2 + (uint32_t)(m0 + lc * 8) * 2u;
+      off[j] = (uint32_t)kperm(row) * ld2 + (uint32_t)(m0 + lc * 8) * 2u;
     }
   }
   __device__ __forceinline__ void issue(int k0, char* stage, int wave) const {
@@ -142,6 +153,14 @@ __device__ __forceinline__ void mma_substep(f32x16 (&acc)[4][4], const Frags& f,
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(f.a[i], b[j], acc[i][j]);
+}
+
+// The first sub-step of a tile: accumulators start from zero.
+__device__ __forceinline__ void mma_substep_first(f32x16 (&acc)[4][4], const Frags& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(f.a[i], f.b[j], f32x16{});
 }
 
 // Interleave 16 MFMAs with 8 LDS reads (and optionally 16 buffer loads).

@@ -25,6 +25,10 @@
 // attn.cu row_softmax_kernel and of the FMHA example's softmax_step; the
 // rescale by 2^(m_t - M) is that example's correction step, done once per
 // tile with exact factors.
+#include <algorithm>
+#include <atomic>
+#include <type_traits>
+
 #include "device.h"
 #include "gemm_core.h"
 #include "internal.h"
@@ -60,187 +64,263 @@ __device__ __forceinline__ u32x4 unswap_halves(u32x4 x, int r) {
 // queries [256 qt, +256) on the N side, so each lane of the accumulator owns a
 // query and holds 4 runs of 4 consecutive keys per 32x32 block.
 //
+// E layout: row `query` of head bh holds the tile's keys in blocks of 32; inside
+// a block, key c sits at position kperm(c) (bits 2 and 3 of c exchanged).  A
+// lane's 16 values of one 32x32 accumulator block are then two runs of 8
+// consecutive positions, stored straight from registers as two 16-byte writes
+// (the lanes of the other half-wave fill the 16 bytes between).  The values
+// pass reads V rows in the same order.
+//
 // Epilogue, per query: m = ceil(max over the tile's keys of y), y = sl2 * s;
 // E = bf16(2^(y - m)) (so 1/2 < max E <= 1); psum = sum of the stored E.
 // MASK selects the edge-tile version (keys past L, keys after the query); it is
 // a template flag so that the per-element test compiles to selects, not branches.
-// The E tile (256 queries x 256 keys) is staged through the drained GEMM stages
-// in LDS so that the global stores write whole 512-byte row segments.
+struct ScoresSmem {
+  GemmSmem g;
+  float red[2][kTile];   // per-wave-row partial maxima
+  float red2[2][kTile];  // per-wave-row partial sums
+};
+
+struct ScoresTile {
+  int bh, qt, kt;
+};
+
+// Tile idx of the pass: heads in order, then query tiles, then key tiles
+// (causal: only kt <= qt, row by row).
+__device__ __forceinline__ ScoresTile scores_tile(int idx, int T, int causal) {
+  ScoresTile t;
+  const int per_head = causal ? T * (T + 1) / 2 : T * T;
+  t.bh = idx / per_head;
+  const int r = idx - t.bh * per_head;
+  if (causal) {
+    int qt = (int)((sqrtf(8.f * (float)r + 1.f) - 1.f) * 0.5f);
+    while ((qt + 1) * (qt + 2) / 2 <= r) ++qt;
+    while (qt * (qt + 1) / 2 > r) --qt;
+    t.qt = qt;
+    t.kt = r - qt * (qt + 1) / 2;
+  } else {
+    t.qt = r / T;
+    t.kt = r - t.qt * T;
+  }
+  return t;
+}
+
 template <bool MASK>
-__device__ __forceinline__ void scores_epilogue(const f32x16 (&acc)[4][4], float (&red)[2][kTile],
-                                                char* __restrict__ stage,
-                                                uint16_t* __restrict__ Eh,
-                                                float* __restrict__ mref_t,
-                                                float* __restrict__ psum_t, int L, int Ls,
-                                                int kt, int qt, float sl2, int causal) {
+__device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][4], ScoresSmem& sm,
+                                                uint16_t* __restrict__ E,
+                                                float* __restrict__ mref,
+                                                float* __restrict__ psum, const ScoresTile& t,
+                                                int L, int Ls, int T, float sl2, int causal) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, c32 = lane & 31, h = lane >> 5;
-  const int key0 = kt * kTile + wm * 128;
-  // Key key0 + 4h + c (c = 32 bi + 8 (j / 4) + j % 4, a constant) is allowed for
-  // query column bj iff c < lim[bj].
-  int lim[4];
+  const int key0 = t.kt * kTile + wm * 128;
+  uint16_t* Eh = E + (size_t)t.bh * L * Ls;
+  float mt[4], ps[4];
+
+  // One column of accumulator blocks (32 queries) at a time, so that only its
+  // 64 values are held in ordinary registers: partial maximum over this wave's
+  // 128 keys, exchange with the wave holding the other 128 keys, exponentials.
 #pragma unroll
   for (int bj = 0; bj < 4; ++bj) {
-    const int query = qt * kTile + wn * 128 + bj * 32 + c32;
-    lim[bj] = (causal ? min(L, query + 1) : L) - (key0 + 4 * h);
-  }
-  auto masked = [&](int bi, int bj, int j) { return bi * 32 + 8 * (j >> 2) + (j & 3) >= lim[bj]; };
-
-  // Per-query maximum of y over this wave's 128 keys (interior tiles: on the
-  // raw accumulator, then scaled; the sign of sl2 picks max or min).
-  float wmax[4];
-  if (!MASK && sl2 >= 0.f) {
+    if (bj > 0) {
+      // Pass the column through acc + 0 * 0 (exact) with a zero the compiler
+      // cannot see before this point: otherwise it reads every column's
+      // accumulators ahead of the first barrier and keeps all 256 copies.
+      bf16x8 z = {};
+      asm volatile("" : "+v"(z));
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
+      for (int bi = 0; bi < 4; ++bi) acc[bi][bj] = mfma32x32x16(z, z, acc[bi][bj]);
+    }
+    const int ql = wn * 128 + bj * 32 + c32;
+    const int query = t.qt * kTile + ql;
+    // Key key0 + 4h + c (c = 32 bi + 8 (j / 4) + j % 4, a constant) is allowed
+    // for this query iff c < lim.
+    int lim = (causal ? min(L, query + 1) : L) - (key0 + 4 * h);
+    auto masked = [&](int bi, int j) { return bi * 32 + 8 * (j >> 2) + (j & 3) >= lim; };
+
+    // Maximum of y (interior tiles: on the raw accumulator, then scaled; the
+    // sign of sl2 picks max or min).
+    float wmax;
+    if (!MASK && sl2 >= 0.f) {
       float hi = acc[0][bj][0];
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
         for (int j = 0; j < 16; ++j) hi = fmaxf(hi, acc[bi][bj][j]);
-      wmax[bj] = hi * sl2;
-    }
-  } else if (!MASK) {
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
+      wmax = hi * sl2;
+    } else if (!MASK) {
       float lo = acc[0][bj][0];
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
         for (int j = 0; j < 16; ++j) lo = fminf(lo, acc[bi][bj][j]);
-      wmax[bj] = lo * sl2;
-    }
-  } else {
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
+      wmax = lo * sl2;
+    } else {
       float mx = -INFINITY;
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          mx = fmaxf(mx, masked(bi, bj, j) ? -INFINITY : acc[bi][bj][j] * sl2);
-      wmax[bj] = mx;
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, masked(bi, j) ? -INFINITY : acc[bi][bj][j] * sl2);
+      wmax = mx;
     }
-  }
-#pragma unroll
-  for (int bj = 0; bj < 4; ++bj) {
-    const float m = wave_swap32_max(wmax[bj]);
-    if (h == 0) red[wm][wn * 128 + bj * 32 + c32] = m;
-  }
-  __syncthreads();  // red complete; every wave is past its GEMM (the stages are free)
-  // Recompute the mask below instead of keeping 256 mask bits alive across the
-  // barrier (the compiler would otherwise hold them in scalar registers).
-#pragma unroll
-  for (int bj = 0; bj < 4; ++bj) asm volatile("" : "+v"(lim[bj]));
+    wmax = wave_swap32_max(wmax);
+    if (h == 0) sm.red[wm][ql] = wmax;
+    __syncthreads();  // both key halves' maxima for this column are in red
+    // Recompute the mask below instead of keeping 64 mask bits alive across the
+    // barrier (the compiler would otherwise hold them in scalar registers).
+    asm volatile("" : "+v"(lim));
 
-  // E into LDS as [query][key] rows of 512 bytes; 16-byte chunk c of row r is
-  // stored at chunk c ^ (r % 32), with its two 8-byte halves swapped when
-  // r % 32 >= 16 (the 32 rows one write instruction touches then fill 32
-  // different bank pairs).
-  float mt[4], ps[4];
-#pragma unroll
-  for (int bj = 0; bj < 4; ++bj) {
-    const int ql = wn * 128 + bj * 32 + c32;
-    const float tmax = fmaxf(red[0][ql], red[1][ql]);
+    const float tmax = fmaxf(sm.red[0][ql], sm.red[1][ql]);
     const float m2 = tmax == -INFINITY ? -INFINITY : ceilf(tmax);
     const float add = tmax == -INFINITY ? 0.f : -m2;
     float s = 0.f;
-    char* row = stage + ql * 512 + 8 * (h ^ (c32 >> 4));
+    uint16_t* row = Eh + (size_t)min(query, L - 1) * Ls + key0 + 8 * h;
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
+      u32x4 w[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float e[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           e[r] = exp2_fast(fmaf(acc[bi][bj][4 * i + r], sl2, add));
-          if (MASK) e[r] = masked(bi, bj, 4 * i + r) ? 0.f : e[r];
+          if (MASK) e[r] = masked(bi, 4 * i + r) ? 0.f : e[r];
         }
         const unsigned w0 = pack_bf16x2(e[0], e[1]), w1 = pack_bf16x2(e[2], e[3]);
         // the normaliser sums exactly the rounded values the values pass multiplies
         s = add_bf16x2(w1, add_bf16x2(w0, s));
-        const int chunk = wm * 16 + bi * 4 + i;
-        *(u32x2*)(row + ((chunk ^ c32) << 4)) = u32x2{w0, w1};
+        // keys 8 i + 4 h + 0..3 of the block sit at positions 16 (i / 2) + 8 h + 4 (i % 2) + 0..3
+        w[i >> 1][2 * (i & 1)] = w0;
+        w[i >> 1][2 * (i & 1) + 1] = w1;
+      }
+      if (query < L) {
+        *(u32x4*)(row + 32 * bi) = w[0];
+        *(u32x4*)(row + 32 * bi + 16) = w[1];
       }
     }
     mt[bj] = m2;
     ps[bj] = wave_swap32_sum(s);
+    __builtin_amdgcn_sched_barrier(0);  // keep the next column's copies after this one's
   }
-  __syncthreads();  // E tile complete in LDS; red no longer read
   if (h == 0) {
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) red[wm][wn * 128 + bj * 32 + c32] = ps[bj];
-  }
-  // Whole-row stores: thread t writes chunk t % 32 of rows t / 32 + 8 j.
-  {
-    const int c = tid & 31;
-    uint16_t* base = Eh + (size_t)(qt * kTile) * Ls + kt * kTile + 8 * c;
-#pragma unroll 8
-    for (int j = 0; j < 32; ++j) {
-      const int r = (tid >> 5) + 8 * j;
-      if (qt * kTile + r < L)
-        *(u32x4*)(base + (size_t)r * Ls) = unswap_halves(*(const u32x4*)(stage + r * 512 + ((c ^ (r & 31)) << 4)), r);
-    }
+    for (int bj = 0; bj < 4; ++bj) sm.red2[wm][wn * 128 + bj * 32 + c32] = ps[bj];
   }
   __syncthreads();  // partial sums complete
   if (wm == 0 && h == 0) {
+    float* mref_t = mref + ((size_t)t.bh * T + t.kt) * L;
+    float* psum_t = psum + ((size_t)t.bh * T + t.kt) * L;
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
       const int ql = wn * 128 + bj * 32 + c32;
-      const int query = qt * kTile + ql;
+      const int query = t.qt * kTile + ql;
       if (query < L) {
         mref_t[query] = mt[bj];
-        psum_t[query] = red[0][ql] + red[1][ql];
+        psum_t[query] = sm.red2[0][ql] + sm.red2[1][ql];
       }
     }
   }
 }
 
-// One LDS object per kernel: with a single object the compiler attaches no
-// alias scopes, and its LDS-DMA wait tracking then does not make the fragment
-// reads of one stage wait for the loads just issued into the other (with
-// several objects it does, and every K step stalls on the whole memory latency).
-// The stage protocol itself (wait for this wave's loads, then a barrier) is
-// explicit in the GEMM loop.
-struct ScoresSmem {
-  GemmSmem g;
-  float red[2][kTile];
-};
-
+// Persistent: workgroup g takes tiles g, g + G, g + 2G, ... (G = grid size; g
+// after the XCD renumbering, so each XCD works through a contiguous range).
+// The K steps of all its tiles form one stream through the two LDS stages:
+// the loads run two steps ahead across tile boundaries, so the next tile's
+// first stages arrive while this tile's epilogue computes and stores E.
+// One LDS object (see the GEMM loop's notes on the compiler's LDS-DMA waits).
 __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict__ q,
                                                      const uint16_t* __restrict__ k,
                                                      uint16_t* __restrict__ E,
                                                      float* __restrict__ mref,
                                                      float* __restrict__ psum, int L, int d, int T,
-                                                     int Ls, float sl2, int causal) {
+                                                     int Ls, float sl2, int causal, int ntiles) {
   __shared__ ScoresSmem smem;
   GemmSmem& sm = smem.g;
-  float(&red)[2][kTile] = smem.red;
 
-  const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int per_head = T * T;
-  const int bh = lid / per_head;
-  const int r = lid % per_head;
-  const int qt = r / T, kt = r % T;
-  if (causal && kt > qt) return;  // every key after every query of the tile
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int G = (int)gridDim.x;
+  const int first = (int)xcd_logical_id(blockIdx.x, gridDim.x);
+  const int my_tiles = (ntiles - 1 - first) / G + 1;  // first < ntiles
+  const int nk = d / kStepK;                          // >= 3 on this path
+  const int total = my_tiles * nk;
+  const uint32_t row_bytes = (uint32_t)d * 2u;
 
-  const uint32_t head_bytes = (uint32_t)L * d * 2;
-  const auto rq = make_rsrc(q + (size_t)bh * L * d, head_bytes);
-  const auto rk = make_rsrc(k + (size_t)bh * L * d, head_bytes);
+  KContiguous la, lb;  // per-lane offsets within a tile; resources start at its first row
+  la.init(make_rsrc(k, 0), (uint32_t)d, 0, wave, lane);
+  lb.init(make_rsrc(q, 0), (uint32_t)d, 0, wave, lane);
+
+  // Load cursor: the step (tile li, K step lk) whose loads go out next.
+  int li = 0, lk = 0;
+  __amdgpu_buffer_rsrc_t rk, rq;
+  auto set_load_tile = [&](int i) {
+    const ScoresTile t = scores_tile(first + i * G, T, causal);
+    const int k0 = t.kt * kTile, q0 = t.qt * kTile;
+    rk = make_rsrc(k + ((size_t)t.bh * L + k0) * d, (uint32_t)(L - k0) * row_bytes);
+    rq = make_rsrc(q + ((size_t)t.bh * L + q0) * d, (uint32_t)(L - q0) * row_bytes);
+  };
+  auto issue_next = [&](char* sa, char* sb) {
+    la.issue_from(rk, lk * kStepK, sa, wave);
+    lb.issue_from(rq, lk * kStepK, sb, wave);
+    if (++lk == nk) {
+      lk = 0;
+      if (++li < my_tiles) set_load_tile(li);
+    }
+  };
+
+  set_load_tile(0);
+  issue_next(sm.a[0], sm.b[0]);
+  wait_vmem();
+  block_sync();
+  issue_next(sm.a[1], sm.b[1]);  // total >= nk >= 3
 
   f32x16 acc[4][4];
   NoTransform nx;
-  gemm_tile<KContiguous>(acc, rk, (uint32_t)d, kt * kTile, rq, (uint32_t)d, qt * kTile, d / kStepK,
-                         sm, nx);
+  Frags cur, nxt;
+  read_frags(cur, la, lb, sm.a[0], sm.b[0], wm, wn, lane, 0);
 
-  uint16_t* Eh = E + (size_t)bh * L * Ls;
-  float* mref_t = mref + ((size_t)bh * T + kt) * L;
-  float* psum_t = psum + ((size_t)bh * T + kt) * L;
-  const bool need_mask = (kt + 1) * kTile > L || (causal && kt >= qt);
-  char* stage = sm.a[0];  // 128 KB of drained GEMM stages hold the E tile
-  if (need_mask)
-    scores_epilogue<true>(acc, red, stage, Eh, mref_t, psum_t, L, Ls, kt, qt, sl2, causal);
-  else
-    scores_epilogue<false>(acc, red, stage, Eh, mref_t, psum_t, L, Ls, kt, qt, sl2, causal);
+  // One K step s: sub-step 0 starts the accumulators when FIRST.
+  auto step = [&](auto first_step, int s) {
+    constexpr bool FIRST = decltype(first_step)::value;
+    const int st = s & 1;
+    const char* sa = sm.a[st];
+    const char* sb = sm.b[st];
+#pragma unroll
+    for (int ss = 0; ss < 3; ++ss) {
+      read_frags(nxt, la, lb, sa, sb, wm, wn, lane, ss + 1);
+      if (FIRST && ss == 0)
+        mma_substep_first(acc, cur);
+      else
+        mma_substep(acc, cur, nx);
+      sched_substep(false);
+      cur = nxt;
+    }
+    // Last sub-step: next stage complete everywhere, this stage drained.
+    wait_vmem();
+    block_sync();
+    if (s + 2 < total) issue_next(sm.a[st], sm.b[st]);
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out as one burst, ahead of the MFMAs
+    read_frags(nxt, la, lb, sm.a[st ^ 1], sm.b[st ^ 1], wm, wn, lane, 0);  // past the end: unused
+    mma_substep(acc, cur, nx);
+    sched_substep(false);
+    cur = nxt;
+  };
+
+  int s = 0;
+  for (int i = 0; i < my_tiles; ++i) {
+    step(std::true_type{}, s++);
+    for (int kk = 1; kk < nk; ++kk) step(std::false_type{}, s++);
+    const ScoresTile t = scores_tile(first + i * G, T, causal);
+    const bool need_mask = (t.kt + 1) * kTile > L || (causal && t.kt >= t.qt);
+    if (need_mask)
+      scores_epilogue<true>(acc, smem, E, mref, psum, t, L, Ls, T, sl2, causal);
+    else
+      scores_epilogue<false>(acc, smem, E, mref, psum, t, L, Ls, T, sl2, causal);
+    // The next step's first fragments: read again (its stage is not refilled
+    // before that step's end) instead of holding them through the epilogue.
+    read_frags(cur, la, lb, sm.a[s & 1], sm.b[s & 1], wm, wn, lane, 0);
+  }
+  wait_vmem();
 }
 
 // ---------------------------------------------------------------------------
@@ -394,15 +474,32 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
 
 }  // namespace
 
+// Compute units of the current device (cached per device).
+static int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, float* psum, int BH,
                          const TwoPassDims& t, float sl2, bool causal, hipStream_t s) {
   const uint16_t* qp = (const uint16_t*)q;
   const uint16_t* kp = (const uint16_t*)k;
   uint16_t* ep = (uint16_t*)E;
   int L = t.L, d = t.d, T = t.T, Ls = t.Ls, c = causal ? 1 : 0;
-  void* args[] = {&qp, &kp, &ep, &mref, &psum, &L, &d, &T, &Ls, &sl2, &c};
-  return hipLaunchKernel((const void*)&scores_kernel, dim3((unsigned)(BH * T * T)), dim3(256),
-                         args, 0, s);
+  int ntiles = BH * (causal ? T * (T + 1) / 2 : T * T);
+  const int grid = std::min(ntiles, device_cu_count());  // one workgroup per CU (LDS-bound)
+  void* args[] = {&qp, &kp, &ep, &mref, &psum, &L, &d, &T, &Ls, &sl2, &c, &ntiles};
+  return hipLaunchKernel((const void*)&scores_kernel, dim3((unsigned)grid), dim3(256), args, 0, s);
 }
 
 hipError_t launch_values(const void* v, const void* E, const float* mref, const float* psum,

@@ -188,14 +188,15 @@ __device__ __forceinline__ void block_sync() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Interleave 16 MFMAs with 4 LDS reads.
+// 16 MFMAs with 4 LDS reads early among them (the reads feed the next sub-step's
+// first MFMAs).
 __device__ __forceinline__ void sched_substep_b_only() {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
   }
+  __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);  // 12 MFMAs
 }
 
 // acc[i][j] = A[m0 + 128 wm + 32 i + .., 0:64 nk] . B[n0 + 128 wn + 32 j + .., 0:64 nk].

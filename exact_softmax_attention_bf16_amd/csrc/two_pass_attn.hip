@@ -259,13 +259,16 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
     rk = make_rsrc(k + ((size_t)t.bh * L + k0) * d, (uint32_t)(L - k0) * row_bytes);
     rq = make_rsrc(q + ((size_t)t.bh * L + q0) * d, (uint32_t)(L - q0) * row_bytes);
   };
-  auto issue_next = [&](char* sa, char* sb) {
-    la.issue_from(rk, lk * kStepK, sa, wave);
-    lb.issue_from(rq, lk * kStepK, sb, wave);
+  auto advance = [&]() {
     if (++lk == nk) {
       lk = 0;
       if (++li < my_tiles) set_load_tile(li);
     }
+  };
+  auto issue_next = [&](char* sa, char* sb) {
+    la.issue_from(rk, lk * kStepK, sa, wave);
+    lb.issue_from(rq, lk * kStepK, sb, wave);
+    advance();
   };
 
   set_load_tile(0);
@@ -298,12 +301,27 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
     // Last sub-step: next stage complete everywhere, this stage drained.
     wait_vmem();
     block_sync();
-    if (s + 2 < total) issue_next(sm.a[st], sm.b[st]);
-    __builtin_amdgcn_sched_barrier(0);  // the loads go out as one burst, ahead of the MFMAs
-    read_frags(nxt, la, lb, sm.a[st ^ 1], sm.b[st ^ 1], wm, wn, lane, 0);  // past the end: unused
-    mma_substep(acc, cur, nx);
-    sched_substep(false);
+    // This sub-step's MFMAs in pairs, each pair followed by one load of each
+    // operand for step s + 2 (past the end the cursor stays on the last tile: a
+    // reload into a stage no longer read), with the next step's first fragments
+    // read after the sixth pair.  Measured: loads as a burst right after the
+    // barrier, or those reads right after it, both cost a few percent.
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      if (p == 6) {
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(nxt, la, lb, sm.a[st ^ 1], sm.b[st ^ 1], wm, wn, lane, 0);  // past the end: unused
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const int i = p >> 1, j0 = 2 * (p & 1);
+      acc[i][j0] = mfma32x32x16(cur.a[i], cur.b[j0], acc[i][j0]);
+      acc[i][j0 + 1] = mfma32x32x16(cur.a[i], cur.b[j0 + 1], acc[i][j0 + 1]);
+      la.issue_one(rk, lk * kStepK, sm.a[st], wave, p);
+      lb.issue_one(rq, lk * kStepK, sm.b[st], wave, p);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     cur = nxt;
+    if (s + 2 < total) advance();
   };
 
   int s = 0;

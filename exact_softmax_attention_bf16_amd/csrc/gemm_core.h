@@ -1,7 +1,8 @@
-// gemm_core.h -- 256x256 bf16 MFMA tile, C = A B^T with both operands K-contiguous.
+// gemm_core.h -- 256x256 bf16 MFMA tiles for the large-head-dim path.
 //
-// Used by both passes of the large-head-dim path: the scores pass (A = K rows,
-// B = Q rows, K = d) and the values pass (A = V^T rows, B = E rows, K = keys).
+// Building blocks of both passes -- the scores pass (A = K rows, B = Q rows,
+// K = d; its own persistent loop) and the values pass (A = V read as V^T,
+// B = E rows, K = keys; gemm_tile below).
 //
 // Workgroup: 4 waves in a 2x2 grid, each wave owning a 128x128 block of C as
 // 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 registers per lane, held
@@ -13,16 +14,17 @@
 // fragments of sub-step s + 1 are read from LDS while the MFMAs of sub-step s
 // run.  In the last sub-step the wave waits for its own loads of the next
 // stage, the workgroup meets at one barrier (next stage complete everywhere,
-// current stage no longer read), the loads two steps ahead are issued into
-// the stage just drained in one burst (measured faster than spreading them
-// between the MFMAs), and the first fragments of the next step are read.
+// current stage no longer read), the first fragments of the next step are
+// read, and the loads two steps ahead go into the stage just drained, one
+// after each pair of the sub-step's MFMAs (issued as one burst they hold up
+// the MFMAs behind them while the address queue drains).
 //
 // The compiler guards LDS reads against direct-to-LDS loads still in flight:
 // a read it cannot prove disjoint from them gets a wait for all of them.
 // Ordinary reads of a kernel whose LDS is one object pass; the transpose
 // reads of the K-outer layout never do.  So for that layout all A fragments of
-// the next step are read before the burst is issued (held in registers for the
-// whole step), and no read after the burst is one the compiler would stall.
+// the next step are read before its loads are issued (held in registers for the
+// whole step), and no read after them is one the compiler would stall.
 #pragma once
 
 #include "device.h"
@@ -46,7 +48,6 @@ struct GemmSmem {
 __device__ __forceinline__ int kc_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 struct KContiguous {
-  static constexpr bool kWholeStepA = false;
   __amdgpu_buffer_rsrc_t r;
   uint32_t off[8];
 
@@ -116,6 +117,9 @@ struct KOuter {
     for (int j = 0; j < 8; ++j)
       load16_to_lds(r, stage + (wave * 8 + j) * 1024, off[j] + (uint32_t)k0 * ld2);
   }
+  __device__ __forceinline__ void issue_one(int k0, char* stage, int wave, int j) const {
+    load16_to_lds(r, stage + (wave * 8 + j) * 1024, off[j] + (uint32_t)k0 * ld2);
+  }
   __device__ __forceinline__ bf16x8 frag(const char* stage, int mbase, int ss, int lane) const {
     const int g = lane >> 4, L = lane & 15;
     const int m = mbase + (g & 1) * 16 + 4 * (L & 3);
@@ -167,23 +171,13 @@ __device__ __forceinline__ void mma_substep_first(f32x16 (&acc)[4][4], const Fra
     for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(f.a[i], f.b[j], f32x16{});
 }
 
-// Interleave 16 MFMAs with 8 LDS reads (and optionally 16 buffer loads).
-__device__ __forceinline__ void sched_substep(bool with_vmem) {
-  if (with_vmem) {
+// Interleave 16 MFMAs with 8 LDS reads.
+__device__ __forceinline__ void sched_substep() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // 2 VMEM reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-    }
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
   }
 }
 
@@ -203,13 +197,16 @@ __device__ __forceinline__ void sched_substep_b_only() {
   __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);  // 12 MFMAs
 }
 
-// acc[i][j] = A[m0 + 128 wm + 32 i + .., 0:64 nk] . B[n0 + 128 wn + 32 j + .., 0:64 nk].
-// LA is the layout policy of A (KContiguous or KOuter), B is K-contiguous.
+// acc[i][j] = A[m0 + 128 wm + 32 i + .., 0:64 nk] . B[n0 + 128 wn + 32 j + .., 0:64 nk]
+// with A in the K-outer layout (LA = KOuter) and B K-contiguous.  All A
+// fragments of a step are read right after the barrier, before that step's
+// loads go out (the transpose reads would otherwise wait for them).
 // `bx.step(kt)` runs before step kt's MFMAs; `bx(frag, j)` may rewrite each B fragment.
 template <class LA, class BX>
 __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_rsrc_t ra,
                                           uint32_t lda, int m0, __amdgpu_buffer_rsrc_t rb,
                                           uint32_t ldb, int n0, int nk, GemmSmem& sm, BX& bx) {
+  static_assert(LA::kWholeStepA, "the K loop below reads A a whole step at a time");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -230,73 +227,54 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
   block_sync();
   const int k1 = nk > 1 ? kStepK : 0;
 
-  if constexpr (!LA::kWholeStepA) {
-    la.issue(k1, sm.a[1], wave);
-    lb.issue(k1, sm.b[1], wave);
-    Frags cur, nxt;
-    read_frags(cur, la, lb, sm.a[0], sm.b[0], wm, wn, lane, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int st = kt & 1;
-      const char* sa = sm.a[st];
-      const char* sb = sm.b[st];
-      bx.step(kt);
+  Frags f[4];  // f[ss].a: A of sub-step ss; f[ss].b: B of sub-step ss (as it arrives)
+  auto read_a_step = [&](Frags (&g)[4], const char* sa) {
 #pragma unroll
-      for (int ss = 0; ss < 3; ++ss) {
-        read_frags(nxt, la, lb, sa, sb, wm, wn, lane, ss + 1);
-        mma_substep(acc, cur, bx);
-        sched_substep(false);
-        cur = nxt;
-      }
-      // Last sub-step: next stage complete everywhere, this stage drained.
-      wait_vmem();
-      block_sync();
-      const int k2 = (kt + 2 < nk ? kt + 2 : nk - 1) * kStepK;  // past the end: reload, unused
-      la.issue(k2, sm.a[st], wave);
-      lb.issue(k2, sm.b[st], wave);
-      __builtin_amdgcn_sched_barrier(0);  // the loads go out as one burst, ahead of the MFMAs
-      read_frags(nxt, la, lb, sm.a[st ^ 1], sm.b[st ^ 1], wm, wn, lane, 0);
-      mma_substep(acc, cur, bx);
-      sched_substep(false);
-      cur = nxt;
+    for (int ss = 0; ss < 4; ++ss)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g[ss].a[i] = la.frag(sa, wm * 128 + i * 32, ss, lane);
+  };
+  auto read_b = [&](bf16x8 (&b)[4], const char* sb, int ss) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = lb.frag(sb, wn * 128 + j * 32, ss, lane);
+  };
+  read_a_step(f, sm.a[0]);
+  read_b(f[0].b, sm.b[0], 0);
+  la.issue(k1, sm.a[1], wave);
+  lb.issue(k1, sm.b[1], wave);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    const char* sb = sm.b[st];
+    bx.step(kt);
+#pragma unroll
+    for (int ss = 0; ss < 3; ++ss) {
+      read_b(f[ss + 1].b, sb, ss + 1);
+      mma_substep(acc, f[ss], bx);
+      sched_substep_b_only();
     }
-  } else {
-    // A fragments of a whole step in registers, read before each burst.
-    Frags f[4];  // f[ss].a: A of sub-step ss; f[ss].b: B of sub-step ss (as it arrives)
-    auto read_a_step = [&](Frags (&g)[4], const char* sa) {
+    // Last sub-step: next stage complete everywhere, this stage drained.
+    const Frags last = f[3];
+    wait_vmem();
+    block_sync();
+    read_a_step(f, sm.a[st ^ 1]);
+    read_b(f[0].b, sm.b[st ^ 1], 0);
+    const int k2 = (kt + 2 < nk ? kt + 2 : nk - 1) * kStepK;  // past the end: reload, unused
+    // The reads above, then the sub-step's MFMAs in pairs with one load of each
+    // operand after each pair.
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 lbf[4];
 #pragma unroll
-      for (int ss = 0; ss < 4; ++ss)
+    for (int j = 0; j < 4; ++j) lbf[j] = bx(last.b[j], j);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) g[ss].a[i] = la.frag(sa, wm * 128 + i * 32, ss, lane);
-    };
-    auto read_b = [&](bf16x8 (&b)[4], const char* sb, int ss) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = lb.frag(sb, wn * 128 + j * 32, ss, lane);
-    };
-    read_a_step(f, sm.a[0]);
-    read_b(f[0].b, sm.b[0], 0);
-    la.issue(k1, sm.a[1], wave);
-    lb.issue(k1, sm.b[1], wave);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int st = kt & 1;
-      const char* sb = sm.b[st];
-      bx.step(kt);
-#pragma unroll
-      for (int ss = 0; ss < 3; ++ss) {
-        read_b(f[ss + 1].b, sb, ss + 1);
-        mma_substep(acc, f[ss], bx);
-        sched_substep_b_only();
-      }
-      const Frags last = f[3];
-      wait_vmem();
-      block_sync();
-      read_a_step(f, sm.a[st ^ 1]);
-      read_b(f[0].b, sm.b[st ^ 1], 0);
-      const int k2 = (kt + 2 < nk ? kt + 2 : nk - 1) * kStepK;  // past the end: reload, unused
-      la.issue(k2, sm.a[st], wave);
-      lb.issue(k2, sm.b[st], wave);
-      __builtin_amdgcn_sched_barrier(0);  // reads, then the burst, then the MFMAs
-      mma_substep(acc, last, bx);
+    for (int p = 0; p < 8; ++p) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int i = p >> 1, j0 = 2 * (p & 1);
+      acc[i][j0] = mfma32x32x16(last.a[i], lbf[j0], acc[i][j0]);
+      acc[i][j0 + 1] = mfma32x32x16(last.a[i], lbf[j0 + 1], acc[i][j0 + 1]);
+      la.issue_one(k2, sm.a[st], wave, p);
+      lb.issue_one(lb.r, k2, sm.b[st], wave, p);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
   wait_vmem();  // no LDS writes in flight past the loop
 }

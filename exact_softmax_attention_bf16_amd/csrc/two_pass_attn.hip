@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
         mma_substep_first(acc, cur);
       else
         mma_substep(acc, cur, nx);
-      sched_substep(false);
+      sched_substep();
       cur = nxt;
     }
     // Last sub-step: next stage complete everywhere, this stage drained.

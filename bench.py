@@ -92,6 +92,67 @@ def cpu_baseline(w, q, k, v, budget_s: float):
             "sample": f"{done} of {len(heads)} heads (L={w.L}, d={w.d}, all rows), {dt:.1f} s, float64"}
 
 
+def design_probe(args) -> int:
+    """The large-d alternative that materialises S, timed stage by stage.
+
+    S = Q K^T (bf16 out of hipBLASLt, half the bytes of the fp32 S the pages
+    write, so a lower bound), P = softmax(S) over keys (torch, fp32 inside,
+    bf16 out), O = P V.  The scale is folded into Q beforehand (exact for a
+    power of two).  Each stage is timed with events over the same calls."""
+    import torch
+
+    from exact_softmax_attention_bf16_amd import attention
+    from synth import WORKLOADS, make_qkv
+
+    w = WORKLOADS[args.workload]
+    if w.causal or w.d <= 128:
+        log("[probe] the probe covers the unmasked large-d workloads")
+        return 2
+    dev = torch.device("cuda:0")
+    q, k, v = make_qkv(w.B, w.H, w.L, w.d, w.seed)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(qd)
+    n = w.B * w.H
+    qs = (qd.float() * w.scale).to(torch.bfloat16).reshape(n, w.L, w.d)
+    kt = kd.reshape(n, w.L, w.d).transpose(1, 2).contiguous()  # bmm's right operand, contiguous
+    vv = vd.reshape(n, w.L, w.d)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    stages = {"s_gemm": 0.0, "softmax": 0.0, "pv_gemm": 0.0}
+    steps = max(args.steps // 5, 3)
+    for it in range(args.warmup + steps):
+        ev[0].record()
+        S = torch.bmm(qs, kt)
+        ev[1].record()
+        P = torch.softmax(S, dim=-1)
+        ev[2].record()
+        O = torch.bmm(P, vv)
+        ev[3].record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            for i, name in enumerate(stages):
+                stages[name] += ev[i].elapsed_time(ev[i + 1]) / steps
+        del S, P, O
+    for _ in range(args.warmup):
+        attention(qd, kd, vd, scale=w.scale, causal=False, out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        attention(qd, kd, vd, scale=w.scale, causal=False, out=out)
+    torch.cuda.synchronize()
+    ours = (time.perf_counter() - t0) * 1e3 / steps
+    s_bytes = n * w.L * w.L * 2  # one bf16 S (or P) tensor
+    line = {"probe": "materialised_S", "workload": w.name,
+            "s_gemm_ms": round(stages["s_gemm"], 4), "softmax_ms": round(stages["softmax"], 4),
+            "pv_gemm_ms": round(stages["pv_gemm"], 4),
+            "total_ms": round(sum(stages.values()), 4),
+            "softmax_pass_bytes": 2 * s_bytes,
+            "softmax_pass_GBps": round(2 * s_bytes / (stages["softmax"] * 1e-3) / 1e9, 1),
+            "hbm_peak_GBps": 8000,
+            "attn_forward_ms": round(ours, 4)}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,7 +164,14 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 256 MiB device-to-device three times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
+    ap.add_argument("--design-probe", action="store_true",
+                    help="time the materialised-S alternative for large d from library pieces "
+                         "(hipBLASLt bmm for Q K^T and P V, torch softmax between them) next to "
+                         "attn_forward on the same workload, and print one JSON line")
     args = ap.parse_args()
+
+    if args.design_probe:
+        return design_probe(args)
 
     if args.copy_probe:
         import torch

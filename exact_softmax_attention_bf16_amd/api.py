@@ -51,11 +51,14 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | 
     else:
         _check(out, "out", q)
     lib = _lib.load()
-    with torch.cuda.device(q.device):
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-        status = lib.attn_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                  B, H, L, d, float(scale), 1 if causal else 0,
-                                  ctypes.c_void_p(stream))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, d, float(scale),
+            1 if causal else 0)
+    if q.device.index == torch.cuda.current_device():
+        status = lib.attn_forward(*args, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    else:  # the library launches on the current device: switch to q's for the call
+        with torch.cuda.device(q.device):
+            status = lib.attn_forward(
+                *args, ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream))
     if status != _lib.ATTN_OK:
         raise _lib.AttnError(status)
     return out

@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdint>
 #include <map>
+#include <utility>
 #include <mutex>
 #include <vector>
 
@@ -36,37 +37,60 @@ bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
   return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
 }
 
-// ---- stream-ordered workspace: one pool per device, memory kept between calls.
-std::mutex g_pool_mu;
-std::map<int, hipMemPool_t> g_pools;
+// ---- workspace: one buffer per (device, stream), kept between calls.
+//
+// Work on one stream runs in order, so the stream's buffer can be reused by the
+// next call without any host wait; calls on different streams get different
+// buffers.  After each use an event is recorded on the stream; the next use
+// makes the stream wait for it (a no-op on the same stream, an ordering edge if
+// a new stream ever reuses a destroyed stream's handle), and growing the buffer
+// waits for it on the host before freeing the old one.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  hipEvent_t done = nullptr;
+  bool recorded = false;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-hipError_t device_pool(hipStream_t stream, hipMemPool_t* pool) {
+hipError_t acquire_workspace(hipStream_t stream, size_t bytes, Workspace** out) {
   int dev = 0;
   hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lk(g_pool_mu);
-  auto it = g_pools.find(dev);
-  if (it != g_pools.end()) {
-    *pool = it->second;
-    return hipSuccess;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  Workspace& w = g_ws[{dev, stream}];
+  if (!w.done) {
+    e = hipEventCreateWithFlags(&w.done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      w.done = nullptr;
+      return e;
+    }
   }
-  hipMemPoolProps props = {};
-  props.allocType = hipMemAllocationTypePinned;
-  props.handleTypes = hipMemHandleTypeNone;
-  props.location.type = hipMemLocationTypeDevice;
-  props.location.id = dev;
-  hipMemPool_t p = nullptr;
-  e = hipMemPoolCreate(&p, &props);
-  if (e != hipSuccess) return e;
-  uint64_t keep = UINT64_MAX;
-  e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
-  if (e != hipSuccess) {
-    (void)hipMemPoolDestroy(p);
+  if (w.bytes < bytes) {
+    if (w.ptr) {
+      if (w.recorded && (e = hipEventSynchronize(w.done)) != hipSuccess) return e;
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    if ((e = hipMalloc(&w.ptr, bytes)) != hipSuccess) {
+      w.ptr = nullptr;
+      return e;
+    }
+    w.bytes = bytes;
+  } else if (w.recorded && (e = hipStreamWaitEvent(stream, w.done, 0)) != hipSuccess) {
     return e;
   }
-  g_pools[dev] = p;
-  *pool = p;
+  *out = &w;
   return hipSuccess;
+}
+
+hipError_t release_workspace(hipStream_t stream, Workspace* w) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  const hipError_t e = hipEventRecord(w->done, stream);
+  w->recorded = e == hipSuccess;
+  return e;
 }
 
 // ---- kernel timing (benchmarks only).
@@ -77,6 +101,24 @@ struct TimingRecord {
 std::mutex g_timing_mu;
 bool g_timing = false;
 std::vector<TimingRecord> g_records;
+std::vector<hipEvent_t> g_free_events;  // reused across calls (creating events is slow)
+
+hipError_t take_event(hipEvent_t* ev) {
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    if (!g_free_events.empty()) {
+      *ev = g_free_events.back();
+      g_free_events.pop_back();
+      return hipSuccess;
+    }
+  }
+  return hipEventCreate(ev);
+}
+
+void give_event(hipEvent_t ev) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_free_events.push_back(ev);
+}
 
 bool timing_on() {
   std::lock_guard<std::mutex> lk(g_timing_mu);
@@ -87,14 +129,14 @@ template <class F>
 hipError_t timed(int id, hipStream_t s, bool on, F&& launch) {
   if (!on) return launch();
   TimingRecord r{id, nullptr, nullptr};
-  hipError_t e = hipEventCreate(&r.start);
-  if (e == hipSuccess) e = hipEventCreate(&r.stop);
+  hipError_t e = take_event(&r.start);
+  if (e == hipSuccess) e = take_event(&r.stop);
   if (e == hipSuccess) e = hipEventRecord(r.start, s);
   if (e == hipSuccess) e = launch();
   if (e == hipSuccess) e = hipEventRecord(r.stop, s);
   if (e != hipSuccess) {
-    if (r.start) (void)hipEventDestroy(r.start);
-    if (r.stop) (void)hipEventDestroy(r.stop);
+    if (r.start) give_event(r.start);
+    if (r.stop) give_event(r.stop);
     return e;
   }
   std::lock_guard<std::mutex> lk(g_timing_mu);
@@ -109,11 +151,10 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, int64_t
   const int64_t chunk = heads_per_chunk(BH, per_head);
   const bool on = timing_on();
 
-  hipMemPool_t pool = nullptr;
-  if (device_pool(stream, &pool) != hipSuccess) return ATTN_ERR_WORKSPACE;
-  void* ws = nullptr;
-  if (hipMallocFromPoolAsync(&ws, (size_t)(per_head * chunk), pool, stream) != hipSuccess)
+  Workspace* wsp = nullptr;
+  if (acquire_workspace(stream, (size_t)(per_head * chunk), &wsp) != hipSuccess)
     return ATTN_ERR_WORKSPACE;
+  void* ws = wsp->ptr;
 
   auto r256 = [](int64_t x) { return (x + 255) / 256 * 256; };
   const int64_t e_bytes = r256((int64_t)t.L * t.Ls * 2) * chunk;
@@ -139,8 +180,8 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, int64_t
         return attn::launch_values(vc, E, mref, psum, oc, n, t, causal, stream);
       });
   }
-  const hipError_t ferr = hipFreeAsync(ws, stream);
-  if (err != hipSuccess || ferr != hipSuccess) return ATTN_ERR_HIP;
+  const hipError_t rerr = release_workspace(stream, wsp);
+  if (err != hipSuccess || rerr != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
 
@@ -240,8 +281,8 @@ int attn_timing_collect(double* sum_ms, int64_t* launches, int n) {
       if (sum_ms) sum_ms[r.id] += ms;
       if (launches) launches[r.id] += 1;
     }
-    (void)hipEventDestroy(r.start);
-    (void)hipEventDestroy(r.stop);
+    give_event(r.start);
+    give_event(r.stop);
   }
   return status;
 }

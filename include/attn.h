@@ -22,8 +22,10 @@
  *   - Every argument is checked on the host before any HIP call; a failed check
  *     returns its status code and queues nothing.  No exception crosses the ABI.
  *   - Thread safety: any number of host threads may call concurrently.  Calls on
- *     different streams are independent: workspace comes from a stream-ordered
- *     pool, so two calls never share scratch memory.
+ *     different streams are independent: the two-pass path keeps one workspace
+ *     buffer per (device, stream), reused by later calls on that stream (work on
+ *     a stream runs in order), so two calls in flight never share scratch memory.
+ *     The buffers live until the process ends.
  */
 #ifndef ATTN_MI355X_ATTN_H
 #define ATTN_MI355X_ATTN_H
@@ -68,10 +70,11 @@ enum {
  *   causal  : 0 = no mask; nonzero = key j allowed for query i iff j <= i.
  *   stream  : HIP stream the kernels are queued on.
  *
- * Returns ATTN_OK or one of the codes above.  For d > 128 the call draws a
- * workspace from a per-device stream-ordered pool and returns it on `stream`
- * after the last kernel (about 2*L*(256*ceil(L/256) + 128) + 8*L*ceil(L/256)
- * bytes per head, heads processed in chunks of at most 2 GiB).
+ * Returns ATTN_OK or one of the codes above.  For d > 128 the call uses the
+ * workspace buffer the library keeps for (current device, stream), growing it
+ * when needed (about 2*L*(256*ceil(L/256) + 128) + 8*L*ceil(L/256) bytes per
+ * head, heads processed in chunks of at most 2 GiB).  Growing waits on the host
+ * for the stream's previous use of the buffer; reuse does not.
  */
 int attn_forward(const void* q, const void* k, const void* v, void* out,
                  int64_t B, int64_t H, int64_t L, int64_t d,

@@ -172,3 +172,43 @@ def test_kernel_timing_records_each_kernel():
         attention(q, k, v)
     assert set(res) == {"scores", "values"}
     assert all(c == 2 and ms > 0 for ms, c in res.values())
+
+
+def test_workspace_grows_and_is_reused_on_one_stream():
+    """The two-pass workspace of a stream: small call, larger call (the buffer
+    grows), small call again, all queued back to back before one sync."""
+    from exact_softmax_attention_bf16_amd import attention
+    dev = torch.device("cuda:0")
+    cases = [(1, 1, 300, 256, 21), (2, 1, 1300, 256, 22), (1, 2, 257, 512, 23)]
+    ins = [tuple(t.to(dev) for t in make_qkv(B, H, L, d, s)) for B, H, L, d, s in cases]
+    outs = [attention(q, k, v) for q, k, v in ins]
+    torch.cuda.synchronize()
+    for (B, H, L, d, s), (q, k, v), o in zip(cases, ins, outs):
+        ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1.0 / math.sqrt(d), False)
+        ok, a, r = within_bar(to_f64(o), ref)
+        _report(f"workspace reuse L={L} d={d}", a, r)
+        assert ok
+
+
+def test_two_streams_do_not_share_workspace():
+    """Calls queued on two streams at once (each with its own inputs) both match."""
+    from exact_softmax_attention_bf16_amd import attention
+    dev = torch.device("cuda:0")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    a = tuple(t.to(dev) for t in make_qkv(1, 1, 1000, 512, 24))
+    b = tuple(t.to(dev) for t in make_qkv(1, 1, 1000, 512, 25))
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            oa = attention(*a)
+        with torch.cuda.stream(s2):
+            ob = attention(*b)
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    for x, o in ((a, outs[-1][0]), (b, outs[-1][1])):
+        ref = oracle.attention(*(to_f64(t) for t in x), 1.0 / math.sqrt(512), False)
+        ok, am, r = within_bar(to_f64(o), ref)
+        _report("two streams", am, r)
+        assert ok
+    assert all(torch.equal(p[0], outs[-1][0]) and torch.equal(p[1], outs[-1][1]) for p in outs)

@@ -44,19 +44,22 @@ struct GemmSmem {
 // Its stage holds 256 rows x 64 K values; each 128-byte LDS row keeps eight
 // 16-byte chunks at chunk ^ swz(row), swz(row) = (row % 8) ^ ((row / 8) % 2):
 // the 8 or 16 consecutive rows one fragment read serves per LDS cycle then hit
-// distinct banks.  Per-lane byte offsets of the 8 chunks this lane copies, at k = 0.
+// distinct banks.  Per-lane byte offsets of the chunks this lane copies, at k = 0.
 __device__ __forceinline__ int kc_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-struct KContiguous {
+// NW waves share the stage's 2048 chunks: each issues 32 / NW loads of 1 KB.
+template <int NW>
+struct KContiguousT {
+  static constexpr int kLoads = 32 / NW;
   __amdgpu_buffer_rsrc_t r;
-  uint32_t off[8];
+  uint32_t off[kLoads];
 
   __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t rsrc, uint32_t ld, int r0, int wave,
                                        int lane) {
     r = rsrc;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int P = (wave * 8 + j) * 64 + lane;  // 16-byte chunk slot in the stage
+    for (int j = 0; j < kLoads; ++j) {
+      const int P = (wave * kLoads + j) * 64 + lane;  // 16-byte chunk slot in the stage
       const int row = P >> 3, pc = P & 7, lc = pc ^ kc_swz(row);
       off[j] = ((uint32_t)(r0 + row) * ld + (uint32_t)(lc * 8)) * 2u;
     }
@@ -70,12 +73,12 @@ struct KContiguous {
   __device__ __forceinline__ void issue_from(__amdgpu_buffer_rsrc_t rs, int k0, char* stage,
                                              int wave) const {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) issue_one(rs, k0, stage, wave, j);
+    for (int j = 0; j < kLoads; ++j) issue_one(rs, k0, stage, wave, j);
   }
-  // Load j of the eight.
+  // Load j of this wave's kLoads.
   __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int k0, char* stage,
                                             int wave, int j) const {
-    load16_to_lds(rs, stage + (wave * 8 + j) * 1024, off[j] + (uint32_t)k0 * 2u);
+    load16_to_lds(rs, stage + (wave * kLoads + j) * 1024, off[j] + (uint32_t)k0 * 2u);
   }
   // MFMA fragment: lane supplies row rbase + lane % 32, K values 16 ss + 8 (lane / 32) .. + 8.
   __device__ __forceinline__ bf16x8 frag(const char* stage, int rbase, int ss, int lane) const {
@@ -134,50 +137,69 @@ struct KOuter {
   }
 };
 
+using KContiguous = KContiguousT<4>;
+
 struct NoTransform {
   __device__ __forceinline__ void step(int) {}
   __device__ __forceinline__ bf16x8 operator()(bf16x8 f, int) const { return f; }
 };
 
-struct Frags {
-  bf16x8 a[4], b[4];
+// One k16 sub-step's fragments of a wave: 4 A blocks of 32 rows, NJ B blocks.
+template <int NJ>
+struct FragsT {
+  bf16x8 a[4], b[NJ];
 };
+using Frags = FragsT<4>;
 
-template <class LA, class LB>
-__device__ __forceinline__ void read_frags(Frags& f, const LA& la, const LB& lb, const char* sa,
-                                           const char* sb, int wm, int wn, int lane, int ss) {
+// A rows abase + 32 i, B rows bbase + 32 j.
+template <class LA, class LB, int NJ>
+__device__ __forceinline__ void read_frags(FragsT<NJ>& f, const LA& la, const LB& lb,
+                                           const char* sa, const char* sb, int abase, int bbase,
+                                           int lane, int ss) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = la.frag(sa, wm * 128 + i * 32, ss, lane);
+  for (int i = 0; i < 4; ++i) f.a[i] = la.frag(sa, abase + i * 32, ss, lane);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = lb.frag(sb, wn * 128 + j * 32, ss, lane);
+  for (int j = 0; j < NJ; ++j) f.b[j] = lb.frag(sb, bbase + j * 32, ss, lane);
 }
 
-template <class BX>
-__device__ __forceinline__ void mma_substep(f32x16 (&acc)[4][4], const Frags& f, const BX& bx) {
-  bf16x8 b[4];
+template <int NJ, class BX>
+__device__ __forceinline__ void mma_substep(f32x16 (&acc)[4][NJ], const FragsT<NJ>& f,
+                                            const BX& bx) {
+  bf16x8 b[NJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) b[j] = bx(f.b[j], j);
+  for (int j = 0; j < NJ; ++j) b[j] = bx(f.b[j], j);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(f.a[i], b[j], acc[i][j]);
+    for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(f.a[i], b[j], acc[i][j]);
 }
 
 // The first sub-step of a tile: accumulators start from zero.
-__device__ __forceinline__ void mma_substep_first(f32x16 (&acc)[4][4], const Frags& f) {
+template <int NJ>
+__device__ __forceinline__ void mma_substep_first(f32x16 (&acc)[4][NJ], const FragsT<NJ>& f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(f.a[i], f.b[j], f32x16{});
+    for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(f.a[i], f.b[j], f32x16{});
 }
 
-// Interleave 16 MFMAs with 8 LDS reads.
+// Interleave a sub-step's 4 NJ MFMAs with the 4 + NJ LDS reads of the next.
+template <int NJ>
 __device__ __forceinline__ void sched_substep() {
+  if constexpr (NJ == 4) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
   }
 }
 

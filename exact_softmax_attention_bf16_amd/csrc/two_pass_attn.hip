@@ -85,6 +85,17 @@ struct ScoresTile {
   int bh, qt, kt;
 };
 
+// 8 waves, two per SIMD: wave w (group g = w / 4, wm = (w / 2) % 2, wn = w % 2)
+// owns keys [128 wm, +128) x queries [128 wn + 64 g, +64) of the tile, as 4 x 2
+// accumulator blocks.  Two waves per SIMD keep the matrix cores busier than
+// one wave with twice the accumulators (measured 68-72% against 55-57% of
+// cycles on this GEMM shape), at 1.5x the LDS fragment reads.
+constexpr int kScoresWaves = 8;
+constexpr int kScoresNJ = 2;
+__device__ __forceinline__ int scores_query_base(int wave) {
+  return (wave & 1) * 128 + (wave >> 2) * 64;
+}
+
 // Tile idx of the pass: heads in order, then query tiles, then key tiles
 // (causal: only kt <= qt, row by row).
 __device__ __forceinline__ ScoresTile scores_tile(int idx, int T, int causal) {
@@ -106,22 +117,23 @@ __device__ __forceinline__ ScoresTile scores_tile(int idx, int T, int causal) {
 }
 
 template <bool MASK>
-__device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][4], ScoresSmem& sm,
+__device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ], ScoresSmem& sm,
                                                 uint16_t* __restrict__ E,
                                                 float* __restrict__ mref,
                                                 float* __restrict__ psum, const ScoresTile& t,
                                                 int L, int Ls, int T, float sl2, int causal) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, c32 = lane & 31, h = lane >> 5;
+  const int wm = (wave >> 1) & 1, c32 = lane & 31, h = lane >> 5;
+  const int qbase = scores_query_base(wave);  // this wave's first query column in the tile
   const int key0 = t.kt * kTile + wm * 128;
   uint16_t* Eh = E + (size_t)t.bh * L * Ls;
-  float mt[4], ps[4];
+  float mt[kScoresNJ], ps[kScoresNJ];
 
   // One column of accumulator blocks (32 queries) at a time, so that only its
   // 64 values are held in ordinary registers: partial maximum over this wave's
   // 128 keys, exchange with the wave holding the other 128 keys, exponentials.
 #pragma unroll
-  for (int bj = 0; bj < 4; ++bj) {
+  for (int bj = 0; bj < kScoresNJ; ++bj) {
     if (bj > 0) {
       // Pass the column through acc + 0 * 0 (exact) with a zero the compiler
       // cannot see before this point: otherwise it reads every column's
@@ -131,7 +143,7 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][4], ScoresSmem&
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi) acc[bi][bj] = mfma32x32x16(z, z, acc[bi][bj]);
     }
-    const int ql = wn * 128 + bj * 32 + c32;
+    const int ql = qbase + bj * 32 + c32;
     const int query = t.qt * kTile + ql;
     // Key key0 + 4h + c (c = 32 bi + 8 (j / 4) + j % 4, a constant) is allowed
     // for this query iff c < lim.
@@ -204,15 +216,15 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][4], ScoresSmem&
   }
   if (h == 0) {
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) sm.red2[wm][wn * 128 + bj * 32 + c32] = ps[bj];
+    for (int bj = 0; bj < kScoresNJ; ++bj) sm.red2[wm][qbase + bj * 32 + c32] = ps[bj];
   }
   __syncthreads();  // partial sums complete
   if (wm == 0 && h == 0) {
     float* mref_t = mref + ((size_t)t.bh * T + t.kt) * L;
     float* psum_t = psum + ((size_t)t.bh * T + t.kt) * L;
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
-      const int ql = wn * 128 + bj * 32 + c32;
+    for (int bj = 0; bj < kScoresNJ; ++bj) {
+      const int ql = qbase + bj * 32 + c32;
       const int query = t.qt * kTile + ql;
       if (query < L) {
         mref_t[query] = mt[bj];
@@ -228,25 +240,25 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][4], ScoresSmem&
 // the loads run two steps ahead across tile boundaries, so the next tile's
 // first stages arrive while this tile's epilogue computes and stores E.
 // One LDS object (see the GEMM loop's notes on the compiler's LDS-DMA waits).
-__global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict__ q,
-                                                     const uint16_t* __restrict__ k,
-                                                     uint16_t* __restrict__ E,
-                                                     float* __restrict__ mref,
-                                                     float* __restrict__ psum, int L, int d, int T,
-                                                     int Ls, float sl2, int causal, int ntiles) {
+__global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, uint16_t* __restrict__ E,
+    float* __restrict__ mref, float* __restrict__ psum, int L, int d, int T, int Ls, float sl2,
+    int causal, int ntiles) {
   __shared__ ScoresSmem smem;
   GemmSmem& sm = smem.g;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int abase = ((wave >> 1) & 1) * 128;  // key rows of this wave
+  const int bbase = scores_query_base(wave);  // query rows of this wave
   const int G = (int)gridDim.x;
   const int first = (int)xcd_logical_id(blockIdx.x, gridDim.x);
   const int my_tiles = (ntiles - 1 - first) / G + 1;  // first < ntiles
   const int nk = d / kStepK;                          // >= 3 on this path
   const int total = my_tiles * nk;
   const uint32_t row_bytes = (uint32_t)d * 2u;
+  constexpr int kLoads = KContiguousT<kScoresWaves>::kLoads;  // per wave and operand
 
-  KContiguous la, lb;  // per-lane offsets within a tile; resources start at its first row
+  KContiguousT<kScoresWaves> la, lb;  // per-lane offsets within a tile; resources start at its first row
   la.init(make_rsrc(k, 0), (uint32_t)d, 0, wave, lane);
   lb.init(make_rsrc(q, 0), (uint32_t)d, 0, wave, lane);
 
@@ -277,10 +289,10 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
   block_sync();
   issue_next(sm.a[1], sm.b[1]);  // total >= nk >= 3
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][kScoresNJ];
   NoTransform nx;
-  Frags cur, nxt;
-  read_frags(cur, la, lb, sm.a[0], sm.b[0], wm, wn, lane, 0);
+  FragsT<kScoresNJ> cur, nxt;
+  read_frags(cur, la, lb, sm.a[0], sm.b[0], abase, bbase, lane, 0);
 
   // One K step s: sub-step 0 starts the accumulators when FIRST.
   auto step = [&](auto first_step, int s) {
@@ -290,12 +302,12 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
     const char* sb = sm.b[st];
 #pragma unroll
     for (int ss = 0; ss < 3; ++ss) {
-      read_frags(nxt, la, lb, sa, sb, wm, wn, lane, ss + 1);
+      read_frags(nxt, la, lb, sa, sb, abase, bbase, lane, ss + 1);
       if (FIRST && ss == 0)
         mma_substep_first(acc, cur);
       else
         mma_substep(acc, cur, nx);
-      sched_substep();
+      sched_substep<kScoresNJ>();
       cur = nxt;
     }
     // Last sub-step: next stage complete everywhere, this stage drained.
@@ -304,18 +316,18 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
     // This sub-step's MFMAs in pairs, each pair followed by one load of each
     // operand for step s + 2 (past the end the cursor stays on the last tile: a
     // reload into a stage no longer read), with the next step's first fragments
-    // read after the sixth pair.  Measured: loads as a burst right after the
+    // read before the last pair.  Measured: loads as a burst right after the
     // barrier, or those reads right after it, both cost a few percent.
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      if (p == 6) {
+    for (int p = 0; p < 4; ++p) {
+      if (p == 3) {
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(nxt, la, lb, sm.a[st ^ 1], sm.b[st ^ 1], wm, wn, lane, 0);  // past the end: unused
+        read_frags(nxt, la, lb, sm.a[st ^ 1], sm.b[st ^ 1], abase, bbase, lane, 0);  // past the end: unused
       }
       __builtin_amdgcn_sched_barrier(0);
-      const int i = p >> 1, j0 = 2 * (p & 1);
-      acc[i][j0] = mfma32x32x16(cur.a[i], cur.b[j0], acc[i][j0]);
-      acc[i][j0 + 1] = mfma32x32x16(cur.a[i], cur.b[j0 + 1], acc[i][j0 + 1]);
+      acc[p][0] = mfma32x32x16(cur.a[p], cur.b[0], acc[p][0]);
+      acc[p][1] = mfma32x32x16(cur.a[p], cur.b[1], acc[p][1]);
+      static_assert(kLoads == 4, "one load of each operand per MFMA pair");
       la.issue_one(rk, lk * kStepK, sm.a[st], wave, p);
       lb.issue_one(rq, lk * kStepK, sm.b[st], wave, p);
     }
@@ -336,7 +348,7 @@ __global__ __launch_bounds__(256) void scores_kernel(const uint16_t* __restrict_
       scores_epilogue<false>(acc, smem, E, mref, psum, t, L, Ls, T, sl2, causal);
     // The next step's first fragments: read again (its stage is not refilled
     // before that step's end) instead of holding them through the epilogue.
-    read_frags(cur, la, lb, sm.a[s & 1], sm.b[s & 1], wm, wn, lane, 0);
+    read_frags(cur, la, lb, sm.a[s & 1], sm.b[s & 1], abase, bbase, lane, 0);
   }
   wait_vmem();
 }
@@ -517,7 +529,8 @@ hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, flo
   int ntiles = BH * (causal ? T * (T + 1) / 2 : T * T);
   const int grid = std::min(ntiles, device_cu_count());  // one workgroup per CU (LDS-bound)
   void* args[] = {&qp, &kp, &ep, &mref, &psum, &L, &d, &T, &Ls, &sl2, &c, &ntiles};
-  return hipLaunchKernel((const void*)&scores_kernel, dim3((unsigned)grid), dim3(256), args, 0, s);
+  return hipLaunchKernel((const void*)&scores_kernel, dim3((unsigned)grid),
+                         dim3(64 * kScoresWaves), args, 0, s);
 }
 
 hipError_t launch_values(const void* v, const void* E, const float* mref, const float* psum,

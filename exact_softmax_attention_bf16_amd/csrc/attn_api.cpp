@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <map>
@@ -30,6 +31,23 @@ int64_t heads_per_chunk(int64_t BH, int64_t head_bytes) {
   int64_t n = kChunkBudget / (head_bytes > 0 ? head_bytes : 1);
   if (n < 1) n = 1;
   return n < BH ? n : BH;
+}
+
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Two-pass workspace for a chunk of n heads: per head E and the two statistics
+// tables, plus the values pass's fp32 partial outputs when it splits the keys.
+int64_t chunk_workspace_bytes(int64_t n, const attn::TwoPassDims& t, bool causal) {
+  const int split = attn::values_split(n, t, causal);
+  const int64_t part = split > 1 ? round256((int64_t)split * n * t.L * t.d * 4) : 0;
+  return n * attn::two_pass_head_bytes(t) + part;
+}
+
+// Bytes attn_forward draws for BH heads: the largest of its chunks.
+int64_t two_pass_workspace_bytes(int64_t BH, const attn::TwoPassDims& t, bool causal) {
+  const int64_t chunk = heads_per_chunk(BH, attn::two_pass_head_bytes(t));
+  const int64_t last = BH - (BH - 1) / chunk * chunk;
+  return std::max(chunk_workspace_bytes(chunk, t, causal), chunk_workspace_bytes(last, t, causal));
 }
 
 bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
@@ -152,17 +170,10 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, int64_t
   const bool on = timing_on();
 
   Workspace* wsp = nullptr;
-  if (acquire_workspace(stream, (size_t)(per_head * chunk), &wsp) != hipSuccess)
+  if (acquire_workspace(stream, (size_t)two_pass_workspace_bytes(BH, t, causal), &wsp) !=
+      hipSuccess)
     return ATTN_ERR_WORKSPACE;
-  void* ws = wsp->ptr;
-
-  auto r256 = [](int64_t x) { return (x + 255) / 256 * 256; };
-  const int64_t e_bytes = r256((int64_t)t.L * t.Ls * 2) * chunk;
-  const int64_t st_bytes = r256((int64_t)t.T * t.L * 4) * chunk;
-  char* base = (char*)ws;
-  void* E = base;
-  float* mref = (float*)(base + e_bytes);
-  float* psum = (float*)(base + e_bytes + st_bytes);
+  char* base = (char*)wsp->ptr;
 
   const int64_t head_elems = L * d;
   hipError_t err = hipSuccess;
@@ -172,12 +183,24 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, int64_t
     const uint16_t* kc = (const uint16_t*)k + h0 * head_elems;
     const uint16_t* vc = (const uint16_t*)v + h0 * head_elems;
     uint16_t* oc = (uint16_t*)out + h0 * head_elems;
+    // This chunk's layout: E, the two statistics tables, the partial outputs.
+    const int64_t e_bytes = round256((int64_t)t.L * t.Ls * 2) * n;
+    const int64_t st_bytes = round256((int64_t)t.T * t.L * 4) * n;
+    void* E = base;
+    float* mref = (float*)(base + e_bytes);
+    float* psum = (float*)(base + e_bytes + st_bytes);
+    float* part = (float*)(base + e_bytes + 2 * st_bytes);
+    const int split = attn::values_split(n, t, causal);
     err = timed(ATTN_KERNEL_SCORES, stream, on, [&] {
       return attn::launch_scores(qc, kc, E, mref, psum, n, t, sl2, causal, stream);
     });
     if (err == hipSuccess)
       err = timed(ATTN_KERNEL_VALUES, stream, on, [&] {
-        return attn::launch_values(vc, E, mref, psum, oc, n, t, causal, stream);
+        return attn::launch_values(vc, E, mref, psum, oc, part, split, n, t, causal, stream);
+      });
+    if (err == hipSuccess && split > 1)
+      err = timed(ATTN_KERNEL_VALUES_REDUCE, stream, on, [&] {
+        return attn::launch_values_reduce(part, oc, split, n, t, stream);
       });
   }
   const hipError_t rerr = release_workspace(stream, wsp);
@@ -213,13 +236,11 @@ int attn_path_for_head_dim(int64_t d) {
 }
 
 int64_t attn_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int causal) {
-  (void)causal;
   if (B < 0 || H < 0 || L < 0 || attn_path_for_head_dim(d) != ATTN_PATH_TWO_PASS) return 0;
   if (B == 0 || H == 0 || L == 0) return 0;
   if (L > (int64_t)1 << 20) return 0;
   const attn::TwoPassDims t = attn::two_pass_dims(L, d);
-  const int64_t per_head = attn::two_pass_head_bytes(t);
-  return per_head * heads_per_chunk(B * H, per_head);
+  return two_pass_workspace_bytes(B * H, t, causal != 0);
 }
 
 int attn_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,

@@ -140,7 +140,7 @@ struct KOuter {
 using KContiguous = KContiguousT<4>;
 
 struct NoTransform {
-  __device__ __forceinline__ void step(int) {}
+  __device__ __forceinline__ void step(int, bool) {}
   __device__ __forceinline__ bf16x8 operator()(bf16x8 f, int) const { return f; }
 };
 
@@ -219,15 +219,17 @@ __device__ __forceinline__ void sched_substep_b_only() {
   __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);  // 12 MFMAs
 }
 
-// acc[i][j] = A[m0 + 128 wm + 32 i + .., 0:64 nk] . B[n0 + 128 wn + 32 j + .., 0:64 nk]
-// with A in the K-outer layout (LA = KOuter) and B K-contiguous.  All A
-// fragments of a step are read right after the barrier, before that step's
-// loads go out (the transpose reads would otherwise wait for them).
-// `bx.step(kt)` runs before step kt's MFMAs; `bx(frag, j)` may rewrite each B fragment.
+// acc[i][j] = A[m0 + 128 wm + 32 i + .., K] . B[n0 + 128 wn + 32 j + .., K] over the
+// K steps [k_first, k_first + nk) (64 wide each), with A in the K-outer layout
+// (LA = KOuter) and B K-contiguous.  All A fragments of a step are read right
+// after the barrier, before that step's loads go out (the transpose reads
+// would otherwise wait for them).  `bx.step(kt, first)` runs before step kt's
+// MFMAs (kt absolute); `bx(frag, j)` may rewrite each B fragment.
 template <class LA, class BX>
 __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_rsrc_t ra,
                                           uint32_t lda, int m0, __amdgpu_buffer_rsrc_t rb,
-                                          uint32_t ldb, int n0, int nk, GemmSmem& sm, BX& bx) {
+                                          uint32_t ldb, int n0, int k_first, int nk,
+                                          GemmSmem& sm, BX& bx) {
   static_assert(LA::kWholeStepA, "the K loop below reads A a whole step at a time");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -242,12 +244,14 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
   la.init(ra, lda, m0, wave, lane);
   lb.init(rb, ldb, n0, wave, lane);
 
-  // Stage 0 <- step 0; stage 1 <- step 1 (a harmless reload of step 0 when nk == 1).
-  la.issue(0, sm.a[0], wave);
-  lb.issue(0, sm.b[0], wave);
+  // Stage 0 <- the first step; stage 1 <- the second (a harmless reload of the
+  // first when nk == 1).
+  const int kb = k_first * kStepK;
+  la.issue(kb, sm.a[0], wave);
+  lb.issue(kb, sm.b[0], wave);
   wait_vmem();
   block_sync();
-  const int k1 = nk > 1 ? kStepK : 0;
+  const int k1 = kb + (nk > 1 ? kStepK : 0);
 
   Frags f[4];  // f[ss].a: A of sub-step ss; f[ss].b: B of sub-step ss (as it arrives)
   auto read_a_step = [&](Frags (&g)[4], const char* sa) {
@@ -267,7 +271,7 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
     const char* sb = sm.b[st];
-    bx.step(kt);
+    bx.step(k_first + kt, kt == 0);
 #pragma unroll
     for (int ss = 0; ss < 3; ++ss) {
       read_b(f[ss + 1].b, sb, ss + 1);
@@ -280,7 +284,7 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
     block_sync();
     read_a_step(f, sm.a[st ^ 1]);
     read_b(f[0].b, sm.b[st ^ 1], 0);
-    const int k2 = (kt + 2 < nk ? kt + 2 : nk - 1) * kStepK;  // past the end: reload, unused
+    const int k2 = kb + (kt + 2 < nk ? kt + 2 : nk - 1) * kStepK;  // past the end: reload, unused
     // The reads above, then the sub-step's MFMAs in pairs with one load of each
     // operand after each pair.
     __builtin_amdgcn_sched_barrier(0);

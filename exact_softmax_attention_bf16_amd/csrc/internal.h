@@ -37,7 +37,19 @@ hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, flo
                          const TwoPassDims& t, float sl2, bool causal, hipStream_t s);
 
 // Values pass: O = (sum over tiles of 2^(m_t - M) E_t V_t) / (sum_t 2^(m_t - M) psum_t).
+// With split > 1 the keys of each query tile are divided among `split`
+// workgroups, each writing its share of O in fp32 to part[split][BH][L][d];
+// launch_values_reduce then sums the shares into bf16 `out`.
+constexpr int kValuesTargetWorkgroups = 256;  // MI355X compute units
+constexpr int kValuesMaxSplit = 4;
+constexpr int kValuesMinSplitSteps = 8;  // K steps (64 keys each) per split at least
+// Splits used for BH heads: 1 unless the unsplit grid would leave at least half
+// of the compute units idle.  Depends on the shape only.
+int values_split(int64_t BH, const TwoPassDims& t, bool causal);
 hipError_t launch_values(const void* v, const void* E, const float* mref, const float* psum,
-                         void* out, int BH, const TwoPassDims& t, bool causal, hipStream_t s);
+                         void* out, float* part, int split, int BH, const TwoPassDims& t,
+                         bool causal, hipStream_t s);
+hipError_t launch_values_reduce(const float* part, void* out, int split, int BH,
+                                const TwoPassDims& t, hipStream_t s);
 
 }  // namespace attn

@@ -366,8 +366,8 @@ struct PowerOfTwoShift {
   int col[4];                   // this lane's four query columns in the tile
   unsigned sw[4];               // current shift words (s << 7 | s << 23)
 
-  __device__ __forceinline__ void step(int kt) {
-    if ((kt & 3) == 0) {
+  __device__ __forceinline__ void step(int kt, bool first) {
+    if ((kt & 3) == 0 || first) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const unsigned s = tab[kt >> 2][col[j]];
@@ -389,29 +389,40 @@ struct ValuesSmem {
   float inv_l[kTile];
 };
 
+// SPLIT: the keys of each query tile are divided among `split` workgroups that
+// write fp32 shares of O to `part` (a separate instantiation, so that the
+// unsplit kernel carries none of it).
+template <bool SPLIT>
 __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict__ v,
                                                      const uint16_t* __restrict__ E,
                                                      const float* __restrict__ mref,
                                                      const float* __restrict__ psum,
-                                                     uint16_t* __restrict__ out, int L, int d,
-                                                     int T, int Ls, int Lk, int causal, int ncb) {
+                                                     uint16_t* __restrict__ out,
+                                                     float* __restrict__ part, int L, int d,
+                                                     int T, int Ls, int Lk, int causal, int ncb,
+                                                     int split, int nheads) {
   __shared__ ValuesSmem smem;
   GemmSmem& sm = smem.g;
   uint8_t(&shift_tab)[kMaxTiles][kTile] = smem.shift_tab;
   float(&inv_l)[kTile] = smem.inv_l;
 
+  if (!SPLIT) split = 1;
   const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int per_head = T * ncb;
+  const int per_head = T * ncb * split;
   const int bh = lid / per_head;
   const int r = lid % per_head;
-  const int qt = r / ncb, ct = r % ncb;
+  const int qt = r / (ncb * split), ct = (r / split) % ncb, sp = SPLIT ? r % split : 0;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, c32 = lane & 31, h = lane >> 5;
 
   const int tiles = causal ? qt + 1 : T;
   const int kend = causal ? min(Lk, (qt + 1) * kTile) : Lk;
-  const int nk = kend / kStepK;
+  // Split sp of `split` takes K steps [k_first, k_first + nk) (never empty:
+  // the host keeps split <= the fewest steps of any query tile).
+  const int nk_all = kend / kStepK;
+  const int k_first = SPLIT ? nk_all * sp / split : 0;
+  const int nk = SPLIT ? nk_all * (sp + 1) / split - k_first : nk_all;
 
   // Thread tid owns query qt*256 + tid: M = max_t m_t, l = sum_t 2^(m_t - M) psum_t,
   // and the shift M - m_t of each tile (a nonnegative integer; -inf tiles -> 255).
@@ -463,7 +474,32 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
   const auto ra = make_rsrc(v + (size_t)bh * L * d, (uint32_t)L * d * 2);
   const auto rb = make_rsrc(E + (size_t)bh * L * Ls, (uint32_t)L * Ls * 2);
   f32x16 acc[4][4];
-  gemm_tile<KOuter>(acc, ra, (uint32_t)d, ct * kTile, rb, (uint32_t)Ls, qt * kTile, nk, sm, sh);
+  gemm_tile<KOuter>(acc, ra, (uint32_t)d, ct * kTile, rb, (uint32_t)Ls, qt * kTile, k_first, nk,
+                    sm, sh);
+
+  if constexpr (SPLIT) {
+    // This split's share of O = (its part of the sum) / l, in fp32, for the
+    // reduction kernel: lane (query) stores 4 consecutive channels at a time.
+    float* ph = part + ((size_t)sp * nheads + bh) * L * d;
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const int query = qt * kTile + wn * 128 + bj * 32 + c32;
+      if (query >= L) continue;
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ch = ct * kTile + wm * 128 + bi * 32 + 8 * i + 4 * h;
+          if (ch < d) {
+            const f32x16& a = acc[bi][bj];
+            f32x4 o = {a[4 * i] * invl[bj], a[4 * i + 1] * invl[bj], a[4 * i + 2] * invl[bj],
+                       a[4 * i + 3] * invl[bj]};
+            *(f32x4*)(ph + (size_t)query * d + ch) = o;
+          }
+        }
+    }
+    return;
+  }
 
   // O[query][ch] = acc / l, rounded once to bf16.  The tile goes through the
   // drained GEMM stages as [query][256 channels] rows (laid out like the E tile
@@ -502,6 +538,23 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
   }
 }
 
+// out = bf16(sum over the splits of part), 8 elements per thread.
+__global__ __launch_bounds__(256) void values_reduce_kernel(const float* __restrict__ part,
+                                                            uint16_t* __restrict__ out,
+                                                            int64_t n8, int64_t stride, int split) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    const f32x4* p = (const f32x4*)part + 2 * i;
+    f32x4 lo = p[0], hi = p[1];
+    for (int s = 1; s < split; ++s) {
+      lo += p[(size_t)s * (stride / 4)];
+      hi += p[(size_t)s * (stride / 4) + 1];
+    }
+    const u32x4 w = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                     pack_bf16x2(hi[2], hi[3])};
+    *((u32x4*)out + i) = w;
+  }
+}
+
 }  // namespace
 
 // Compute units of the current device (cached per device).
@@ -533,15 +586,41 @@ hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, flo
                          dim3(64 * kScoresWaves), args, 0, s);
 }
 
+int values_split(int64_t BH, const TwoPassDims& t, bool causal) {
+  const int64_t base = BH * t.T * ((t.d + kTile - 1) / kTile);  // workgroups without a split
+  if (base * 2 > kValuesTargetWorkgroups) return 1;
+  const int64_t steps = t.Lk / kStepK;                       // K steps of a full query tile
+  const int64_t fewest = causal ? std::min<int64_t>(kTile / kStepK, steps) : steps;
+  // Each split keeps at least kValuesMinSplitSteps K steps: shorter loops are
+  // dominated by the fixed cost of a workgroup, and the partials cost a pass.
+  int64_t s = std::min<int64_t>(kValuesTargetWorkgroups / base, kValuesMaxSplit);
+  s = std::min(s, fewest / kValuesMinSplitSteps);
+  return s >= 2 ? (int)s : 1;
+}
+
 hipError_t launch_values(const void* v, const void* E, const float* mref, const float* psum,
-                         void* out, int BH, const TwoPassDims& t, bool causal, hipStream_t s) {
+                         void* out, float* part, int split, int BH, const TwoPassDims& t,
+                         bool causal, hipStream_t s) {
   const uint16_t* vtp = (const uint16_t*)v;
   const uint16_t* ep = (const uint16_t*)E;
   uint16_t* op = (uint16_t*)out;
   int L = t.L, d = t.d, T = t.T, Ls = t.Ls, Lk = t.Lk, c = causal ? 1 : 0;
   int ncb = (t.d + kTile - 1) / kTile;
-  void* args[] = {&vtp, &ep, &mref, &psum, &op, &L, &d, &T, &Ls, &Lk, &c, &ncb};
-  return hipLaunchKernel((const void*)&values_kernel, dim3((unsigned)(BH * T * ncb)), dim3(256),
+  int nheads = BH;
+  void* args[] = {&vtp, &ep, &mref, &psum, &op, &part, &L, &d, &T, &Ls, &Lk, &c, &ncb, &split,
+                  &nheads};
+  const void* kern = split > 1 ? (const void*)&values_kernel<true> : (const void*)&values_kernel<false>;
+  return hipLaunchKernel(kern, dim3((unsigned)(BH * T * ncb * split)), dim3(256), args, 0, s);
+}
+
+hipError_t launch_values_reduce(const float* part, void* out, int split, int BH,
+                                const TwoPassDims& t, hipStream_t s) {
+  int64_t stride = (int64_t)BH * t.L * t.d;  // floats per split
+  int64_t n8 = stride / 8;                   // d is a multiple of 64
+  const int blocks = (int)std::min<int64_t>((n8 + 255) / 256, 2048);
+  uint16_t* op = (uint16_t*)out;
+  void* args[] = {&part, &op, &n8, &stride, &split};
+  return hipLaunchKernel((const void*)&values_reduce_kernel, dim3((unsigned)blocks), dim3(256),
                          args, 0, s);
 }
 

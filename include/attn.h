@@ -73,8 +73,11 @@ enum {
  * Returns ATTN_OK or one of the codes above.  For d > 128 the call uses the
  * workspace buffer the library keeps for (current device, stream), growing it
  * when needed (about 2*L*(256*ceil(L/256) + 128) + 8*L*ceil(L/256) bytes per
- * head, heads processed in chunks of at most 2 GiB).  Growing waits on the host
- * for the stream's previous use of the buffer; reuse does not.
+ * head, heads processed in chunks of at most 2 GiB; when so few heads would
+ * leave most compute units idle, also up to 4 fp32 copies of the output for
+ * a split over the keys -- attn_workspace_bytes gives the exact figure).
+ * Growing waits on the host for the stream's previous use of the buffer;
+ * reuse does not.
  */
 int attn_forward(const void* q, const void* k, const void* v, void* out,
                  int64_t B, int64_t H, int64_t L, int64_t d,
@@ -102,7 +105,8 @@ enum {
   ATTN_KERNEL_ONLINE = 0,  /* fused online-softmax kernel (d <= 128)              */
   ATTN_KERNEL_SCORES = 1,  /* two-pass path: S = QK^T tiles -> bf16 exp + stats   */
   ATTN_KERNEL_VALUES = 2,  /* two-pass path: O = P V with the row normalisation   */
-  ATTN_KERNEL_COUNT = 3
+  ATTN_KERNEL_VALUES_REDUCE = 3, /* two-pass path, few heads: sum of the key splits */
+  ATTN_KERNEL_COUNT = 4
 };
 int attn_timing_enable(int enable);
 int attn_timing_collect(double* sum_ms, int64_t* launches, int n);

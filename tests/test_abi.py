@@ -61,14 +61,45 @@ def test_path_for_head_dim(d, path):
     assert eab.path_for_head_dim(d) == path
 
 
+def _values_split(n, L, d, causal):
+    """Key splits of the values pass for n heads: 1 unless the unsplit grid
+    (n * T * ceil(d/256) workgroups) would fill at most half of 256 CUs; then as
+    many as fit in 256, at most 4, with at least 8 K steps (64 keys) per split in
+    the query tile with the fewest; below 2, no split."""
+    T = -(-L // 256)
+    base = n * T * (-(-d // 256))
+    if 2 * base > 256:
+        return 1
+    steps = -(-L // 64)
+    fewest = min(4, steps) if causal else steps
+    s = min(256 // base, 4, fewest // 8)
+    return s if s >= 2 else 1
+
+
 def test_workspace_bytes():
-    # per head: E (L rows of 256*T + 128 bf16, T = ceil(L/256)) and two fp32 [T, L] tables
+    # per head: E (L rows of 256*T + 128 bf16, T = ceil(L/256)) and two fp32 [T, L] tables;
+    # plus split * n * L * d fp32 partial outputs when the values pass splits the keys
     L, d, T = 3432, 1024, 14
     ls = 256 * T + 128
     r = lambda x: (x + 255) // 256 * 256
     per_head = r(L * ls * 2) + 2 * r(T * L * 4)
-    assert eab.workspace_bytes(1, 1, L, d) == per_head
+    assert _values_split(1, L, d, False) == 4 and _values_split(31, L, d, False) == 1
+    assert _values_split(4, L, d, False) == 1
+    assert eab.workspace_bytes(1, 1, L, d) == per_head + r(4 * L * d * 4)
+    assert eab.workspace_bytes(4, 1, L, d) == 4 * per_head
     assert eab.workspace_bytes(31, 1, L, d) == 31 * per_head
+    # tiny: L = 286, d = 256: 5 K steps -> too short to split
+    Lt, dt, Tt = 286, 256, 2
+    pt = r(Lt * (256 * Tt + 128) * 2) + 2 * r(Tt * Lt * 4)
+    assert _values_split(1, Lt, dt, False) == 1
+    assert eab.workspace_bytes(1, 1, Lt, dt) == pt
+    # causal: the first query tile has 4 K steps -> no split
+    assert _values_split(1, 3432, 1024, True) == 1
+    assert eab.workspace_bytes(1, 1, 3432, 1024, True) == per_head
+    # L = 1100, d = 256: base 5, 18 K steps -> 2 splits
+    assert _values_split(1, 1100, 256, False) == 2
+    assert eab.workspace_bytes(1, 1, 1100, 256) == (
+        r(1100 * (256 * 5 + 128) * 2) + 2 * r(5 * 1100 * 4) + r(2 * 1100 * 256 * 4))
     assert eab.workspace_bytes(4, 8, 1024, 64) == 0       # online path: none
     assert eab.workspace_bytes(0, 1, L, d) == 0
     big = eab.workspace_bytes(1000, 1, L, d)              # chunked under ~2 GiB

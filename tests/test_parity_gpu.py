@@ -165,13 +165,37 @@ def test_empty_problem():
 
 def test_kernel_timing_records_each_kernel():
     from exact_softmax_attention_bf16_amd import attention, kernel_timing
-    q, k, v = (t.cuda() for t in make_qkv(1, 1, 512, 1024, 14))
+    q, k, v = (t.cuda() for t in make_qkv(1, 1, 1100, 1024, 14))
     res = {}
     with kernel_timing(res):
         attention(q, k, v)
         attention(q, k, v)
-    assert set(res) == {"scores", "values"}
+    # one head of L=1100, d=1024 leaves most CUs idle: the values pass splits its keys
+    assert set(res) == {"scores", "values", "values_reduce"}
     assert all(c == 2 and ms > 0 for ms, c in res.values())
+
+
+def test_kernel_timing_without_split():
+    from exact_softmax_attention_bf16_amd import attention, kernel_timing
+    q, k, v = (t.cuda() for t in make_qkv(16, 1, 1024, 1024, 15))  # 256 workgroups: no split
+    res = {}
+    with kernel_timing(res):
+        attention(q, k, v)
+    assert set(res) == {"scores", "values"}
+
+
+@pytest.mark.parametrize("L,d,splits", [(1100, 256, 2), (1500, 256, 3), (2100, 512, 4),
+                                         (2100, 512, 1)])
+def test_values_key_split(L, d, splits):
+    """Few heads: the values pass divides the keys among 2-4 workgroups and sums
+    their fp32 shares (splits == 1: the same shape with enough heads not to)."""
+    B = 1 if splits > 1 else 32
+    q, k, v = make_qkv(B, 1, L, d, 30 + splits)
+    o = run_gpu(q, k, v, 1.0 / math.sqrt(d), False)
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1.0 / math.sqrt(d), False)
+    ok, a, r = within_bar(to_f64(o), ref)
+    _report(f"key split x{splits} L={L} d={d}", a, r)
+    assert ok
 
 
 def test_workspace_grows_and_is_reused_on_one_stream():

@@ -7,7 +7,13 @@
 // by l at the end.  The exponent is taken base 2 with the scale folded in
 // (scale * log2 e), as that page does; exp2 is the hardware v_exp_f32.
 //
-// gfx950 mapping (one workgroup = 4 waves = 128 queries of one head):
+// gfx950 mapping (one workgroup = 8 waves = 128 queries of one head):
+//   * Waves 0-3 and 4-7 form two groups over the same 128 queries; group g takes
+//     the key blocks t = g, g + 2, ... with its own double-buffered K/V tiles,
+//     so every SIMD runs two waves and one wave's softmax overlaps the other's
+//     MFMAs.  At the end group 1 hands its (m, l, O) to group 0 through LDS and
+//     group 0 merges the two exactly: O = (2^(m0-M) O0 + 2^(m1-M) O1) /
+//     (2^(m0-M) l0 + 2^(m1-M) l1), M = max(m0, m1).
 //   * Each wave owns 32 queries.  It computes S^T = K Q^T for a 64-key block
 //     with v_mfma_f32_32x32x16_bf16, keys on the M side and queries on the N
 //     side, so that every lane owns one query: the row max and row sum are
@@ -28,33 +34,46 @@
 namespace attn {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kBM = 32 * kWaves;  // queries per workgroup
+constexpr int kQWaves = 4;            // query waves per group
+constexpr int kGroups = 2;            // groups taking alternate key blocks
+constexpr int kWaves = kQWaves * kGroups;
+constexpr int kBM = 32 * kQWaves;     // queries per workgroup
 constexpr int kBN = 64;           // keys per step
 constexpr float kLazy = 8.f;      // reference slack (log2 units) before O is rescaled
 
+template <int D>
+struct OnlineSmem {
+  static constexpr int KT_BYTES = 64 * D * 2;
+  static constexpr int VT_BYTES = D * (64 * 2 + 8);
+  char kbuf[kGroups][2][KT_BYTES];
+  char vbuf[kGroups][2][VT_BYTES];
+};
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void online_attn_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v,
                                                           uint16_t* __restrict__ out, int L,
                                                           int nqb, float sl2) {
   constexpr int CPR = D / 8;                       // 16-byte chunks per K row
   constexpr int SWZ = (CPR >= 8 ? 8 : CPR) - 1;    // chunk-index bits that are swizzled
-  constexpr int KT_BYTES = kBN * D * 2;
   constexpr int VROW = kBN * 2 + 8;                // bytes per V^T row: 64 keys + pad
-  constexpr int VT_BYTES = D * VROW;
   constexpr int K_LOADS = kBN * CPR / 256;         // direct loads per thread per K tile
   constexpr int V_BLOCKS = 16 * CPR;               // 4-key x 8-channel blocks per V tile
   constexpr int NS = D / 16;                       // k16 steps for S
   constexpr int NCB = D / 32;                      // 32-channel blocks of O
   static_assert(K_LOADS >= 1 && V_BLOCKS <= 256, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) char kbuf[2][KT_BYTES];
-  __shared__ __attribute__((aligned(16))) char vbuf[2][VT_BYTES];
+  // One LDS object (two would make the compiler wait on every direct load in
+  // flight before each LDS read).
+  __shared__ OnlineSmem<D> smem;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ltid = threadIdx.x & 255, lane = threadIdx.x & 63;
+  const int g = threadIdx.x >> 8;           // key-block group
+  const int wave = (threadIdx.x >> 6) & 3;  // query wave within the group
   const int c32 = lane & 31, h = lane >> 5;
+  auto& kbuf = smem.kbuf[g];
+  auto& vbuf = smem.vbuf[g];
 
   const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int bh = lid / nqb;
@@ -82,16 +101,17 @@ __global__ __launch_bounds__(256) void online_attn_kernel(const uint16_t* __rest
   auto issue_k = [&](int t, int buf) {
 #pragma unroll
     for (int j = 0; j < K_LOADS; ++j) {
-      const int P = (j * kWaves + wave) * 64 + lane;
+      const int P = (j * kQWaves + wave) * 64 + lane;
       const int row = P / CPR, pc = P % CPR;
       const int lc = pc ^ (row & SWZ);
       const uint32_t voff = (uint32_t)((t * kBN + row) * D + lc * 8) * 2;
-      load16_to_lds(rk, &kbuf[buf][(j * kWaves + wave) * 64 * 16], voff);
+      load16_to_lds(rk, &kbuf[buf][(j * kQWaves + wave) * 64 * 16], voff);
     }
   };
-  // Thread tid owns V block (g = tid % 16 -> keys 4g..4g+3, c8 = tid / 16 -> channels 8c8..+7).
-  const bool vblk = tid < V_BLOCKS;
-  const int vg = tid & 15, vc8 = tid >> 4;
+  // Thread ltid of a group owns V block (vg = ltid % 16 -> keys 4vg..4vg+3,
+  // vc8 = ltid / 16 -> channels 8vc8..+7).
+  const bool vblk = ltid < V_BLOCKS;
+  const int vg = ltid & 15, vc8 = ltid >> 4;
   auto load_v = [&](int t, u32x4 (&vr)[4]) {
     if (vblk) {
 #pragma unroll
@@ -117,22 +137,29 @@ __global__ __launch_bounds__(256) void online_attn_kernel(const uint16_t* __rest
   for (int c = 0; c < NCB; ++c) o[c] = f32x16{};
   float m = -INFINITY, lsum = 0.f;
 
+  // Group g takes key blocks t = g + kGroups * it.  Both groups run the same
+  // number of iterations (so that every wave meets every barrier); a block
+  // past the end is skipped.
+  const int niter = (ntiles + kGroups - 1) / kGroups;
   u32x4 vr[4];
-  issue_k(0, 0);
-  load_v(0, vr);
-  wait_vmem();
-  store_vt(0, vr);
+  if (g < ntiles) {
+    issue_k(g, 0);
+    load_v(g, vr);
+    wait_vmem();
+    store_vt(0, vr);
+  }
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const bool has_next = t + 1 < ntiles;
+  for (int it = 0; it < niter; ++it) {
+    const int t = g + kGroups * it;
+    const int buf = it & 1;
+    const bool has_next = t + kGroups < ntiles;
     if (has_next) {
-      issue_k(t + 1, buf ^ 1);
-      load_v(t + 1, vr);
+      issue_k(t + kGroups, buf ^ 1);
+      load_v(t + kGroups, vr);
     }
     const int kbase = t * kBN;
-    const bool active = !CAUSAL || kbase <= q0 + 31;
+    const bool active = t < ntiles && (!CAUSAL || kbase <= q0 + 31);
     if (active) {
       // S^T block: 64 keys x 32 queries, two 32-key halves.
       f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -228,9 +255,38 @@ __global__ __launch_bounds__(256) void online_attn_kernel(const uint16_t* __rest
     __syncthreads();
   }
 
-  // Epilogue: O = O / l, rounded once to bf16.  Lane holds channels
-  // 32c + 8i + 4h + r (r = 0..3) of query myq in o[c][4i + r].
-  const float inv = 1.f / wave_swap32_sum(lsum);
+  // Merge the two groups' partial results.  Group 1 leaves m, l and O (fp32) in
+  // the K/V tiles, which no wave reads any more; group 0 combines.  Lane holds
+  // channels 32c + 8i + 4h + r (r = 0..3) of query myq in o[c][4i + r].
+  lsum = wave_swap32_sum(lsum);
+  float* xo = (float*)&smem;                      // [4 waves][NCB][16][64 lanes]
+  float* xm = xo + kQWaves * NCB * 16 * 64;       // [4 waves][64 lanes]
+  float* xl = xm + kQWaves * 64;
+  static_assert(sizeof(OnlineSmem<D>) >= (kQWaves * NCB * 16 * 64 + 2 * kQWaves * 64) * 4,
+                "exchange fits in the tiles");
+  if (g == 1) {
+#pragma unroll
+    for (int c = 0; c < NCB; ++c)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) xo[((wave * NCB + c) * 16 + j) * 64 + lane] = o[c][j];
+    xm[wave * 64 + lane] = m;
+    xl[wave * 64 + lane] = lsum;
+  }
+  __syncthreads();
+  if (g == 1) return;
+  {
+    const float m1 = xm[wave * 64 + lane], l1 = xl[wave * 64 + lane];
+    const float M = fmaxf(m, m1);
+    const float a0 = m == -INFINITY ? 0.f : exp2_fast(m - M);
+    const float a1 = m1 == -INFINITY ? 0.f : exp2_fast(m1 - M);
+    lsum = a0 * lsum + a1 * l1;
+#pragma unroll
+    for (int c = 0; c < NCB; ++c)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        o[c][j] = a0 * o[c][j] + a1 * xo[((wave * NCB + c) * 16 + j) * 64 + lane];
+  }
+  const float inv = 1.f / lsum;
   if (myq < L) {
     uint16_t* orow = out + head + (size_t)myq * D;
 #pragma unroll
@@ -249,7 +305,7 @@ template <int D, bool C>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* out, int BH, int L,
                       float sl2, hipStream_t s) {
   const int nqb = (L + kBM - 1) / kBM;
-  const dim3 grid((unsigned)(nqb * BH)), block(256);
+  const dim3 grid((unsigned)(nqb * BH)), block(64 * kWaves);
   const uint16_t* qp = (const uint16_t*)q;
   const uint16_t* kp = (const uint16_t*)k;
   const uint16_t* vp = (const uint16_t*)v;

@@ -129,20 +129,11 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ], Sco
   uint16_t* Eh = E + (size_t)t.bh * L * Ls;
   float mt[kScoresNJ], ps[kScoresNJ];
 
-  // One column of accumulator blocks (32 queries) at a time, so that only its
-  // 64 values are held in ordinary registers: partial maximum over this wave's
-  // 128 keys, exchange with the wave holding the other 128 keys, exponentials.
+  // One column of accumulator blocks (32 queries) at a time: partial maximum
+  // over this wave's 128 keys, exchange with the wave holding the other 128
+  // keys, exponentials and stores.
 #pragma unroll
   for (int bj = 0; bj < kScoresNJ; ++bj) {
-    if (bj > 0) {
-      // Pass the column through acc + 0 * 0 (exact) with a zero the compiler
-      // cannot see before this point: otherwise it reads every column's
-      // accumulators ahead of the first barrier and keeps all 256 copies.
-      bf16x8 z = {};
-      asm volatile("" : "+v"(z));
-#pragma unroll
-      for (int bi = 0; bi < 4; ++bi) acc[bi][bj] = mfma32x32x16(z, z, acc[bi][bj]);
-    }
     const int ql = qbase + bj * 32 + c32;
     const int query = t.qt * kTile + ql;
     // Key key0 + 4h + c (c = 32 bi + 8 (j / 4) + j % 4, a constant) is allowed

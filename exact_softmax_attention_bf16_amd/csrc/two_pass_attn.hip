@@ -85,15 +85,22 @@ struct ScoresTile {
   int bh, qt, kt;
 };
 
-// 8 waves, two per SIMD: wave w (group g = w / 4, wm = (w / 2) % 2, wn = w % 2)
-// owns keys [128 wm, +128) x queries [128 wn + 64 g, +64) of the tile, as 4 x 2
-// accumulator blocks.  Two waves per SIMD keep the matrix cores busier than
-// one wave with twice the accumulators (measured 68-72% against 55-57% of
-// cycles on this GEMM shape), at 1.5x the LDS fragment reads.
+// 8 waves, two per SIMD: wave w owns keys [128 wm, +128) x queries
+// [128 wn + 64 hf, +64) of the tile, as 4 x 2 accumulator blocks.  Two waves
+// per SIMD keep the matrix cores busier than one wave with twice the
+// accumulators (measured 68-72% against 55-57% of cycles on this GEMM shape),
+// at 1.5x the LDS fragment reads.
+//
+// Waves w and w + 4 share a SIMD; with p = w % 4 and g = w / 4 the roles are
+// wm = p / 2 ^ g, wn = p % 2 ^ g, hf = p / 2, so the two waves of a SIMD differ
+// in both key half and query half.  On the last key tile or query tile of a
+// head, whose far half lies past L, every SIMD then keeps one wave of real work
+// while its partner (see scores_wave_idle) skips its MFMAs.
 constexpr int kScoresWaves = 8;
 constexpr int kScoresNJ = 2;
+__device__ __forceinline__ int scores_key_half(int wave) { return ((wave >> 1) ^ (wave >> 2)) & 1; }
 __device__ __forceinline__ int scores_query_base(int wave) {
-  return (wave & 1) * 128 + (wave >> 2) * 64;
+  return ((wave ^ (wave >> 2)) & 1) * 128 + ((wave >> 1) & 1) * 64;
 }
 
 // Tile idx of the pass: heads in order, then query tiles, then key tiles
@@ -116,6 +123,19 @@ __device__ __forceinline__ ScoresTile scores_tile(int idx, int T, int causal) {
   return t;
 }
 
+// True when every score of this wave's block in the tile is discarded: its keys
+// or its queries all lie past L, or (causal) all its keys follow all its
+// queries.  Such a wave issues its share of the loads and meets every barrier
+// but skips its fragment reads and MFMAs, and enters the epilogue with zero
+// accumulators, none of which reach memory: keys past L or after the query are
+// selected away, and rows past L are not stored (their maxima and sums are
+// exchanged only with the partner wave holding the same rows).
+__device__ __forceinline__ bool scores_wave_idle(const ScoresTile& t, int wave, int L, int causal) {
+  const int key0 = t.kt * kTile + scores_key_half(wave) * 128;
+  const int q0 = t.qt * kTile + scores_query_base(wave);
+  return key0 >= L || q0 >= L || (causal && key0 > q0 + 63);
+}
+
 template <bool MASK>
 __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ], ScoresSmem& sm,
                                                 uint16_t* __restrict__ E,
@@ -123,7 +143,7 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ], Sco
                                                 float* __restrict__ psum, const ScoresTile& t,
                                                 int L, int Ls, int T, float sl2, int causal) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave >> 1) & 1, c32 = lane & 31, h = lane >> 5;
+  const int wm = scores_key_half(wave), c32 = lane & 31, h = lane >> 5;
   const int qbase = scores_query_base(wave);  // this wave's first query column in the tile
   const int key0 = t.kt * kTile + wm * 128;
   uint16_t* Eh = E + (size_t)t.bh * L * Ls;
@@ -239,7 +259,7 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
   GemmSmem& sm = smem.g;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int abase = ((wave >> 1) & 1) * 128;  // key rows of this wave
+  const int abase = scores_key_half(wave) * 128;  // key rows of this wave
   const int bbase = scores_query_base(wave);  // query rows of this wave
   const int G = (int)gridDim.x;
   const int first = (int)xcd_logical_id(blockIdx.x, gridDim.x);
@@ -327,11 +347,34 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
     if (s + 2 < total) advance();
   };
 
+  // A step of a wave whose block of the tile is discarded: its loads and the
+  // barrier only.
+  auto idle_step = [&](int s) {
+    const int st = s & 1;
+    wait_vmem();
+    block_sync();
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      la.issue_one(rk, lk * kStepK, sm.a[st], wave, p);
+      lb.issue_one(rq, lk * kStepK, sm.b[st], wave, p);
+    }
+    if (s + 2 < total) advance();
+  };
+
   int s = 0;
   for (int i = 0; i < my_tiles; ++i) {
-    step(std::true_type{}, s++);
-    for (int kk = 1; kk < nk; ++kk) step(std::false_type{}, s++);
     const ScoresTile t = scores_tile(first + i * G, T, causal);
+    if (__builtin_amdgcn_readfirstlane((int)scores_wave_idle(t, wave, L, causal))) {
+      // Fresh (zero) accumulators: nothing stays live across tiles.
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < kScoresNJ; ++bj) acc[bi][bj] = f32x16{};
+      for (int kk = 0; kk < nk; ++kk) idle_step(s++);
+    } else {
+      step(std::true_type{}, s++);
+      for (int kk = 1; kk < nk; ++kk) step(std::false_type{}, s++);
+    }
     const bool need_mask = (t.kt + 1) * kTile > L || (causal && t.kt >= t.qt);
     if (need_mask)
       scores_epilogue<true>(acc, smem, E, mref, psum, t, L, Ls, T, sl2, causal);

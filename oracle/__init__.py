@@ -8,8 +8,10 @@ from .exact import (
     attention,
     attention_rows,
     causal_mask,
+    log_sum_exp,
     logits,
     probabilities,
+    row_log_sum_exp,
     softmax_rows,
     weighted_values,
 )
@@ -18,8 +20,10 @@ __all__ = [
     "attention",
     "attention_rows",
     "causal_mask",
+    "log_sum_exp",
     "logits",
     "probabilities",
+    "row_log_sum_exp",
     "softmax_rows",
     "weighted_values",
 ]

@@ -14,9 +14,16 @@ What it computes, and where the pages define it:
     subtracted before the exponential, then normalised by the row sum), times V,
     with an optional causal mask that removes keys after the query.
 
+  * cuDNN native_sparse_attention fmha.py, __call__ and the epilogue: the query
+    heads may be a multiple of the key/value heads, each key/value head serving
+    a group of consecutive query heads (a zero stride over the group index
+    broadcasts it); and the optional LSE output per query row, the log of the
+    row sum plus the scaled row maximum, i.e. log(sum_j exp(z_ij)).
+
 The method reaches exactly the plain definition (up to rounding order), so this
 oracle is that definition written out, one step per function, in the pages'
-order: logits, mask, row softmax, weighted sum of value rows.  Inputs are the
+order: logits, mask, row softmax, weighted sum of value rows; and for the LSE
+output the row maximum plus the log of the shifted row sum.  Inputs are the
 exact bf16 values as float64 arrays; the result is float64 and never rounded.
 
 Readings where the pages leave a step open (each listed in the design notes):
@@ -30,10 +37,12 @@ Readings where the pages leave a step open (each listed in the design notes):
 
 Pins (tests/test_oracle.py): brute-force loops with math.fsum on tiny inputs,
 closed forms (constant V, equal keys, causal row 0, scale 0, L = 1, a one-hot
-limit with huge logits, a hand-worked example in tests/golden), invariants
-(rows of P sum to 1, key-shift invariance, permutation equivariance, linearity
-in V) and a cross-check against torch's CPU float64 attention.  No function
-here is unpinned.
+limit with huge logits, a hand-worked example in tests/golden, log L and
+log(i + 1) for the LSE of equal keys, one constant value per key/value head
+for the head groups), invariants (rows of P sum to 1, key-shift invariance,
+permutation equivariance, linearity in V, the LSE's exact shift when every
+key moves by the same vector) and a cross-check against torch's CPU float64
+attention.  No function here is unpinned.
 """
 from __future__ import annotations
 
@@ -66,25 +75,38 @@ def weighted_values(P: np.ndarray, V: np.ndarray) -> np.ndarray:
     return P @ V
 
 
+def row_log_sum_exp(Z: np.ndarray) -> np.ndarray:
+    """log(sum_j exp(Z[r, j])) per row, as the row maximum plus the log of the
+    row sum of exp(Z - max) (the LSE the FMHA epilogue stores)."""
+    m = Z.max(axis=1)
+    assert np.all(np.isfinite(m)), "a row with every key masked"
+    return m + np.log(np.exp(Z - m[:, None]).sum(axis=1))
+
+
 def _head(x, b: int, h: int) -> np.ndarray:
     """One (batch, head) slice as float64 (exact for bf16 or float32 inputs)."""
     return np.asarray(x[b, h], dtype=np.float64)
 
 
 def _dims(q, k, v):
-    if not (len(np.shape(q)) == 4 and np.shape(q) == np.shape(k)
-            and np.shape(k)[:3] == np.shape(v)[:3]):
-        raise ValueError("q, k, v must be [B, H, L, d] sharing B, H, L (q, k share d)")
-    return np.shape(q)[:3]
+    """(B, H, L, group): q is [B, H, L, d]; k and v are [B, H_kv, L, .] with
+    H_kv dividing H, and query head h reads key/value head h // group."""
+    sq, sk, sv = np.shape(q), np.shape(k), np.shape(v)
+    if not (len(sq) == 4 and len(sk) == 4 and len(sv) == 4 and sq[0] == sk[0] == sv[0]
+            and sq[2] == sk[2] == sv[2] and sq[3] == sk[3] and sk[1] == sv[1]
+            and sk[1] >= 1 and sq[1] % sk[1] == 0):
+        raise ValueError("q must be [B, H, L, d] and k, v [B, H_kv, L, .] with H_kv dividing H "
+                         "(q, k share d)")
+    return sq[0], sq[1], sq[2], sq[1] // sk[1]
 
 
 def probabilities(q, k, scale: float, causal: bool = False) -> np.ndarray:
     """P = softmax(s * Q K^T) (masked when causal), shape [B, H, L, L]."""
-    B, H, L = _dims(q, k, k)
+    B, H, L, g = _dims(q, k, k)
     P = np.empty((B, H, L, L), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            Z = logits(_head(q, b, h), _head(k, b, h), scale)
+            Z = logits(_head(q, b, h), _head(k, b, h // g), scale)
             if causal:
                 Z = causal_mask(Z, np.arange(L))
             P[b, h] = softmax_rows(Z)
@@ -92,16 +114,33 @@ def probabilities(q, k, scale: float, causal: bool = False) -> np.ndarray:
 
 
 def attention(q, k, v, scale: float, causal: bool = False) -> np.ndarray:
-    """O = softmax(s * Q K^T) V for every (batch, head); float64 [B, H, L, d]."""
-    B, H, L = _dims(q, k, v)
-    O = np.empty(tuple(np.shape(v)), dtype=np.float64)
+    """O = softmax(s * Q K^T) V for every (batch, head); float64 [B, H, L, dv].
+
+    k and v may have fewer heads than q (H_kv dividing H): query head h then
+    reads key/value head h // (H / H_kv)."""
+    B, H, L, g = _dims(q, k, v)
+    O = np.empty((B, H, L, np.shape(v)[-1]), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            Z = logits(_head(q, b, h), _head(k, b, h), scale)
+            Z = logits(_head(q, b, h), _head(k, b, h // g), scale)
             if causal:
                 Z = causal_mask(Z, np.arange(L))
-            O[b, h] = weighted_values(softmax_rows(Z), _head(v, b, h))
+            O[b, h] = weighted_values(softmax_rows(Z), _head(v, b, h // g))
     return O
+
+
+def log_sum_exp(q, k, scale: float, causal: bool = False) -> np.ndarray:
+    """lse[b, h, i] = log(sum over allowed keys j of exp(s * q_i . k_j)); float64
+    [B, H, L].  Key heads are grouped as in attention()."""
+    B, H, L, g = _dims(q, k, k)
+    out = np.empty((B, H, L), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            Z = logits(_head(q, b, h), _head(k, b, h // g), scale)
+            if causal:
+                Z = causal_mask(Z, np.arange(L))
+            out[b, h] = row_log_sum_exp(Z)
+    return out
 
 
 def attention_rows(q, k, v, scale: float, causal: bool, rows) -> np.ndarray:
@@ -110,13 +149,14 @@ def attention_rows(q, k, v, scale: float, causal: bool, rows) -> np.ndarray:
     ``rows`` is a sequence of (b, h, i); returns float64 [len(rows), d].  Used to
     check full-size runs on a sample of rows the oracle can afford one by one.
     """
+    g = _dims(q, k, v)[3]
     out = np.empty((len(rows), np.shape(v)[-1]), dtype=np.float64)
     cache = {}
     for r, (b, h, i) in enumerate(rows):
-        if (b, h) not in cache:
+        if (b, h // g) not in cache:
             cache.clear()  # one head's K and V in float64 at a time
-            cache[(b, h)] = (_head(k, b, h), _head(v, b, h))
-        K, V = cache[(b, h)]
+            cache[(b, h // g)] = (_head(k, b, h // g), _head(v, b, h // g))
+        K, V = cache[(b, h // g)]
         Z = logits(np.asarray(q[b, h, i : i + 1], dtype=np.float64), K, scale)
         if causal:
             Z = causal_mask(Z, np.array([i]))

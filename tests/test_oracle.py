@@ -272,3 +272,148 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
     attr, bad = MUTANTS[name]
     monkeypatch.setattr(oa, attr, bad)
     assert not _pins_pass(), f"pins did not catch mutant {name}"
+
+
+# ---- log-sum-exp output and grouped key/value heads --------------------------
+
+def brute_force_lse(q, k, scale, causal):
+    """log(sum_j exp(s q_i . k_j)) with scalar loops, math.fsum and no max shift
+    (the tiny cases keep every logit small)."""
+    B, H, L, d = q.shape
+    g = H // k.shape[1]
+    out = np.zeros((B, H, L))
+    for b in range(B):
+        for h in range(H):
+            for i in range(L):
+                keys = range(i + 1) if causal else range(L)
+                z = [scale * math.fsum(q[b, h, i, c] * k[b, h // g, j, c] for c in range(d)) for j in keys]
+                out[b, h, i] = math.log(math.fsum(math.exp(x) for x in z))
+    return out
+
+
+@pytest.mark.parametrize("B,H,L,d,scale,causal", TINY)
+def test_lse_brute_force_tiny(B, H, L, d, scale, causal):
+    q, k = rnd((B, H, L, d), 60 + L), rnd((B, H, L, d), 61 + d)
+    assert close(oracle.log_sum_exp(q, k, scale, causal), brute_force_lse(q, k, scale, causal))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_equal_keys_is_logit_plus_log_count(causal):
+    # every key equal to k0: each allowed logit is s q_i . k0, so the sum is
+    # (number of allowed keys) * exp(s q_i . k0)
+    L, d, s = 11, 6, 0.4
+    q = rnd((1, 1, L, d), 62)
+    k0 = rnd((d,), 63)
+    k = np.broadcast_to(k0, (1, 1, L, d)).copy()
+    count = np.arange(1, L + 1) if causal else np.full(L, L)
+    expected = s * (q[0, 0] @ k0) + np.log(count)
+    assert close(oracle.log_sum_exp(q, k, s, causal)[0, 0], expected)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_scale_zero_is_log_count(causal):
+    L = 9
+    q, k = rnd((1, 2, L, 4), 64), rnd((1, 2, L, 4), 65)
+    count = np.arange(1, L + 1) if causal else np.full(L, L)
+    got = oracle.log_sum_exp(q, k, 0.0, causal)
+    assert close(got, np.broadcast_to(np.log(count), got.shape))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_shifts_with_a_common_key_offset(causal):
+    # k_j -> k_j + c adds s q_i . c to every logit of row i, hence to its LSE
+    L, d, s = 10, 5, 0.6
+    q, k = rnd((1, 1, L, d), 66), rnd((1, 1, L, d), 67)
+    c = rnd((d,), 68)
+    base = oracle.log_sum_exp(q, k, s, causal)[0, 0]
+    shifted = oracle.log_sum_exp(q, k + c, s, causal)[0, 0]
+    assert close(shifted - base, s * (q[0, 0] @ c))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_torch_logsumexp(causal):
+    L, d, s = 17, 8, 0.9
+    q, k = rnd((2, 3, L, d), 69), rnd((2, 3, L, d), 70)
+    z = s * torch.from_numpy(q) @ torch.from_numpy(k).transpose(-1, -2).contiguous()
+    if causal:
+        z = z.masked_fill(torch.ones(L, L, dtype=torch.bool).triu(1), float("-inf"))
+    assert close(oracle.log_sum_exp(q, k, s, causal), torch.logsumexp(z, dim=-1).numpy())
+
+
+def test_lse_ties_probabilities():
+    # P_ij = exp(z_ij - lse_i) for the allowed keys
+    L, d, s = 8, 4, 0.7
+    q, k = rnd((1, 1, L, d), 71), rnd((1, 1, L, d), 72)
+    P = oracle.probabilities(q, k, s, True)[0, 0]
+    Z = oracle.causal_mask(oracle.logits(q[0, 0], k[0, 0], s), np.arange(L))
+    with np.errstate(all="ignore"):
+        assert close(np.exp(Z - oracle.log_sum_exp(q, k, s, True)[0, 0][:, None]), P)
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 2), (6, 3), (6, 1), (3, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_heads_constant_values(H, H_kv, causal):
+    # key/value head j holds the constant value j + 1: every output row of query
+    # head h is then exactly h // (H / H_kv) + 1 (consecutive query heads share a
+    # key/value head; an interleaved h % H_kv mapping would differ for H = 4, 6)
+    L, d = 7, 4
+    q, k = rnd((2, H, L, d), 73), rnd((2, H_kv, L, d), 74)
+    v = np.broadcast_to((np.arange(H_kv) + 1.0)[None, :, None, None], (2, H_kv, L, 3)).copy()
+    o = oracle.attention(q, k, v, 0.5, causal)
+    want = (np.arange(H) // (H // H_kv) + 1.0)[None, :, None, None]
+    assert np.allclose(o, np.broadcast_to(want, o.shape), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_heads_equal_repeated_heads(causal):
+    # a grouped call equals the one-to-one call on key/value heads repeated
+    # consecutively, which the brute force pins
+    B, H, H_kv, L, d = 1, 4, 2, 6, 3
+    q, k, v = rnd((B, H, L, d), 75), rnd((B, H_kv, L, d), 76), rnd((B, H_kv, L, d), 77)
+    kr, vr = np.repeat(k, H // H_kv, axis=1), np.repeat(v, H // H_kv, axis=1)
+    assert close(oracle.attention(q, k, v, 0.8, causal), brute_force(q, kr, vr, 0.8, causal))
+    assert close(oracle.log_sum_exp(q, k, 0.8, causal), brute_force_lse(q, kr, 0.8, causal))
+    rows = [(0, h, i) for h in range(H) for i in (0, L - 1)]
+    assert close(oracle.attention_rows(q, k, v, 0.8, causal, rows),
+                 np.stack([brute_force(q, kr, vr, 0.8, causal)[b, h, i] for b, h, i in rows]))
+
+
+def test_grouped_heads_dimension_errors():
+    with pytest.raises(ValueError):  # 3 query heads over 2 key/value heads
+        oracle.attention(np.zeros((1, 3, 4, 2)), np.zeros((1, 2, 4, 2)), np.zeros((1, 2, 4, 2)), 1.0)
+    with pytest.raises(ValueError):  # k and v head counts differ
+        oracle.attention(np.zeros((1, 4, 4, 2)), np.zeros((1, 2, 4, 2)), np.zeros((1, 4, 4, 2)), 1.0)
+
+
+def _lse_pins_pass():
+    try:
+        for B, H, L, d, scale, causal in [(1, 2, 7, 4, 0.5, True), (1, 1, 6, 3, 0.7, False)]:
+            q, k = rnd((B, H, L, d), 80), rnd((B, H, L, d), 81)
+            if not close(oracle.log_sum_exp(q, k, scale, causal), brute_force_lse(q, k, scale, causal)):
+                return False
+        L = 5
+        q = rnd((1, 1, L, 3), 82)
+        k = np.broadcast_to(rnd((3,), 83), (1, 1, L, 3)).copy()
+        if not close(oracle.log_sum_exp(q, k, 0.0, True)[0, 0], np.log(np.arange(1, L + 1))):
+            return False
+        return True
+    except (AssertionError, ValueError, FloatingPointError):
+        return False
+
+
+LSE_MUTANTS = {
+    "lse_max_dropped": lambda Z: np.log(np.exp(Z - Z.max(1, keepdims=True)).sum(1)),
+    "lse_log2": lambda Z: Z.max(1) + np.log2(np.exp(Z - Z.max(1, keepdims=True)).sum(1)),
+    "lse_mean_not_sum": lambda Z: Z.max(1) + np.log(np.exp(Z - Z.max(1, keepdims=True)).mean(1)),
+    "lse_max_only": lambda Z: Z.max(1),
+}
+
+
+def test_lse_pins_pass_unmutated():
+    assert _lse_pins_pass()
+
+
+@pytest.mark.parametrize("name", sorted(LSE_MUTANTS))
+def test_lse_pins_catch_planted_mistake(name, monkeypatch):
+    monkeypatch.setattr(oa, "row_log_sum_exp", LSE_MUTANTS[name])
+    assert not _lse_pins_pass(), f"pins did not catch mutant {name}"

@@ -22,6 +22,7 @@ ATTN_ERR_ALIAS = 6
 ATTN_ERR_WORKSPACE = 7
 ATTN_ERR_HIP = 8
 ATTN_ERR_TOO_LARGE = 9
+ATTN_ERR_BAD_STRIDE = 10
 
 ATTN_PATH_NONE = -1
 ATTN_PATH_ONLINE = 0
@@ -34,6 +35,13 @@ SIGNATURES = {
     "attn_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "attn_forward_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                       ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                       ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_path_for_head_dim": (ctypes.c_int, [ctypes.c_int64]),
     "attn_workspace_bytes": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,

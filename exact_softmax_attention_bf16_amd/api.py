@@ -14,7 +14,8 @@ import torch
 from . import _lib
 
 
-def _check(t: torch.Tensor, name: str, like: torch.Tensor | None = None) -> None:
+def _check(t: torch.Tensor, name: str, shape: tuple | None = None,
+           device: torch.device | None = None) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != torch.bfloat16:
@@ -22,46 +23,86 @@ def _check(t: torch.Tensor, name: str, like: torch.Tensor | None = None) -> None
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a HIP (cuda) device, got {t.device}")
     if t.dim() != 4:
-        raise ValueError(f"{name} must be [B, H, L, d], got shape {tuple(t.shape)}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if like is not None:
-        if t.shape != like.shape:
-            raise ValueError(f"{name} shape {tuple(t.shape)} != q shape {tuple(like.shape)}")
-        if t.device != like.device:
-            raise ValueError(f"{name} is on {t.device}, q on {like.device}")
+        raise ValueError(f"{name} must be [B, heads, L, d], got shape {tuple(t.shape)}")
+    if t.numel() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have contiguous channels (last stride 1)")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} shape {tuple(t.shape)} != expected {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, q on {device}")
+
+
+def _strides(t: torch.Tensor):
+    return (ctypes.c_int64 * 3)(*t.stride()[:3])
+
+
+def _call(fn, q: torch.Tensor, *args) -> None:
+    """Call a forward entry point on q's device and its current stream."""
+    if q.device.index == torch.cuda.current_device():
+        status = fn(*args, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    else:  # the library launches on the current device: switch to q's for the call
+        with torch.cuda.device(q.device):
+            status = fn(*args, ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream))
+    if status != _lib.ATTN_OK:
+        raise _lib.AttnError(status, fn.__name__)
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
-              causal: bool = False, out: torch.Tensor | None = None) -> torch.Tensor:
-    """O = softmax(scale * Q K^T) V for bf16 [B, H, L, d] tensors (HIP kernels only).
+              causal: bool = False, out: torch.Tensor | None = None, return_lse: bool = False):
+    """O = softmax(scale * Q K^T) V on bf16 tensors (HIP kernels only).
 
-    ``scale`` defaults to 1/sqrt(d).  ``out``, if given, must be a contiguous bf16
-    tensor of q's shape that overlaps none of the inputs.  Work is queued on the
-    current stream of q's device.
+    q is [B, H, L, d]; k and v are [B, H_kv, L, d] with H_kv dividing H (query
+    head h reads key/value head h // (H / H_kv): grouped or multi-query
+    attention).  Any strides with contiguous channels are read in place
+    (strides must be multiples of 8 elements).  ``scale`` defaults to 1/sqrt(d).
+    ``out``, if given, is a bf16 [B, H, L, d] tensor (any strides whose elements
+    do not overlap) that overlaps none of the inputs.  With ``return_lse`` the
+    result is (out, lse), lse float32 [B, H, L] holding each row's
+    log(sum_j exp(scale * q . k_j)).  Work is queued on the current stream of
+    q's device.
     """
     _check(q, "q")
-    _check(k, "k", q)
-    _check(v, "v", q)
     B, H, L, d = q.shape
+    if not isinstance(k, torch.Tensor) or k.dim() != 4:
+        raise ValueError("k must be a 4-D tensor [B, H_kv, L, d]")
+    H_kv = k.shape[1]
+    _check(k, "k", (B, H_kv, L, d), q.device)
+    _check(v, "v", (B, H_kv, L, d), q.device)
+    if H_kv == 0 and H > 0 or H_kv > 0 and H % H_kv != 0:
+        raise ValueError(f"key/value heads ({H_kv}) must divide query heads ({H})")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((B, H, L, d), dtype=torch.bfloat16, device=q.device)
     else:
-        _check(out, "out", q)
+        _check(out, "out", (B, H, L, d), q.device)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if return_lse else None
     lib = _lib.load()
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, L, d, float(scale),
-            1 if causal else 0)
-    if q.device.index == torch.cuda.current_device():
-        status = lib.attn_forward(*args, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-    else:  # the library launches on the current device: switch to q's for the call
-        with torch.cuda.device(q.device):
-            status = lib.attn_forward(
-                *args, ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream))
-    if status != _lib.ATTN_OK:
-        raise _lib.AttnError(status)
-    return out
+    plain = (H_kv == H and lse is None
+             and all(t.is_contiguous() for t in (q, k, v, out)))
+    if plain:
+        _call(lib.attn_forward, q, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+              B, H, L, d, float(scale), 1 if causal else 0)
+    else:
+        _call(lib.attn_forward_ex, q, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+              lse.data_ptr() if lse is not None else None, B, H, H_kv, L, d,
+              _strides(q), _strides(k), _strides(v), _strides(out), float(scale),
+              1 if causal else 0)
+    return (out, lse) if return_lse else out
+
+
+def attention_packed_qkv(qkv: torch.Tensor, scale: float | None = None, causal: bool = False,
+                         out: torch.Tensor | None = None, return_lse: bool = False):
+    """Attention over a packed [B, H, L, 3d] tensor whose last dimension holds
+    q, k and v in that order -- the [T, 1, HW, 3C] qkv of the FastVideo Wan2.2
+    VAE decoder's attention (frames T as B, one head) -- read in place through
+    strides, with no copy.  Returns out [B, H, L, d] (and lse, as attention())."""
+    _check(qkv, "qkv")
+    if qkv.shape[-1] % 3 != 0:
+        raise ValueError(f"qkv's last dimension ({qkv.shape[-1]}) must be 3 * d")
+    d = qkv.shape[-1] // 3
+    q, k, v = qkv[..., :d], qkv[..., d:2 * d], qkv[..., 2 * d:]
+    return attention(q, k, v, scale=scale, causal=causal, out=out, return_lse=return_lse)
 
 
 def path_for_head_dim(d: int) -> int:

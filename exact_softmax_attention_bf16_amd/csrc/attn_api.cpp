@@ -162,8 +162,9 @@ hipError_t timed(int id, hipStream_t s, bool on, F&& launch) {
   return hipSuccess;
 }
 
-int run_two_pass(const void* q, const void* k, const void* v, void* out, int64_t BH, int64_t L,
-                 int64_t d, float sl2, bool causal, hipStream_t stream) {
+int run_two_pass(const void* q, const void* k, const void* v, void* out, float* lse,
+                 attn::HeadMap hm, int64_t BH, int64_t L, int64_t d, float sl2, bool causal,
+                 hipStream_t stream) {
   const attn::TwoPassDims t = attn::two_pass_dims(L, d);
   const int64_t per_head = attn::two_pass_head_bytes(t);
   const int64_t chunk = heads_per_chunk(BH, per_head);
@@ -175,14 +176,10 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, int64_t
     return ATTN_ERR_WORKSPACE;
   char* base = (char*)wsp->ptr;
 
-  const int64_t head_elems = L * d;
   hipError_t err = hipSuccess;
   for (int64_t h0 = 0; h0 < BH && err == hipSuccess; h0 += chunk) {
     const int n = (int)((BH - h0) < chunk ? (BH - h0) : chunk);
-    const uint16_t* qc = (const uint16_t*)q + h0 * head_elems;
-    const uint16_t* kc = (const uint16_t*)k + h0 * head_elems;
-    const uint16_t* vc = (const uint16_t*)v + h0 * head_elems;
-    uint16_t* oc = (uint16_t*)out + h0 * head_elems;
+    hm.bh0 = (int)h0;  // the kernels find the chunk's heads through the map
     // This chunk's layout: E, the two statistics tables, the partial outputs.
     const int64_t e_bytes = round256((int64_t)t.L * t.Ls * 2) * n;
     const int64_t st_bytes = round256((int64_t)t.T * t.L * 4) * n;
@@ -192,21 +189,83 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, int64_t
     float* part = (float*)(base + e_bytes + 2 * st_bytes);
     const int split = attn::values_split(n, t, causal);
     err = timed(ATTN_KERNEL_SCORES, stream, on, [&] {
-      return attn::launch_scores(qc, kc, E, mref, psum, n, t, sl2, causal, stream);
+      return attn::launch_scores(q, k, E, mref, psum, hm, n, t, sl2, causal, stream);
     });
     if (err == hipSuccess)
       err = timed(ATTN_KERNEL_VALUES, stream, on, [&] {
-        return attn::launch_values(vc, E, mref, psum, oc, part, split, n, t, causal, stream);
+        return attn::launch_values(v, E, mref, psum, out, lse, part, split, hm, n, t, causal,
+                                   stream);
       });
     if (err == hipSuccess && split > 1)
       err = timed(ATTN_KERNEL_VALUES_REDUCE, stream, on, [&] {
-        return attn::launch_values_reduce(part, oc, split, n, t, stream);
+        return attn::launch_values_reduce(part, out, split, hm, n, t, stream);
       });
   }
   const hipError_t rerr = release_workspace(stream, wsp);
   if (err != hipSuccess || rerr != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
+
+// Checks shared by both forward entry points, after the shape and pointer
+// checks: the kernels' 32-bit offsets and int head counts, then the launches.
+// ld_max: the largest row stride of q, k and v (elements).
+int forward(const void* q, const void* k, const void* v, void* out, float* lse,
+            const attn::HeadMap& hm, int64_t bh, int64_t L, int64_t d, int64_t ld_max,
+            float scale, int causal, hipStream_t stream) {
+  // Kernels address one head with 32-bit byte offsets (rows up to L + 255 are
+  // formed, past-the-end ones read as zero) and count heads in int.
+  if ((L + 256) * ld_max * 2 >= ((int64_t)1 << 31) || bh >= ((int64_t)1 << 31) / 1024)
+    return ATTN_ERR_TOO_LARGE;
+  const float sl2 = scale * 1.4426950408889634f;
+  const bool c = causal != 0;
+
+  if (attn_path_for_head_dim(d) == ATTN_PATH_ONLINE) {
+    const int64_t nqb = (L + 127) / 128;
+    if (nqb * bh >= ((int64_t)1 << 31)) return ATTN_ERR_TOO_LARGE;
+    const hipError_t e = timed(ATTN_KERNEL_ONLINE, stream, timing_on(), [&] {
+      return attn::launch_online(q, k, v, out, lse, hm, (int)bh, (int)L, (int)d, sl2, c, stream);
+    });
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  }
+  const attn::TwoPassDims t = attn::two_pass_dims(L, d);
+  // E rows are addressed up to (L + 255) * Ls * 2 bytes inside a head.
+  if (t.T > attn::kTwoPassMaxTiles || (int64_t)(t.L + 256) * t.Ls * 2 >= ((int64_t)1 << 32) - 1 ||
+      (int64_t)t.T * t.T * bh >= ((int64_t)1 << 31))
+    return ATTN_ERR_TOO_LARGE;
+  return run_two_pass(q, k, v, out, lse, hm, bh, L, d, sl2, c, stream);
+}
+
+// One operand of attn_forward_ex: dims [B, heads, L, d] with element strides
+// st[0..2] (batch, head, row) and unit channel stride.
+struct View {
+  int64_t n[3];
+  int64_t st[3];
+  int64_t d;
+  // Elements from the first to one past the last addressed element.
+  int64_t span() const {
+    int64_t e = d;
+    for (int i = 0; i < 3; ++i) e += (n[i] - 1) * st[i];
+    return e;
+  }
+  bool strides_valid() const {
+    for (int i = 0; i < 3; ++i)
+      if (st[i] < 0 || st[i] % 8 != 0) return false;
+    return st[2] >= d;
+  }
+  // No two elements share an address: with the dims of extent > 1 sorted by
+  // stride, each stride is at least the span of the smaller ones.
+  bool one_to_one() const {
+    int idx[3] = {0, 1, 2};
+    std::sort(idx, idx + 3, [&](int a, int b) { return st[a] < st[b]; });
+    int64_t span_below = d;
+    for (int i : idx) {
+      if (n[i] <= 1) continue;
+      if (st[i] < span_below) return false;
+      span_below += (n[i] - 1) * st[i];
+    }
+    return true;
+  }
+};
 
 }  // namespace
 
@@ -225,6 +284,9 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_WORKSPACE: return "workspace allocation failed";
     case ATTN_ERR_HIP: return "a HIP launch or runtime call failed";
     case ATTN_ERR_TOO_LARGE: return "problem too large: one head exceeds 32-bit byte offsets, or L > 31744 with d > 128";
+    case ATTN_ERR_BAD_STRIDE:
+      return "bad strides: negative, not a multiple of 8 elements, a row stride below d, or an "
+             "output layout whose elements overlap";
     default: return "unknown status";
   }
 }
@@ -257,28 +319,71 @@ int attn_forward(const void* q, const void* k, const void* v, void* out, int64_t
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15) return ATTN_ERR_MISALIGNED;
   if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
     return ATTN_ERR_ALIAS;
+  if (L > ((int64_t)1 << 30) || H > ((int64_t)1 << 30)) return ATTN_ERR_TOO_LARGE;
+  return forward(q, k, v, out, nullptr, attn::contiguous_heads((int)H, (int)L, (int)d), bh, L, d,
+                 d, scale, causal, stream);
+}
 
-  // Kernels address one head with 32-bit byte offsets and count heads in int.
-  const int64_t head_bytes = L * d * 2;
-  if (head_bytes + (int64_t)256 * d * 2 >= ((int64_t)1 << 31) || bh >= ((int64_t)1 << 31) / 1024)
-    return ATTN_ERR_TOO_LARGE;
-  const float sl2 = scale * 1.4426950408889634f;
-  const bool c = causal != 0;
+int attn_forward_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                    int64_t B, int64_t H, int64_t H_kv, int64_t L, int64_t d,
+                    const int64_t* q_strides, const int64_t* k_strides,
+                    const int64_t* v_strides, const int64_t* o_strides, float scale, int causal,
+                    hipStream_t stream) {
+  if (B < 0 || H < 0 || H_kv < 0 || L < 0 || d < 0) return ATTN_ERR_BAD_SHAPE;
+  int64_t bh = 0, rows = 0, elems = 0, bytes = 0;
+  if (__builtin_mul_overflow(B, H, &bh) || __builtin_mul_overflow(bh, L, &rows) ||
+      __builtin_mul_overflow(rows, d, &elems) || __builtin_mul_overflow(elems, (int64_t)2, &bytes))
+    return ATTN_ERR_BAD_SHAPE;
+  if (H > 0 && (H_kv < 1 || H % H_kv != 0)) return ATTN_ERR_BAD_SHAPE;
+  if (!head_dim_supported(d)) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+  if (rows == 0) return ATTN_OK;
+  if (!q || !k || !v || !out) return ATTN_ERR_NULL_PTR;
+  if (L > ((int64_t)1 << 30) || H > ((int64_t)1 << 30)) return ATTN_ERR_TOO_LARGE;
 
-  if (attn_path_for_head_dim(d) == ATTN_PATH_ONLINE) {
-    const int64_t nqb = (L + 127) / 128;
-    if (nqb * bh >= ((int64_t)1 << 31)) return ATTN_ERR_TOO_LARGE;
-    const hipError_t e = timed(ATTN_KERNEL_ONLINE, stream, timing_on(), [&] {
-      return attn::launch_online(q, k, v, out, (int)bh, (int)L, (int)d, sl2, c, stream);
-    });
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  // Views with the default (contiguous) strides where none are given.
+  auto make = [&](const int64_t* st, int64_t heads) {
+    View w{{B, heads, L}, {heads * L * d, L * d, d}, d};
+    if (st)
+      for (int i = 0; i < 3; ++i) w.st[i] = st[i];
+    return w;
+  };
+  const View vq = make(q_strides, H), vk = make(k_strides, H_kv), vv = make(v_strides, H_kv),
+             vo = make(o_strides, H);
+  for (const View* w : {&vq, &vk, &vv, &vo}) {
+    if (!w->strides_valid()) return ATTN_ERR_BAD_STRIDE;
+    // Spans beyond int64 bytes cannot describe memory.
+    if (w->st[0] > (INT64_MAX / 8) / std::max<int64_t>(B, 1) ||
+        w->st[1] > (INT64_MAX / 8) / std::max<int64_t>(H, 1) ||
+        w->st[2] > (INT64_MAX / 8) / std::max<int64_t>(L, 1))
+      return ATTN_ERR_BAD_STRIDE;
   }
-  const attn::TwoPassDims t = attn::two_pass_dims(L, d);
-  // E rows are addressed up to (L + 255) * Ls * 2 bytes inside a head.
-  if (t.T > attn::kTwoPassMaxTiles || (int64_t)(t.L + 256) * t.Ls * 2 >= ((int64_t)1 << 32) - 1 ||
-      (int64_t)t.T * t.T * bh >= ((int64_t)1 << 31))
-    return ATTN_ERR_TOO_LARGE;
-  return run_two_pass(q, k, v, out, bh, L, d, sl2, c, stream);
+  if (!vo.one_to_one()) return ATTN_ERR_BAD_STRIDE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15 || ((uintptr_t)lse & 3))
+    return ATTN_ERR_MISALIGNED;
+  const int64_t ob = vo.span() * 2;
+  if (overlaps(out, ob, q, vq.span() * 2) || overlaps(out, ob, k, vk.span() * 2) ||
+      overlaps(out, ob, v, vv.span() * 2))
+    return ATTN_ERR_ALIAS;
+  if (lse) {
+    const int64_t lb = rows * 4;
+    if (overlaps(lse, lb, out, ob) || overlaps(lse, lb, q, vq.span() * 2) ||
+        overlaps(lse, lb, k, vk.span() * 2) || overlaps(lse, lb, v, vv.span() * 2))
+      return ATTN_ERR_ALIAS;
+  }
+  for (const View* w : {&vq, &vk, &vv, &vo})
+    if (w->st[2] >= ((int64_t)1 << 30)) return ATTN_ERR_TOO_LARGE;
+
+  attn::HeadMap hm;
+  hm.H = (int)H;
+  hm.group = (int)(H / H_kv);
+  hm.bh0 = 0;
+  hm.q = {vq.st[0], vq.st[1], (int)vq.st[2]};
+  hm.k = {vk.st[0], vk.st[1], (int)vk.st[2]};
+  hm.v = {vv.st[0], vv.st[1], (int)vv.st[2]};
+  hm.o = {vo.st[0], vo.st[1], (int)vo.st[2]};
+  const int64_t ld_max = std::max(vq.st[2], std::max(vk.st[2], vv.st[2]));
+  return forward(q, k, v, out, lse, hm, bh, L, d, ld_max, scale, causal, stream);
 }
 
 int attn_timing_enable(int enable) {

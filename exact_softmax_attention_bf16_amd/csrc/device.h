@@ -27,8 +27,17 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // Buffer resource over [base, base + bytes).  Loads past `bytes` return zero,
 // which is how every kernel here pads the ragged tail of a tile.
+// Every caller passes wave-uniform values; they are read from lane 0 so that
+// the compiler keeps the descriptor in scalar registers even when it cannot
+// prove them uniform (e.g. after an integer division it expanded on the VALU),
+// instead of wrapping each load in a loop over distinct descriptors.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* p = (void*)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           0x00020000);
 }
 
 // 16 bytes from byte offset `voff` into registers (zero when out of range).

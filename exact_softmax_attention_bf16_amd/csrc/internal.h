@@ -6,6 +6,46 @@
 
 namespace attn {
 
+// Element strides of one bf16 operand viewed as [B, heads, L, d] with
+// contiguous channels: rows of a head are `ld` elements apart.
+struct Strides {
+  int64_t b, h;  // batch and head strides
+  int ld;        // row stride, >= d, a multiple of 8 (16-byte rows)
+};
+
+// Where the heads of one launch live.  Launch head i is global head
+// bh = bh0 + i = b * H + h; query head h reads key/value head h / group.
+struct HeadMap {
+  int H;      // query heads per batch entry
+  int group;  // query heads per key/value head
+  int bh0;    // global index of the launch's first head
+  Strides q, k, v, o;
+
+  __host__ __device__ int64_t q_off(int i) const { return off(q, i, 1); }
+  __host__ __device__ int64_t k_off(int i) const { return off(k, i, group); }
+  __host__ __device__ int64_t v_off(int i) const { return off(v, i, group); }
+  __host__ __device__ int64_t o_off(int i) const { return off(o, i, 1); }
+  __host__ __device__ int64_t off(const Strides& s, int i, int g) const {
+    const int bh = bh0 + i, b = bh / H, h = bh - b * H;
+    return (int64_t)b * s.b + (int64_t)(h / g) * s.h;
+  }
+};
+
+// Contiguous [B, H, L, d] operands, H query and key/value heads.
+inline HeadMap contiguous_heads(int H, int L, int d) {
+  const Strides s{(int64_t)H * L * d, (int64_t)L * d, d};
+  return HeadMap{H, 1, 0, s, s, s, s};
+}
+
+// True when the map is contiguous_heads(H, L, d): head bh of every operand
+// starts at bh * L * d.
+inline bool is_plain(const HeadMap& m, int L, int d) {
+  auto dense = [&](const Strides& s) {
+    return s.ld == d && s.h == (int64_t)L * d && s.b == (int64_t)m.H * L * d;
+  };
+  return m.group == 1 && dense(m.q) && dense(m.k) && dense(m.v) && dense(m.o);
+}
+
 // Sizes of the two-pass path's per-head staging, all in elements.
 struct TwoPassDims {
   int L;   // sequence length
@@ -27,14 +67,18 @@ constexpr int kTwoPassMaxTiles = 124;
 int64_t two_pass_head_bytes(const TwoPassDims& t);
 
 // Fused online-softmax kernel, d in {32, 64, 128}.  sl2 = scale * log2(e).
-hipError_t launch_online(const void* q, const void* k, const void* v, void* out, int BH, int L,
-                         int d, float sl2, bool causal, hipStream_t s);
+// lse (may be null): fp32 [global head][L], the natural log of each row's
+// softmax denominator.
+hipError_t launch_online(const void* q, const void* k, const void* v, void* out, float* lse,
+                         const HeadMap& hm, int BH, int L, int d, float sl2, bool causal,
+                         hipStream_t s);
 
 // Scores pass: per 256x256 (key, query) tile, E = bf16(2^(y - m)) with
 // y = sl2 * q.k, m = ceil(max over the tile's keys of y) per query, plus m and
 // the sum of the stored E per (tile, query).
-hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, float* psum, int BH,
-                         const TwoPassDims& t, float sl2, bool causal, hipStream_t s);
+hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, float* psum,
+                         const HeadMap& hm, int BH, const TwoPassDims& t, float sl2, bool causal,
+                         hipStream_t s);
 
 // Values pass: O = (sum over tiles of 2^(m_t - M) E_t V_t) / (sum_t 2^(m_t - M) psum_t).
 // With split > 1 the keys of each query tile are divided among `split`
@@ -46,10 +90,11 @@ constexpr int kValuesMinSplitSteps = 8;  // K steps (64 keys each) per split at 
 // Splits used for BH heads: 1 unless the unsplit grid would leave at least half
 // of the compute units idle.  Depends on the shape only.
 int values_split(int64_t BH, const TwoPassDims& t, bool causal);
+// lse as for launch_online.
 hipError_t launch_values(const void* v, const void* E, const float* mref, const float* psum,
-                         void* out, float* part, int split, int BH, const TwoPassDims& t,
-                         bool causal, hipStream_t s);
-hipError_t launch_values_reduce(const float* part, void* out, int split, int BH,
-                                const TwoPassDims& t, hipStream_t s);
+                         void* out, float* lse, float* part, int split, const HeadMap& hm, int BH,
+                         const TwoPassDims& t, bool causal, hipStream_t s);
+hipError_t launch_values_reduce(const float* part, void* out, int split, const HeadMap& hm,
+                                int BH, const TwoPassDims& t, hipStream_t s);
 
 }  // namespace attn

@@ -28,6 +28,9 @@
 //     the current one is consumed.
 //   * Keys past L (and, when causal, past the query) are masked to -inf; loads
 //     past the end of a head return zero through the buffer resource bounds.
+//   * Heads are found through a HeadMap (any batch, head and row strides with
+//     contiguous channels; one key/value head per `group` query heads), and
+//     the merged (m, l) give each row's log-sum-exp when it is asked for.
 #include "device.h"
 #include "internal.h"
 
@@ -49,12 +52,16 @@ struct OnlineSmem {
   char vbuf[kGroups][2][VT_BYTES];
 };
 
-template <int D, bool CAUSAL>
+// PLAIN: q, k, v and out are contiguous [B, H, L, D] with one key/value head
+// per query head, so head bh starts at bh * L * D (no division by H, whose
+// expansion would sit ahead of the first load of this short kernel).
+template <int D, bool CAUSAL, bool PLAIN>
 __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v,
-                                                          uint16_t* __restrict__ out, int L,
-                                                          int nqb, float sl2) {
+                                                          uint16_t* __restrict__ out,
+                                                          float* __restrict__ lse, HeadMap hm,
+                                                          int L, int nqb, float sl2) {
   constexpr int CPR = D / 8;                       // 16-byte chunks per K row
   constexpr int SWZ = (CPR >= 8 ? 8 : CPR) - 1;    // chunk-index bits that are swizzled
   constexpr int VROW = kBN * 2 + 8;                // bytes per V^T row: 64 keys + pad
@@ -69,8 +76,9 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   __shared__ OnlineSmem<D> smem;
 
   const int ltid = threadIdx.x & 255, lane = threadIdx.x & 63;
-  const int g = threadIdx.x >> 8;           // key-block group
-  const int wave = (threadIdx.x >> 6) & 3;  // query wave within the group
+  // Wave-uniform, read from lane 0 so that the branches on them are scalar.
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);             // key-block group
+  const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);  // query wave in the group
   const int c32 = lane & 31, h = lane >> 5;
   auto& kbuf = smem.kbuf[g];
   auto& vbuf = smem.vbuf[g];
@@ -80,11 +88,12 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   int qb = lid % nqb;
   if (CAUSAL) qb = nqb - 1 - qb;  // the longest rows start first
 
-  const size_t head = (size_t)bh * L * D;
-  const uint32_t head_bytes = (uint32_t)L * D * 2;
-  const auto rq = make_rsrc(q + head, head_bytes);
-  const auto rk = make_rsrc(k + head, head_bytes);
-  const auto rv = make_rsrc(v + head, head_bytes);
+  // Rows past L of each head read as zero: the resources end after row L - 1.
+  const int ldq = PLAIN ? D : hm.q.ld, ldk = PLAIN ? D : hm.k.ld, ldv = PLAIN ? D : hm.v.ld;
+  const int64_t plain_off = (int64_t)(hm.bh0 + bh) * L * D;
+  const auto rq = make_rsrc(q + (PLAIN ? plain_off : hm.q_off(bh)), ((uint32_t)(L - 1) * ldq + D) * 2);
+  const auto rk = make_rsrc(k + (PLAIN ? plain_off : hm.k_off(bh)), ((uint32_t)(L - 1) * ldk + D) * 2);
+  const auto rv = make_rsrc(v + (PLAIN ? plain_off : hm.v_off(bh)), ((uint32_t)(L - 1) * ldv + D) * 2);
 
   const int q0 = qb * kBM + wave * 32;  // first query of this wave
   const int myq = q0 + c32;             // this lane's query
@@ -93,7 +102,7 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   bf16x8 qf[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s)
-    qf[s] = __builtin_bit_cast(bf16x8, load16(rq, (uint32_t)(myq * D + 16 * s + 8 * h) * 2));
+    qf[s] = __builtin_bit_cast(bf16x8, load16(rq, (uint32_t)(myq * ldq + 16 * s + 8 * h) * 2));
 
   const int kend = CAUSAL ? min(L, qb * kBM + kBM) : L;
   const int ntiles = (kend + kBN - 1) / kBN;
@@ -104,7 +113,7 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
       const int P = (j * kQWaves + wave) * 64 + lane;
       const int row = P / CPR, pc = P % CPR;
       const int lc = pc ^ (row & SWZ);
-      const uint32_t voff = (uint32_t)((t * kBN + row) * D + lc * 8) * 2;
+      const uint32_t voff = (uint32_t)((t * kBN + row) * ldk + lc * 8) * 2;
       load16_to_lds(rk, &kbuf[buf][(j * kQWaves + wave) * 64 * 16], voff);
     }
   };
@@ -116,7 +125,7 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
     if (vblk) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        vr[kk] = load16(rv, (uint32_t)((t * kBN + 4 * vg + kk) * D + 8 * vc8) * 2);
+        vr[kk] = load16(rv, (uint32_t)((t * kBN + 4 * vg + kk) * ldv + 8 * vc8) * 2);
     }
   };
   auto store_vt = [&](int buf, const u32x4 (&vr)[4]) {
@@ -285,10 +294,14 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         o[c][j] = a0 * o[c][j] + a1 * xo[((wave * NCB + c) * 16 + j) * 64 + lane];
+    m = M;
   }
+  // The row's softmax denominator is sum_j 2^(y_j) = 2^m * lsum (y in log2 units).
+  if (lse != nullptr && myq < L && h == 0)
+    lse[(size_t)(hm.bh0 + bh) * L + myq] = (m + log2f(lsum)) * 0.6931471805599453f;
   const float inv = 1.f / lsum;
   if (myq < L) {
-    uint16_t* orow = out + head + (size_t)myq * D;
+    uint16_t* orow = out + (PLAIN ? plain_off + (int64_t)myq * D : hm.o_off(bh) + (int64_t)myq * hm.o.ld);
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
 #pragma unroll
@@ -301,30 +314,38 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   }
 }
 
-template <int D, bool C>
-hipError_t launch_one(const void* q, const void* k, const void* v, void* out, int BH, int L,
-                      float sl2, hipStream_t s) {
+template <int D, bool C, bool PLAIN>
+hipError_t launch_one(const void* q, const void* k, const void* v, void* out, float* lse,
+                      HeadMap hm, int BH, int L, float sl2, hipStream_t s) {
   const int nqb = (L + kBM - 1) / kBM;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * kWaves);
   const uint16_t* qp = (const uint16_t*)q;
   const uint16_t* kp = (const uint16_t*)k;
   const uint16_t* vp = (const uint16_t*)v;
   uint16_t* op = (uint16_t*)out;
-  void* args[] = {&qp, &kp, &vp, &op, &L, (void*)&nqb, &sl2};
-  return hipLaunchKernel((const void*)&online_attn_kernel<D, C>, grid, block, args, 0, s);
+  void* args[] = {&qp, &kp, &vp, &op, &lse, &hm, &L, (void*)&nqb, &sl2};
+  return hipLaunchKernel((const void*)&online_attn_kernel<D, C, PLAIN>, grid, block, args, 0, s);
+}
+
+template <int D, bool C>
+hipError_t launch_d(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const HeadMap& hm, int BH, int L, float sl2, hipStream_t s) {
+  return is_plain(hm, L, D) ? launch_one<D, C, true>(q, k, v, out, lse, hm, BH, L, sl2, s)
+                            : launch_one<D, C, false>(q, k, v, out, lse, hm, BH, L, sl2, s);
 }
 
 }  // namespace
 
-hipError_t launch_online(const void* q, const void* k, const void* v, void* out, int BH, int L,
-                         int d, float sl2, bool causal, hipStream_t s) {
+hipError_t launch_online(const void* q, const void* k, const void* v, void* out, float* lse,
+                         const HeadMap& hm, int BH, int L, int d, float sl2, bool causal,
+                         hipStream_t s) {
   switch (d) {
-    case 32: return causal ? launch_one<32, true>(q, k, v, out, BH, L, sl2, s)
-                           : launch_one<32, false>(q, k, v, out, BH, L, sl2, s);
-    case 64: return causal ? launch_one<64, true>(q, k, v, out, BH, L, sl2, s)
-                           : launch_one<64, false>(q, k, v, out, BH, L, sl2, s);
-    case 128: return causal ? launch_one<128, true>(q, k, v, out, BH, L, sl2, s)
-                            : launch_one<128, false>(q, k, v, out, BH, L, sl2, s);
+    case 32: return causal ? launch_d<32, true>(q, k, v, out, lse, hm, BH, L, sl2, s)
+                           : launch_d<32, false>(q, k, v, out, lse, hm, BH, L, sl2, s);
+    case 64: return causal ? launch_d<64, true>(q, k, v, out, lse, hm, BH, L, sl2, s)
+                           : launch_d<64, false>(q, k, v, out, lse, hm, BH, L, sl2, s);
+    case 128: return causal ? launch_d<128, true>(q, k, v, out, lse, hm, BH, L, sl2, s)
+                            : launch_d<128, false>(q, k, v, out, lse, hm, BH, L, sl2, s);
     default: return hipErrorInvalidValue;
   }
 }

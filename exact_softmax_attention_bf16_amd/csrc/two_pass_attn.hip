@@ -253,8 +253,8 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ], Sco
 // One LDS object (see the GEMM loop's notes on the compiler's LDS-DMA waits).
 __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, uint16_t* __restrict__ E,
-    float* __restrict__ mref, float* __restrict__ psum, int L, int d, int T, int Ls, float sl2,
-    int causal, int ntiles) {
+    float* __restrict__ mref, float* __restrict__ psum, HeadMap hm, int L, int d, int T, int Ls,
+    float sl2, int causal, int ntiles) {
   __shared__ ScoresSmem smem;
   GemmSmem& sm = smem.g;
 
@@ -266,12 +266,12 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
   const int my_tiles = (ntiles - 1 - first) / G + 1;  // first < ntiles
   const int nk = d / kStepK;                          // >= 3 on this path
   const int total = my_tiles * nk;
-  const uint32_t row_bytes = (uint32_t)d * 2u;
+  const int ldk = hm.k.ld, ldq = hm.q.ld;
   constexpr int kLoads = KContiguousT<kScoresWaves>::kLoads;  // per wave and operand
 
   KContiguousT<kScoresWaves> la, lb;  // per-lane offsets within a tile; resources start at its first row
-  la.init(make_rsrc(k, 0), (uint32_t)d, 0, wave, lane);
-  lb.init(make_rsrc(q, 0), (uint32_t)d, 0, wave, lane);
+  la.init(make_rsrc(k, 0), (uint32_t)ldk, 0, wave, lane);
+  lb.init(make_rsrc(q, 0), (uint32_t)ldq, 0, wave, lane);
 
   // Load cursor: the step (tile li, K step lk) whose loads go out next.
   int li = 0, lk = 0;
@@ -279,8 +279,9 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
   auto set_load_tile = [&](int i) {
     const ScoresTile t = scores_tile(first + i * G, T, causal);
     const int k0 = t.kt * kTile, q0 = t.qt * kTile;
-    rk = make_rsrc(k + ((size_t)t.bh * L + k0) * d, (uint32_t)(L - k0) * row_bytes);
-    rq = make_rsrc(q + ((size_t)t.bh * L + q0) * d, (uint32_t)(L - q0) * row_bytes);
+    // Each resource ends after the head's row L - 1: rows past L read as zero.
+    rk = make_rsrc(k + hm.k_off(t.bh) + (size_t)k0 * ldk, ((uint32_t)(L - 1 - k0) * ldk + d) * 2u);
+    rq = make_rsrc(q + hm.q_off(t.bh) + (size_t)q0 * ldq, ((uint32_t)(L - 1 - q0) * ldq + d) * 2u);
   };
   auto advance = [&]() {
     if (++lk == nk) {
@@ -432,9 +433,10 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
                                                      const float* __restrict__ mref,
                                                      const float* __restrict__ psum,
                                                      uint16_t* __restrict__ out,
-                                                     float* __restrict__ part, int L, int d,
-                                                     int T, int Ls, int Lk, int causal, int ncb,
-                                                     int split, int nheads) {
+                                                     float* __restrict__ lse,
+                                                     float* __restrict__ part, HeadMap hm, int L,
+                                                     int d, int T, int Ls, int Lk, int causal,
+                                                     int ncb, int split, int nheads) {
   __shared__ ValuesSmem smem;
   GemmSmem& sm = smem.g;
   uint8_t(&shift_tab)[kMaxTiles][kTile] = smem.shift_tab;
@@ -493,6 +495,10 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
         if (t0 + u < tiles) shift_tab[t0 + u][tid] = (uint8_t)fminf(M - mt[u], 255.f);
     }
     inv_l[tid] = 1.f / l;
+    // The row's softmax denominator is sum_j 2^(y_j) = 2^M l (y in log2 units).
+    const int query = qt * kTile + tid;
+    if (lse != nullptr && ct == 0 && sp == 0 && query < L)
+      lse[(size_t)(hm.bh0 + bh) * L + query] = (M + log2f(l)) * 0.6931471805599453f;
   }
   __syncthreads();
 
@@ -505,10 +511,14 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
     invl[j] = inv_l[sh.col[j]];
   }
 
-  const auto ra = make_rsrc(v + (size_t)bh * L * d, (uint32_t)L * d * 2);
+  // V's resource ends after the head's row L - 1 (keys past L read as zero).
+  // Channels past d of a 256-channel tile read whatever lies there (zero past
+  // the end) and only feed accumulator rows that are never stored.
+  const int ldv = hm.v.ld;
+  const auto ra = make_rsrc(v + hm.v_off(bh), ((uint32_t)(L - 1) * ldv + d) * 2u);
   const auto rb = make_rsrc(E + (size_t)bh * L * Ls, (uint32_t)L * Ls * 2);
   f32x16 acc[4][4];
-  gemm_tile<KOuter>(acc, ra, (uint32_t)d, ct * kTile, rb, (uint32_t)Ls, qt * kTile, k_first, nk,
+  gemm_tile<KOuter>(acc, ra, (uint32_t)ldv, ct * kTile, rb, (uint32_t)Ls, qt * kTile, k_first, nk,
                     sm, sh);
 
   if constexpr (SPLIT) {
@@ -561,21 +571,25 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
     const int c = tid & 31;
     const int ch = ct * kTile + 8 * c;
     if (ch < d) {
-      uint16_t* oh = out + (size_t)bh * L * d + (size_t)(qt * kTile) * d + ch;
+      const int ldo = hm.o.ld;
+      uint16_t* oh = out + hm.o_off(bh) + (size_t)(qt * kTile) * ldo + ch;
 #pragma unroll 8
       for (int j = 0; j < 32; ++j) {
         const int r = (tid >> 5) + 8 * j;
         if (qt * kTile + r < L)
-          *(u32x4*)(oh + (size_t)r * d) = unswap_halves(*(const u32x4*)(stage + r * 512 + ((c ^ (r & 31)) << 4)), r);
+          *(u32x4*)(oh + (size_t)r * ldo) = unswap_halves(*(const u32x4*)(stage + r * 512 + ((c ^ (r & 31)) << 4)), r);
       }
     }
   }
 }
 
-// out = bf16(sum over the splits of part), 8 elements per thread.
+// out = bf16(sum over the splits of part), 8 elements per thread.  part is
+// [split][head][L][d] contiguous; out is addressed through the head map.
 __global__ __launch_bounds__(256) void values_reduce_kernel(const float* __restrict__ part,
-                                                            uint16_t* __restrict__ out,
-                                                            int64_t n8, int64_t stride, int split) {
+                                                            uint16_t* __restrict__ out, HeadMap hm,
+                                                            int L, int d, int64_t n8,
+                                                            int64_t stride, int split) {
+  const int c8n = d / 8;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
     const f32x4* p = (const f32x4*)part + 2 * i;
     f32x4 lo = p[0], hi = p[1];
@@ -585,7 +599,10 @@ __global__ __launch_bounds__(256) void values_reduce_kernel(const float* __restr
     }
     const u32x4 w = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
                      pack_bf16x2(hi[2], hi[3])};
-    *((u32x4*)out + i) = w;
+    const int64_t row_all = i / c8n;  // head * L + row
+    const int c8 = (int)(i - row_all * c8n);
+    const int bh = (int)(row_all / L), row = (int)(row_all - (int64_t)bh * L);
+    *(u32x4*)(out + hm.o_off(bh) + (size_t)row * hm.o.ld + 8 * c8) = w;
   }
 }
 
@@ -607,15 +624,17 @@ static int device_cu_count() {
   return n;
 }
 
-hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, float* psum, int BH,
-                         const TwoPassDims& t, float sl2, bool causal, hipStream_t s) {
+hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, float* psum,
+                         const HeadMap& hm, int BH, const TwoPassDims& t, float sl2, bool causal,
+                         hipStream_t s) {
   const uint16_t* qp = (const uint16_t*)q;
   const uint16_t* kp = (const uint16_t*)k;
   uint16_t* ep = (uint16_t*)E;
   int L = t.L, d = t.d, T = t.T, Ls = t.Ls, c = causal ? 1 : 0;
   int ntiles = BH * (causal ? T * (T + 1) / 2 : T * T);
   const int grid = std::min(ntiles, device_cu_count());  // one workgroup per CU (LDS-bound)
-  void* args[] = {&qp, &kp, &ep, &mref, &psum, &L, &d, &T, &Ls, &sl2, &c, &ntiles};
+  HeadMap m = hm;
+  void* args[] = {&qp, &kp, &ep, &mref, &psum, &m, &L, &d, &T, &Ls, &sl2, &c, &ntiles};
   return hipLaunchKernel((const void*)&scores_kernel, dim3((unsigned)grid),
                          dim3(64 * kScoresWaves), args, 0, s);
 }
@@ -633,27 +652,30 @@ int values_split(int64_t BH, const TwoPassDims& t, bool causal) {
 }
 
 hipError_t launch_values(const void* v, const void* E, const float* mref, const float* psum,
-                         void* out, float* part, int split, int BH, const TwoPassDims& t,
-                         bool causal, hipStream_t s) {
+                         void* out, float* lse, float* part, int split, const HeadMap& hm, int BH,
+                         const TwoPassDims& t, bool causal, hipStream_t s) {
   const uint16_t* vtp = (const uint16_t*)v;
   const uint16_t* ep = (const uint16_t*)E;
   uint16_t* op = (uint16_t*)out;
   int L = t.L, d = t.d, T = t.T, Ls = t.Ls, Lk = t.Lk, c = causal ? 1 : 0;
   int ncb = (t.d + kTile - 1) / kTile;
   int nheads = BH;
-  void* args[] = {&vtp, &ep, &mref, &psum, &op, &part, &L, &d, &T, &Ls, &Lk, &c, &ncb, &split,
-                  &nheads};
+  HeadMap m = hm;
+  void* args[] = {&vtp, &ep, &mref, &psum, &op, &lse, &part, &m, &L, &d, &T, &Ls, &Lk, &c, &ncb,
+                  &split, &nheads};
   const void* kern = split > 1 ? (const void*)&values_kernel<true> : (const void*)&values_kernel<false>;
   return hipLaunchKernel(kern, dim3((unsigned)(BH * T * ncb * split)), dim3(256), args, 0, s);
 }
 
-hipError_t launch_values_reduce(const float* part, void* out, int split, int BH,
-                                const TwoPassDims& t, hipStream_t s) {
+hipError_t launch_values_reduce(const float* part, void* out, int split, const HeadMap& hm,
+                                int BH, const TwoPassDims& t, hipStream_t s) {
   int64_t stride = (int64_t)BH * t.L * t.d;  // floats per split
   int64_t n8 = stride / 8;                   // d is a multiple of 64
   const int blocks = (int)std::min<int64_t>((n8 + 255) / 256, 2048);
   uint16_t* op = (uint16_t*)out;
-  void* args[] = {&part, &op, &n8, &stride, &split};
+  HeadMap m = hm;
+  int L = t.L, d = t.d;
+  void* args[] = {&part, &op, &m, &L, &d, &n8, &stride, &split};
   return hipLaunchKernel((const void*)&values_reduce_kernel, dim3((unsigned)blocks), dim3(256),
                          args, 0, s);
 }

@@ -49,7 +49,9 @@ enum {
   ATTN_ERR_ALIAS = 6,                /* out overlaps q, k or v                    */
   ATTN_ERR_WORKSPACE = 7,            /* the stream-ordered workspace allocation failed */
   ATTN_ERR_HIP = 8,                  /* a HIP launch or runtime call failed       */
-  ATTN_ERR_TOO_LARGE = 9             /* one head exceeds the kernels' 32-bit byte offsets */
+  ATTN_ERR_TOO_LARGE = 9,            /* one head exceeds the kernels' 32-bit byte offsets */
+  ATTN_ERR_BAD_STRIDE = 10           /* attn_forward_ex: a stride is negative or not a multiple
+                                        of 8, a row stride is below d, or out's elements overlap */
 };
 
 /* Kernel paths chosen by head dimension. */
@@ -82,6 +84,49 @@ enum {
 int attn_forward(const void* q, const void* k, const void* v, void* out,
                  int64_t B, int64_t H, int64_t L, int64_t d,
                  float scale, int causal, hipStream_t stream);
+
+/*
+ * attn_forward_ex -- the same operation on strided operands, with key/value
+ * heads shared by groups of query heads and an optional log-sum-exp output.
+ *
+ * What it adds, and where it comes from: FastVideo wan22_vae_decode attn.cu,
+ * attn_forward, takes one packed [T, 1, HW, 3C] qkv tensor (frames T,
+ * positions HW, channels C) and reads q and k in place with a position stride
+ * of 3C; q, k and v are the channel ranges [0, C), [C, 2C), [2C, 3C).  Here:
+ * q = qkv, k = qkv + C, v = qkv + 2C (element offsets), B = T, H = H_kv = 1,
+ * L = HW, d = C and strides {HW*3C, HW*3C, 3C} for all three; nothing is
+ * copied.  cuDNN native_sparse_attention fmha.py, __call__, takes per-tensor
+ * strides, lets the query heads be a multiple of the key/value heads (each
+ * key/value head broadcast over its group of consecutive query heads) and
+ * optionally writes each row's log-sum-exp (log of the row sum plus the
+ * scaled row maximum, stored in its epilogue).
+ *
+ *   q, out        : [B, H, L, d] views; k, v : [B, H_kv, L, d] views.  Each is a
+ *                   device pointer to its element [0,0,0,0] plus three element
+ *                   strides (batch, head, row) in a host array of 3 int64_t;
+ *                   NULL means contiguous ({heads*L*d, L*d, d}).  Channels are
+ *                   always contiguous.  Strides must be >= 0 and multiples of 8
+ *                   (16-byte rows), row strides >= d; zero batch or head
+ *                   strides broadcast an input.  out's strides must map every
+ *                   element to its own address.  Pointers 16-byte aligned.
+ *   lse           : NULL, or a device pointer to fp32 [B, H, L] contiguous
+ *                   (4-byte aligned) that receives, per query row i, the
+ *                   natural log of its softmax denominator:
+ *                   lse[i] = log(sum over allowed j of exp(scale * q_i . k_j)).
+ *   H_kv          : key/value heads, >= 1 and dividing H; query head h reads
+ *                   key/value head h / (H / H_kv) of the same batch entry.
+ *   B, H, L, d, scale, causal, stream : as for attn_forward.
+ *
+ * out must not overlap q, k, v (compared as the address ranges each view
+ * spans), nor lse any of them; q, k and v may overlap each other (they are
+ * only read).  Returns ATTN_OK or a status code; strides are checked before
+ * any HIP call like everything else.  Workspace as for attn_forward.
+ */
+int attn_forward_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                    int64_t B, int64_t H, int64_t H_kv, int64_t L, int64_t d,
+                    const int64_t* q_strides, const int64_t* k_strides,
+                    const int64_t* v_strides, const int64_t* o_strides,
+                    float scale, int causal, hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 const char* attn_status_string(int status);

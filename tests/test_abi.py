@@ -33,8 +33,9 @@ def fwd(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, B=1, H=1, L=16, d=
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == sorted(["attn_forward", "attn_status_string", "attn_path_for_head_dim",
-                            "attn_workspace_bytes", "attn_timing_enable", "attn_timing_collect"])
+    assert names == sorted(["attn_forward", "attn_forward_ex", "attn_status_string",
+                            "attn_path_for_head_dim", "attn_workspace_bytes",
+                            "attn_timing_enable", "attn_timing_collect"])
     assert set(names) == set(_lib.SIGNATURES)
 
 
@@ -48,7 +49,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(10):
+    for code in range(11):
         s = eab.status_string(code)
         assert s and s != "unknown status"
     assert eab.status_string(99) == "unknown status"
@@ -195,3 +196,110 @@ def test_python_binding_rejects_bad_tensors():
         attention(x, x, x)
     with pytest.raises(TypeError):
         attention(x.float(), x, x)
+
+
+# ---- attn_forward_ex: strides, grouped heads, log-sum-exp --------------------
+
+def st(*x):
+    return (ctypes.c_int64 * 3)(*x)
+
+
+def fwd_ex(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, lse=None, B=1, H=1, H_kv=1,
+           L=16, d=64, qs=None, ks=None, vs=None, os_=None, scale=0.125, causal=0):
+    return _lib.load().attn_forward_ex(q, k, v, out, lse, B, H, H_kv, L, d, qs, ks, vs, os_,
+                                       scale, causal, None)
+
+
+# A valid call would launch; these shapes pass every earlier check and are then
+# refused as too large for the kernels' 32-bit offsets (q's row stride), which
+# shows the layout itself was accepted.
+BIG_L = 1 << 23
+
+
+def test_ex_empty_and_shared_checks():
+    assert fwd_ex(B=0) == _lib.ATTN_OK
+    assert fwd_ex(L=0, q=None) == _lib.ATTN_OK
+    assert fwd_ex(q=None) == _lib.ATTN_ERR_NULL_PTR
+    assert fwd_ex(d=96) == _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM
+    assert fwd_ex(scale=float("inf")) == _lib.ATTN_ERR_BAD_SCALE
+    assert fwd_ex(out=A + 8) == _lib.ATTN_ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 0), (4, 3), (2, 4), (4, -1)])
+def test_ex_key_value_heads_must_divide(H, H_kv):
+    assert fwd_ex(H=H, H_kv=H_kv) == _lib.ATTN_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("which", ["qs", "ks", "vs", "os_"])
+@pytest.mark.parametrize("bad", [(4096, 1024, 60), (4096, 1028, 64), (-1024, 1024, 64),
+                                 (1024, 1024, 32)])
+def test_ex_bad_strides(which, bad):
+    # a stride not a multiple of 8, a negative one, a row stride below d
+    assert fwd_ex(**{which: st(*bad)}, d=64) == _lib.ATTN_ERR_BAD_STRIDE
+
+
+def test_ex_out_elements_must_not_overlap():
+    # two heads of out at the same address
+    assert fwd_ex(H=2, H_kv=2, os_=st(2048, 0, 64)) == _lib.ATTN_ERR_BAD_STRIDE
+    # rows 32 elements apart with d = 64
+    assert fwd_ex(os_=st(4096, 4096, 32)) == _lib.ATTN_ERR_BAD_STRIDE
+
+
+def test_ex_permuted_and_packed_layouts_are_accepted():
+    L, d, H = BIG_L, 64, 2
+    n = L * H * d * 2
+    # out as [B, L, H, d] memory: head stride d, row stride H * d
+    assert fwd_ex(q=A, k=A + n, v=A + 2 * n, out=A + 3 * n, B=1, H=H, H_kv=H, L=L, d=d,
+                  qs=st(L * H * d, d, H * d), ks=st(L * H * d, d, H * d),
+                  vs=st(L * H * d, d, H * d), os_=st(L * H * d, d, H * d)) == _lib.ATTN_ERR_TOO_LARGE
+    # packed [T, 1, HW, 3C]: q, k, v overlap each other (they are only read)
+    C = 64
+    row = 3 * C
+    span = 2 * BIG_L * row * 2
+    ps = st(BIG_L * row, BIG_L * row, row)
+    assert fwd_ex(q=A, k=A + 2 * C, v=A + 4 * C, out=A + span, B=2, H=1, H_kv=1, L=BIG_L, d=C,
+                  qs=ps, ks=ps, vs=ps) == _lib.ATTN_ERR_TOO_LARGE
+
+
+def test_ex_zero_strides_broadcast_inputs():
+    # one key/value head broadcast over all batches and heads (strides 0)
+    L, d = BIG_L, 64
+    assert fwd_ex(q=A, k=A + (1 << 34), v=A + (1 << 35), out=A + (1 << 36), B=2, H=4, H_kv=4,
+                  L=L, d=d, qs=st(4 * L * 2 * d, L * 2 * d, 2 * d), ks=st(0, 0, d),
+                  vs=st(0, 0, d)) == _lib.ATTN_ERR_TOO_LARGE
+
+
+def test_ex_out_must_not_overlap_a_strided_input():
+    # out starts inside the span of a packed q (row stride 3d)
+    L, d = 100, 64
+    ps = st(L * 3 * d, L * 3 * d, 3 * d)
+    assert fwd_ex(q=A, k=A + 2 * d, v=A + 4 * d, out=A + 2 * (L - 1) * 3 * d, L=L, d=d,
+                  qs=ps, ks=ps, vs=ps) == _lib.ATTN_ERR_ALIAS
+
+
+def test_ex_lse_checks():
+    assert fwd_ex(lse=A + 256 * MB + 2) == _lib.ATTN_ERR_MISALIGNED
+    assert fwd_ex(lse=A + 192 * MB + 64) == _lib.ATTN_ERR_ALIAS   # inside out
+    assert fwd_ex(lse=A + 16) == _lib.ATTN_ERR_ALIAS              # inside q
+    L = BIG_L
+    n = L * 64 * 2
+    assert fwd_ex(q=A, k=A + n, v=A + 2 * n, out=A + 3 * n, lse=A + 4 * n, L=L,
+                  qs=st(L * 128, L * 128, 128)) == _lib.ATTN_ERR_TOO_LARGE
+
+
+def test_ex_defaults_match_attn_forward_checks():
+    # NULL strides and H_kv == H: the same verdicts as attn_forward
+    for kw in [dict(B=-1), dict(d=48), dict(scale=float("nan")), dict(q=None), dict(out=A + 8)]:
+        assert fwd_ex(**kw) == fwd(**kw)
+    nbytes = 2 * 3 * 500 * 64 * 2
+    assert fwd_ex(out=A + nbytes - 16, B=2, H=3, H_kv=3, L=500) == _lib.ATTN_ERR_ALIAS
+
+
+def test_python_binding_rejects_bad_layouts():
+    import torch
+    from exact_softmax_attention_bf16_amd import attention, attention_packed_qkv
+    x = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):   # CPU tensors never reach the library
+        attention(x, x[:, :1], x[:, :1])
+    with pytest.raises(ValueError):
+        attention_packed_qkv(torch.zeros(1, 1, 4, 100, dtype=torch.bfloat16))

@@ -1,0 +1,194 @@
+"""GPU parity for attn_forward_ex: packed and permuted layouts read in place,
+grouped key/value heads, and the log-sum-exp output, against the float64 oracle.
+
+Output bar as in test_parity_gpu.py.  LSE bar, from the arithmetic: the kernels
+sum the bf16-rounded exponentials they multiply (bf16 keeps 8 significant
+bits, so round-to-nearest errs by at most 2^-8 relative per term, hence in the
+sum), so the denominator's log is off by at most ln(1 + 2^-8) < 3.90e-3, plus
+fp32 rounding of the logits and of the final scaling (well under 1e-5 relative
+at these sizes): |lse - ref| <= 4e-3 + 1e-5 |ref|.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import make_qkv
+from synth.metrics import within_bar
+
+from gpu_util import to_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+LSE_ATOL, LSE_RTOL = 4e-3, 1e-5
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+
+
+def _report(name, a, r):
+    print(f"[layouts] {name}: max_abs={a:.3e} rel_rms={r:.3e}", flush=True)
+
+
+def lse_ok(got, ref):
+    err = np.abs(to_f64(got) - ref)
+    return bool(np.all(err <= LSE_ATOL + LSE_RTOL * np.abs(ref))), float(err.max())
+
+
+def packed(T, HW, C, seed):
+    q, k, v = make_qkv(T, 1, HW, C, seed)
+    return torch.cat([q, k, v], dim=-1).contiguous(), (q, k, v)
+
+
+@pytest.mark.parametrize("C", [64, 128, 256, 1024])
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_qkv_in_place(C, causal):
+    from exact_softmax_attention_bf16_amd import attention_packed_qkv
+    T, HW = 2, 300
+    qkv, (q, k, v) = packed(T, HW, C, 100 + C)
+    qkv_d = qkv.to(DEV)
+    o = attention_packed_qkv(qkv_d, scale=1.0 / math.sqrt(C), causal=causal)
+    torch.cuda.synchronize()
+    assert o.shape == (T, 1, HW, C)
+    assert torch.equal(qkv_d.cpu(), qkv)  # read only
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1.0 / math.sqrt(C), causal)
+    ok, a, r = within_bar(to_f64(o), ref)
+    _report(f"packed qkv C={C} causal={causal}", a, r)
+    assert ok, (a, r)
+
+
+def test_packed_qkv_wan_frames_sampled():
+    """The decoder's packed layout at its real size: 4 frames of 44 x 78
+    positions, C = 1024, checked on sampled rows of every frame."""
+    from exact_softmax_attention_bf16_amd import attention_packed_qkv
+    T, HW, C = 4, 3432, 1024
+    qkv, (q, k, v) = packed(T, HW, C, 104)
+    o = attention_packed_qkv(qkv.to(DEV), scale=1.0 / 32, causal=False)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = [(t, 0, int(i)) for t in range(T) for i in list(rng.choice(HW, 6, replace=False)) + [0, HW - 1]]
+    ref = oracle.attention_rows(to_f64(q), to_f64(k), to_f64(v), 1.0 / 32, False, rows)
+    got = np.stack([to_f64(o[t, h, i]) for t, h, i in rows])
+    ok, a, r = within_bar(got, ref)
+    _report("packed qkv 4 x 3432 x 1024 (sampled rows)", a, r)
+    assert ok, (a, r)
+
+
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_permuted_layouts(d, causal):
+    """q, k, v and out stored as [B, L, H, d] (heads interleaved in each row)."""
+    from exact_softmax_attention_bf16_amd import attention
+    B, H, L = 2, 3, 261
+    q, k, v = make_qkv(B, H, L, d, 110 + d)
+    perm = [t.transpose(1, 2).contiguous().to(DEV).transpose(1, 2) for t in (q, k, v)]
+    out = torch.empty(B, L, H, d, dtype=torch.bfloat16, device=DEV).transpose(1, 2)
+    o = attention(*perm, scale=1.0 / math.sqrt(d), causal=causal, out=out)
+    torch.cuda.synchronize()
+    assert o.data_ptr() == out.data_ptr()
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1.0 / math.sqrt(d), causal)
+    ok, a, r = within_bar(to_f64(o), ref)
+    _report(f"permuted d={d} causal={causal}", a, r)
+    assert ok, (a, r)
+
+
+@pytest.mark.parametrize("H,H_kv", [(8, 2), (8, 1), (6, 3), (4, 4)])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_key_value_heads(H, H_kv, d, causal):
+    from exact_softmax_attention_bf16_amd import attention
+    B, L = 2, 257
+    q = make_qkv(B, H, L, d, 120 + H)[0]
+    _, k, v = make_qkv(B, H_kv, L, d, 121 + H_kv)
+    o = attention(q.to(DEV), k.to(DEV), v.to(DEV), scale=1.0 / math.sqrt(d), causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1.0 / math.sqrt(d), causal)
+    ok, a, r = within_bar(to_f64(o), ref)
+    _report(f"H={H} H_kv={H_kv} d={d} causal={causal}", a, r)
+    assert ok, (a, r)
+
+
+def test_zero_stride_broadcast_equals_multi_query():
+    """One key/value head given as a head-stride-0 view equals H_kv = 1."""
+    from exact_softmax_attention_bf16_amd import attention
+    B, H, L, d = 2, 4, 300, 64
+    q = make_qkv(B, H, L, d, 130)[0].to(DEV)
+    _, k, v = (t.to(DEV) for t in make_qkv(B, 1, L, d, 131))
+    o1 = attention(q, k, v)
+    o2 = attention(q, k.expand(B, H, L, d), v.expand(B, H, L, d))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128, 256, 1024])
+@pytest.mark.parametrize("L", [1, 130, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse(d, L, causal):
+    from exact_softmax_attention_bf16_amd import attention
+    B, H = 2, 2
+    q, k, v = make_qkv(B, H, L, d, 140 + L + d)
+    s = 1.0 / math.sqrt(d)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, lse = attention(qd, kd, vd, scale=s, causal=causal, return_lse=True)
+    o_plain = attention(qd, kd, vd, scale=s, causal=causal)
+    torch.cuda.synchronize()
+    assert lse.shape == (B, H, L) and lse.dtype == torch.float32
+    assert torch.equal(o, o_plain)  # the same kernels; lse is an extra store
+    ok, err = lse_ok(lse, oracle.log_sum_exp(to_f64(q), to_f64(k), s, causal))
+    print(f"[layouts] lse d={d} L={L} causal={causal}: max err {err:.3e}", flush=True)
+    assert ok, err
+
+
+def test_lse_scale_zero_is_log_count():
+    from exact_softmax_attention_bf16_amd import attention
+    L = 500
+    q, k, v = (t.to(DEV) for t in make_qkv(1, 1, L, 256, 150))
+    _, lse = attention(q, k, v, scale=0.0, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    ok, err = lse_ok(lse[0, 0], np.log(np.arange(1, L + 1)))
+    assert ok, err
+
+
+@pytest.mark.parametrize("L,d", [(1100, 256), (2100, 512)])
+def test_key_split_with_strided_out_and_lse(L, d):
+    """One head: the values pass splits its keys; the reduction writes a strided
+    out (row stride 2d) and the first split writes the LSE."""
+    from exact_softmax_attention_bf16_amd import attention, kernel_timing
+    q, k, v = make_qkv(1, 1, L, d, 160 + L)
+    s = 1.0 / math.sqrt(d)
+    big = torch.full((1, 1, L, 2 * d), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = big[..., :d]
+    res = {}
+    with kernel_timing(res):
+        o, lse = attention(q.to(DEV), k.to(DEV), v.to(DEV), scale=s, out=out, return_lse=True)
+    torch.cuda.synchronize()
+    assert "values_reduce" in res
+    assert bool((big[..., d:] == 7.0).all())  # the gaps between rows are untouched
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), s, False)
+    ok, a, r = within_bar(to_f64(o), ref)
+    _report(f"split + strided out L={L} d={d}", a, r)
+    assert ok, (a, r)
+    ok, err = lse_ok(lse, oracle.log_sum_exp(to_f64(q), to_f64(k), s, False))
+    assert ok, err
+
+
+def test_ex_with_default_strides_equals_attn_forward():
+    """attn_forward_ex with NULL strides and H_kv = H is attn_forward."""
+    import ctypes
+    from exact_softmax_attention_bf16_amd import _lib, attention
+    for d in (64, 1024):
+        q, k, v = (t.to(DEV) for t in make_qkv(2, 2, 700, d, 170 + d))
+        ref = attention(q, k, v)
+        out = torch.empty_like(q)
+        st = _lib.load().attn_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         None, 2, 2, 2, 700, d, None, None, None, None,
+                                         1.0 / math.sqrt(d), 0,
+                                         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        torch.cuda.synchronize()
+        assert st == _lib.ATTN_OK
+        assert torch.equal(out, ref)

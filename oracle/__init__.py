@@ -14,6 +14,7 @@ from .exact import (
     row_log_sum_exp,
     softmax_rows,
     weighted_values,
+    window_mask,
 )
 
 __all__ = [
@@ -26,4 +27,5 @@ __all__ = [
     "row_log_sum_exp",
     "softmax_rows",
     "weighted_values",
+    "window_mask",
 ]

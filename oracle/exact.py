@@ -19,6 +19,10 @@ What it computes, and where the pages define it:
     a group of consecutive query heads (a zero stride over the group index
     broadcasts it); and the optional LSE output per query row, the log of the
     row sum plus the scaled row maximum, i.e. log(sum_j exp(z_ij)).
+  * same page, __call__ parameters window_size_left / window_size_right: a
+    sliding-window mask.  Its body is not on the page; the reading taken is
+    key j allowed for query i iff i - left <= j <= i + right (None: that side
+    unbounded), applied on top of the causal mask.
 
 The method reaches exactly the plain definition (up to rounding order), so this
 oracle is that definition written out, one step per function, in the pages'
@@ -35,11 +39,13 @@ Readings where the pages leave a step open (each listed in the design notes):
   * a row with every key masked cannot occur (the diagonal is always allowed);
     the oracle asserts it rather than inventing an output.
 
-Pins (tests/test_oracle.py): brute-force loops with math.fsum on tiny inputs,
+Pins (tests/test_oracle.py): brute-force loops with math.fsum on tiny inputs
+(with and without windows),
 closed forms (constant V, equal keys, causal row 0, scale 0, L = 1, a one-hot
 limit with huge logits, a hand-worked example in tests/golden, log L and
 log(i + 1) for the LSE of equal keys, one constant value per key/value head
-for the head groups), invariants (rows of P sum to 1, key-shift invariance,
+for the head groups, O = V for a window of width zero, window means of V for
+equal keys), invariants (rows of P sum to 1, key-shift invariance,
 permutation equivariance, linearity in V, the LSE's exact shift when every
 key moves by the same vector) and a cross-check against torch's CPU float64
 attention.  No function here is unpinned.
@@ -59,6 +65,20 @@ def causal_mask(Z: np.ndarray, query_index: np.ndarray) -> np.ndarray:
     Z = Z.copy()
     keys = np.arange(Z.shape[1])
     Z[keys[None, :] > np.asarray(query_index)[:, None]] = -np.inf
+    return Z
+
+
+def window_mask(Z: np.ndarray, query_index: np.ndarray, left, right) -> np.ndarray:
+    """Set Z[r, j] = -inf where key j lies more than `left` keys before or more
+    than `right` keys after the query at position query_index[r] (None: no
+    limit on that side)."""
+    Z = Z.copy()
+    keys = np.arange(Z.shape[1])[None, :]
+    qi = np.asarray(query_index)[:, None]
+    if left is not None:
+        Z[keys < qi - left] = -np.inf
+    if right is not None:
+        Z[keys > qi + right] = -np.inf
     return Z
 
 
@@ -100,50 +120,58 @@ def _dims(q, k, v):
     return sq[0], sq[1], sq[2], sq[1] // sk[1]
 
 
-def probabilities(q, k, scale: float, causal: bool = False) -> np.ndarray:
-    """P = softmax(s * Q K^T) (masked when causal), shape [B, H, L, L]."""
+def _masked_logits(Q, K, scale, causal, window, query_index):
+    """Logits of the rows at query_index with the causal and window masks."""
+    Z = logits(Q, K, scale)
+    if causal:
+        Z = causal_mask(Z, query_index)
+    if window is not None:
+        Z = window_mask(Z, query_index, window[0], window[1])
+    return Z
+
+
+def probabilities(q, k, scale: float, causal: bool = False, window=None) -> np.ndarray:
+    """P = softmax(s * Q K^T) (masked when causal / windowed), shape [B, H, L, L]."""
     B, H, L, g = _dims(q, k, k)
     P = np.empty((B, H, L, L), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            Z = logits(_head(q, b, h), _head(k, b, h // g), scale)
-            if causal:
-                Z = causal_mask(Z, np.arange(L))
+            Z = _masked_logits(_head(q, b, h), _head(k, b, h // g), scale, causal, window,
+                               np.arange(L))
             P[b, h] = softmax_rows(Z)
     return P
 
 
-def attention(q, k, v, scale: float, causal: bool = False) -> np.ndarray:
+def attention(q, k, v, scale: float, causal: bool = False, window=None) -> np.ndarray:
     """O = softmax(s * Q K^T) V for every (batch, head); float64 [B, H, L, dv].
 
     k and v may have fewer heads than q (H_kv dividing H): query head h then
-    reads key/value head h // (H / H_kv)."""
+    reads key/value head h // (H / H_kv).  window = (left, right) restricts
+    query i to keys i - left .. i + right (None on a side: unbounded)."""
     B, H, L, g = _dims(q, k, v)
     O = np.empty((B, H, L, np.shape(v)[-1]), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            Z = logits(_head(q, b, h), _head(k, b, h // g), scale)
-            if causal:
-                Z = causal_mask(Z, np.arange(L))
+            Z = _masked_logits(_head(q, b, h), _head(k, b, h // g), scale, causal, window,
+                               np.arange(L))
             O[b, h] = weighted_values(softmax_rows(Z), _head(v, b, h // g))
     return O
 
 
-def log_sum_exp(q, k, scale: float, causal: bool = False) -> np.ndarray:
+def log_sum_exp(q, k, scale: float, causal: bool = False, window=None) -> np.ndarray:
     """lse[b, h, i] = log(sum over allowed keys j of exp(s * q_i . k_j)); float64
-    [B, H, L].  Key heads are grouped as in attention()."""
+    [B, H, L].  Key heads and the window as in attention()."""
     B, H, L, g = _dims(q, k, k)
     out = np.empty((B, H, L), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            Z = logits(_head(q, b, h), _head(k, b, h // g), scale)
-            if causal:
-                Z = causal_mask(Z, np.arange(L))
+            Z = _masked_logits(_head(q, b, h), _head(k, b, h // g), scale, causal, window,
+                               np.arange(L))
             out[b, h] = row_log_sum_exp(Z)
     return out
 
 
-def attention_rows(q, k, v, scale: float, causal: bool, rows) -> np.ndarray:
+def attention_rows(q, k, v, scale: float, causal: bool, rows, window=None) -> np.ndarray:
     """The same definition evaluated only at the output rows listed in ``rows``.
 
     ``rows`` is a sequence of (b, h, i); returns float64 [len(rows), d].  Used to
@@ -157,8 +185,7 @@ def attention_rows(q, k, v, scale: float, causal: bool, rows) -> np.ndarray:
             cache.clear()  # one head's K and V in float64 at a time
             cache[(b, h // g)] = (_head(k, b, h // g), _head(v, b, h // g))
         K, V = cache[(b, h // g)]
-        Z = logits(np.asarray(q[b, h, i : i + 1], dtype=np.float64), K, scale)
-        if causal:
-            Z = causal_mask(Z, np.array([i]))
+        Z = _masked_logits(np.asarray(q[b, h, i : i + 1], dtype=np.float64), K, scale, causal,
+                           window, np.array([i]))
         out[r] = weighted_values(softmax_rows(Z), V)[0]
     return out

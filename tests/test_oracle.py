@@ -417,3 +417,132 @@ def test_lse_pins_pass_unmutated():
 def test_lse_pins_catch_planted_mistake(name, monkeypatch):
     monkeypatch.setattr(oa, "row_log_sum_exp", LSE_MUTANTS[name])
     assert not _lse_pins_pass(), f"pins did not catch mutant {name}"
+
+
+# ---- sliding windows -----------------------------------------------------------
+
+def allowed_keys(i, L, causal, window):
+    lo, hi = 0, L - 1
+    if window is not None:
+        if window[0] is not None:
+            lo = max(lo, i - window[0])
+        if window[1] is not None:
+            hi = min(hi, i + window[1])
+    if causal:
+        hi = min(hi, i)
+    return range(lo, hi + 1)
+
+
+def brute_force_window(q, k, v, scale, causal, window):
+    """softmax over the allowed keys only (scalar loops, math.fsum)."""
+    B, H, L, d = q.shape
+    out = np.zeros((B, H, L, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            for i in range(L):
+                keys = allowed_keys(i, L, causal, window)
+                z = [scale * math.fsum(q[b, h, i, c] * k[b, h, j, c] for c in range(d)) for j in keys]
+                m = max(z)
+                e = [math.exp(x - m) for x in z]
+                tot = math.fsum(e)
+                for c in range(v.shape[-1]):
+                    out[b, h, i, c] = math.fsum(e[t] * v[b, h, j, c] for t, j in enumerate(keys)) / tot
+    return out
+
+
+WINDOWS = [(0, 0), (1, 0), (0, 2), (2, 3), (None, 1), (3, None), (None, None), (20, 20)]
+
+
+@pytest.mark.parametrize("window", WINDOWS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_brute_force(window, causal):
+    B, H, L, d = 1, 2, 9, 4
+    q, k, v = rnd((B, H, L, d), 90), rnd((B, H, L, d), 91), rnd((B, H, L, d), 92)
+    assert close(oracle.attention(q, k, v, 0.6, causal, window),
+                 brute_force_window(q, k, v, 0.6, causal, window))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_of_width_zero_returns_v(causal):
+    # each query sees only its own key: the softmax of one logit is 1
+    q, k, v = rnd((2, 2, 13, 5), 93), rnd((2, 2, 13, 5), 94), rnd((2, 2, 13, 5), 95)
+    assert np.array_equal(oracle.attention(q, k, v, 0.7, causal, (0, 0)), v)
+
+
+def test_window_limits_reduce_to_causal_and_full():
+    L = 12
+    q, k, v = rnd((1, 2, L, 4), 96), rnd((1, 2, L, 4), 97), rnd((1, 2, L, 4), 98)
+    assert close(oracle.attention(q, k, v, 0.5, False, (None, 0)), oracle.attention(q, k, v, 0.5, True))
+    assert close(oracle.attention(q, k, v, 0.5, False, (L, L)), oracle.attention(q, k, v, 0.5, False))
+    assert close(oracle.attention(q, k, v, 0.5, True, (L, 5)), oracle.attention(q, k, v, 0.5, True))
+
+
+@pytest.mark.parametrize("window", [(2, 1), (0, 3), (4, 0), (None, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_equal_keys_give_window_means(window, causal):
+    L, d = 11, 3
+    q, v = rnd((1, 1, L, d), 99), rnd((1, 1, L, d), 100)
+    k = np.broadcast_to(rnd((d,), 101), (1, 1, L, d)).copy()
+    want = np.stack([v[0, 0, list(allowed_keys(i, L, causal, window))].mean(axis=0) for i in range(L)])
+    assert close(oracle.attention(q, k, v, 0.9, causal, window)[0, 0], want)
+
+
+@pytest.mark.parametrize("window", [(2, 1), (0, 0), (None, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_lse_scale_zero_is_log_count(window, causal):
+    L = 10
+    q, k = rnd((1, 1, L, 3), 102), rnd((1, 1, L, 3), 103)
+    want = np.log([len(allowed_keys(i, L, causal, window)) for i in range(L)])
+    assert close(oracle.log_sum_exp(q, k, 0.0, causal, window)[0, 0], want)
+
+
+def test_window_rows_match_full():
+    L = 14
+    q, k, v = rnd((1, 2, L, 4), 104), rnd((1, 2, L, 4), 105), rnd((1, 2, L, 4), 106)
+    rows = [(0, h, i) for h in range(2) for i in (0, 5, L - 1)]
+    full = oracle.attention(q, k, v, 0.4, True, (3, 2))
+    assert close(oracle.attention_rows(q, k, v, 0.4, True, rows, (3, 2)),
+                 np.stack([full[b, h, i] for b, h, i in rows]))
+
+
+def _window_pins_pass():
+    try:
+        q, k, v = rnd((1, 1, 9, 4), 110), rnd((1, 1, 9, 4), 111), rnd((1, 1, 9, 4), 112)
+        for window in [(2, 3), (1, 0), (0, 2)]:
+            if not close(oracle.attention(q, k, v, 0.6, False, window),
+                         brute_force_window(q, k, v, 0.6, False, window)):
+                return False
+        if not np.array_equal(oracle.attention(q, k, v, 0.7, False, (0, 0)), v):
+            return False
+        return True
+    except (AssertionError, ValueError, FloatingPointError):
+        return False
+
+
+def _shifted_window(dl, dr, swap=False):
+    def bad(Z, qi, left, right):
+        if swap:
+            left, right = right, left
+        return oa_window_ref(Z, qi, None if left is None else left + dl,
+                             None if right is None else right + dr)
+    return bad
+
+
+oa_window_ref = oa.window_mask
+WINDOW_MUTANTS = {
+    "window_left_one_short": _shifted_window(-1, 0),
+    "window_left_one_long": _shifted_window(1, 0),
+    "window_right_one_short": _shifted_window(0, -1),
+    "window_right_one_long": _shifted_window(0, 1),
+    "window_sides_swapped": _shifted_window(0, 0, swap=True),
+}
+
+
+def test_window_pins_pass_unmutated():
+    assert _window_pins_pass()
+
+
+@pytest.mark.parametrize("name", sorted(WINDOW_MUTANTS))
+def test_window_pins_catch_planted_mistake(name, monkeypatch):
+    monkeypatch.setattr(oa, "window_mask", WINDOW_MUTANTS[name])
+    assert not _window_pins_pass(), f"pins did not catch mutant {name}"

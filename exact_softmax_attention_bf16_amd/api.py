@@ -48,7 +48,8 @@ def _call(fn, q: torch.Tensor, *args) -> None:
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
-              causal: bool = False, out: torch.Tensor | None = None, return_lse: bool = False):
+              causal: bool = False, out: torch.Tensor | None = None, return_lse: bool = False,
+              window: tuple | None = None):
     """O = softmax(scale * Q K^T) V on bf16 tensors (HIP kernels only).
 
     q is [B, H, L, d]; k and v are [B, H_kv, L, d] with H_kv dividing H (query
@@ -58,8 +59,10 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | 
     ``out``, if given, is a bf16 [B, H, L, d] tensor (any strides whose elements
     do not overlap) that overlaps none of the inputs.  With ``return_lse`` the
     result is (out, lse), lse float32 [B, H, L] holding each row's
-    log(sum_j exp(scale * q . k_j)).  Work is queued on the current stream of
-    q's device.
+    log(sum_j exp(scale * q . k_j)).  ``window = (left, right)`` is a sliding
+    window: query i sees only keys i - left .. i + right (None on a side:
+    unbounded); causal also caps right at 0.  Work is queued on the current
+    stream of q's device.
     """
     _check(q, "q")
     B, H, L, d = q.shape
@@ -77,8 +80,13 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | 
     else:
         _check(out, "out", (B, H, L, d), q.device)
     lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if return_lse else None
+    wl, wr = -1, -1
+    if window is not None:
+        wl, wr = (-1 if w is None else int(w) for w in window)
+        if wl < 0 and window[0] is not None or wr < 0 and window[1] is not None:
+            raise ValueError(f"window sides must be >= 0 or None, got {window}")
     lib = _lib.load()
-    plain = (H_kv == H and lse is None
+    plain = (H_kv == H and lse is None and window is None
              and all(t.is_contiguous() for t in (q, k, v, out)))
     if plain:
         _call(lib.attn_forward, q, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
@@ -87,12 +95,13 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | 
         _call(lib.attn_forward_ex, q, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
               lse.data_ptr() if lse is not None else None, B, H, H_kv, L, d,
               _strides(q), _strides(k), _strides(v), _strides(out), float(scale),
-              1 if causal else 0)
+              1 if causal else 0, wl, wr)
     return (out, lse) if return_lse else out
 
 
 def attention_packed_qkv(qkv: torch.Tensor, scale: float | None = None, causal: bool = False,
-                         out: torch.Tensor | None = None, return_lse: bool = False):
+                         out: torch.Tensor | None = None, return_lse: bool = False,
+                         window: tuple | None = None):
     """Attention over a packed [B, H, L, 3d] tensor whose last dimension holds
     q, k and v in that order -- the [T, 1, HW, 3C] qkv of the FastVideo Wan2.2
     VAE decoder's attention (frames T as B, one head) -- read in place through
@@ -102,7 +111,8 @@ def attention_packed_qkv(qkv: torch.Tensor, scale: float | None = None, causal: 
         raise ValueError(f"qkv's last dimension ({qkv.shape[-1]}) must be 3 * d")
     d = qkv.shape[-1] // 3
     q, k, v = qkv[..., :d], qkv[..., d:2 * d], qkv[..., 2 * d:]
-    return attention(q, k, v, scale=scale, causal=causal, out=out, return_lse=return_lse)
+    return attention(q, k, v, scale=scale, causal=causal, out=out, return_lse=return_lse,
+                     window=window)
 
 
 def path_for_head_dim(d: int) -> int:

@@ -37,17 +37,17 @@ int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
 // Two-pass workspace for a chunk of n heads: per head E and the two statistics
 // tables, plus the values pass's fp32 partial outputs when it splits the keys.
-int64_t chunk_workspace_bytes(int64_t n, const attn::TwoPassDims& t, bool causal) {
-  const int split = attn::values_split(n, t, causal);
+int64_t chunk_workspace_bytes(int64_t n, const attn::TwoPassDims& t, const attn::Band& band) {
+  const int split = attn::values_split(n, t, band);
   const int64_t part = split > 1 ? round256((int64_t)split * n * t.L * t.d * 4) : 0;
   return n * attn::two_pass_head_bytes(t) + part;
 }
 
 // Bytes attn_forward draws for BH heads: the largest of its chunks.
-int64_t two_pass_workspace_bytes(int64_t BH, const attn::TwoPassDims& t, bool causal) {
+int64_t two_pass_workspace_bytes(int64_t BH, const attn::TwoPassDims& t, const attn::Band& band) {
   const int64_t chunk = heads_per_chunk(BH, attn::two_pass_head_bytes(t));
   const int64_t last = BH - (BH - 1) / chunk * chunk;
-  return std::max(chunk_workspace_bytes(chunk, t, causal), chunk_workspace_bytes(last, t, causal));
+  return std::max(chunk_workspace_bytes(chunk, t, band), chunk_workspace_bytes(last, t, band));
 }
 
 bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
@@ -163,15 +163,15 @@ hipError_t timed(int id, hipStream_t s, bool on, F&& launch) {
 }
 
 int run_two_pass(const void* q, const void* k, const void* v, void* out, float* lse,
-                 attn::HeadMap hm, int64_t BH, int64_t L, int64_t d, float sl2, bool causal,
-                 hipStream_t stream) {
+                 attn::HeadMap hm, int64_t BH, int64_t L, int64_t d, float sl2,
+                 const attn::Band& band, hipStream_t stream) {
   const attn::TwoPassDims t = attn::two_pass_dims(L, d);
   const int64_t per_head = attn::two_pass_head_bytes(t);
   const int64_t chunk = heads_per_chunk(BH, per_head);
   const bool on = timing_on();
 
   Workspace* wsp = nullptr;
-  if (acquire_workspace(stream, (size_t)two_pass_workspace_bytes(BH, t, causal), &wsp) !=
+  if (acquire_workspace(stream, (size_t)two_pass_workspace_bytes(BH, t, band), &wsp) !=
       hipSuccess)
     return ATTN_ERR_WORKSPACE;
   char* base = (char*)wsp->ptr;
@@ -187,13 +187,13 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, float* 
     float* mref = (float*)(base + e_bytes);
     float* psum = (float*)(base + e_bytes + st_bytes);
     float* part = (float*)(base + e_bytes + 2 * st_bytes);
-    const int split = attn::values_split(n, t, causal);
+    const int split = attn::values_split(n, t, band);
     err = timed(ATTN_KERNEL_SCORES, stream, on, [&] {
-      return attn::launch_scores(q, k, E, mref, psum, hm, n, t, sl2, causal, stream);
+      return attn::launch_scores(q, k, E, mref, psum, hm, n, t, sl2, band, stream);
     });
     if (err == hipSuccess)
       err = timed(ATTN_KERNEL_VALUES, stream, on, [&] {
-        return attn::launch_values(v, E, mref, psum, out, lse, part, split, hm, n, t, causal,
+        return attn::launch_values(v, E, mref, psum, out, lse, part, split, hm, n, t, band,
                                    stream);
       });
     if (err == hipSuccess && split > 1)
@@ -211,19 +211,18 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, float* 
 // ld_max: the largest row stride of q, k and v (elements).
 int forward(const void* q, const void* k, const void* v, void* out, float* lse,
             const attn::HeadMap& hm, int64_t bh, int64_t L, int64_t d, int64_t ld_max,
-            float scale, int causal, hipStream_t stream) {
+            float scale, const attn::Band& band, hipStream_t stream) {
   // Kernels address one head with 32-bit byte offsets (rows up to L + 255 are
   // formed, past-the-end ones read as zero) and count heads in int.
   if ((L + 256) * ld_max * 2 >= ((int64_t)1 << 31) || bh >= ((int64_t)1 << 31) / 1024)
     return ATTN_ERR_TOO_LARGE;
   const float sl2 = scale * 1.4426950408889634f;
-  const bool c = causal != 0;
 
   if (attn_path_for_head_dim(d) == ATTN_PATH_ONLINE) {
     const int64_t nqb = (L + 127) / 128;
     if (nqb * bh >= ((int64_t)1 << 31)) return ATTN_ERR_TOO_LARGE;
     const hipError_t e = timed(ATTN_KERNEL_ONLINE, stream, timing_on(), [&] {
-      return attn::launch_online(q, k, v, out, lse, hm, (int)bh, (int)L, (int)d, sl2, c, stream);
+      return attn::launch_online(q, k, v, out, lse, hm, (int)bh, (int)L, (int)d, sl2, band, stream);
     });
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
   }
@@ -232,7 +231,7 @@ int forward(const void* q, const void* k, const void* v, void* out, float* lse,
   if (t.T > attn::kTwoPassMaxTiles || (int64_t)(t.L + 256) * t.Ls * 2 >= ((int64_t)1 << 32) - 1 ||
       (int64_t)t.T * t.T * bh >= ((int64_t)1 << 31))
     return ATTN_ERR_TOO_LARGE;
-  return run_two_pass(q, k, v, out, lse, hm, bh, L, d, sl2, c, stream);
+  return run_two_pass(q, k, v, out, lse, hm, bh, L, d, sl2, band, stream);
 }
 
 // One operand of attn_forward_ex: dims [B, heads, L, d] with element strides
@@ -302,7 +301,7 @@ int64_t attn_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int cau
   if (B == 0 || H == 0 || L == 0) return 0;
   if (L > (int64_t)1 << 20) return 0;
   const attn::TwoPassDims t = attn::two_pass_dims(L, d);
-  return two_pass_workspace_bytes(B * H, t, causal != 0);
+  return two_pass_workspace_bytes(B * H, t, attn::make_band(-1, -1, causal != 0, L));
 }
 
 int attn_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
@@ -321,15 +320,16 @@ int attn_forward(const void* q, const void* k, const void* v, void* out, int64_t
     return ATTN_ERR_ALIAS;
   if (L > ((int64_t)1 << 30) || H > ((int64_t)1 << 30)) return ATTN_ERR_TOO_LARGE;
   return forward(q, k, v, out, nullptr, attn::contiguous_heads((int)H, (int)L, (int)d), bh, L, d,
-                 d, scale, causal, stream);
+                 d, scale, attn::make_band(-1, -1, causal != 0, L), stream);
 }
 
 int attn_forward_ex(const void* q, const void* k, const void* v, void* out, float* lse,
                     int64_t B, int64_t H, int64_t H_kv, int64_t L, int64_t d,
                     const int64_t* q_strides, const int64_t* k_strides,
                     const int64_t* v_strides, const int64_t* o_strides, float scale, int causal,
-                    hipStream_t stream) {
+                    int64_t window_left, int64_t window_right, hipStream_t stream) {
   if (B < 0 || H < 0 || H_kv < 0 || L < 0 || d < 0) return ATTN_ERR_BAD_SHAPE;
+  if (window_left < -1 || window_right < -1) return ATTN_ERR_BAD_SHAPE;
   int64_t bh = 0, rows = 0, elems = 0, bytes = 0;
   if (__builtin_mul_overflow(B, H, &bh) || __builtin_mul_overflow(bh, L, &rows) ||
       __builtin_mul_overflow(rows, d, &elems) || __builtin_mul_overflow(elems, (int64_t)2, &bytes))
@@ -383,7 +383,8 @@ int attn_forward_ex(const void* q, const void* k, const void* v, void* out, floa
   hm.v = {vv.st[0], vv.st[1], (int)vv.st[2]};
   hm.o = {vo.st[0], vo.st[1], (int)vo.st[2]};
   const int64_t ld_max = std::max(vq.st[2], std::max(vk.st[2], vv.st[2]));
-  return forward(q, k, v, out, lse, hm, bh, L, d, ld_max, scale, causal, stream);
+  return forward(q, k, v, out, lse, hm, bh, L, d, ld_max, scale,
+                 attn::make_band(window_left, window_right, causal != 0, L), stream);
 }
 
 int attn_timing_enable(int enable) {

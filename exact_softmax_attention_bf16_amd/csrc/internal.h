@@ -46,6 +46,35 @@ inline bool is_plain(const HeadMap& m, int L, int d) {
   return m.group == 1 && dense(m.q) && dense(m.k) && dense(m.v) && dense(m.o);
 }
 
+// Keys each query sees: key j is allowed for query i iff
+// i - left <= j <= i + right (and j < L).  An unbounded side holds kNoLimit;
+// causal attention is {kNoLimit, 0}.
+constexpr int kNoLimit = 1 << 30;
+struct Band {
+  int left, right;
+};
+inline Band make_band(int64_t left, int64_t right, bool causal, int64_t L) {
+  Band b;
+  b.left = (left < 0 || left >= L) ? kNoLimit : (int)left;
+  b.right = (right < 0 || right >= L) ? kNoLimit : (int)right;
+  if (causal) b.right = 0;
+  return b;
+}
+__host__ __device__ inline bool band_is_full(const Band& b) {
+  return b.left >= kNoLimit && b.right >= kNoLimit;
+}
+__host__ __device__ inline bool band_is_causal(const Band& b) {
+  return b.left >= kNoLimit && b.right == 0;
+}
+// Score tiles (edge `tile` keys) that query tile qt meets: [*lo, *hi] within [0, T).
+__host__ __device__ inline void band_tiles(const Band& b, int qt, int T, int tile, int* lo,
+                                           int* hi) {
+  const int first_key = qt * tile - b.left;  // the tile's first query, leftmost key
+  *lo = (b.left >= kNoLimit || first_key <= 0) ? 0 : first_key / tile;
+  const int64_t last_key = (int64_t)qt * tile + tile - 1 + b.right;
+  *hi = (b.right >= kNoLimit || last_key >= (int64_t)T * tile) ? T - 1 : (int)(last_key / tile);
+}
+
 // Sizes of the two-pass path's per-head staging, all in elements.
 struct TwoPassDims {
   int L;   // sequence length
@@ -70,15 +99,15 @@ int64_t two_pass_head_bytes(const TwoPassDims& t);
 // lse (may be null): fp32 [global head][L], the natural log of each row's
 // softmax denominator.
 hipError_t launch_online(const void* q, const void* k, const void* v, void* out, float* lse,
-                         const HeadMap& hm, int BH, int L, int d, float sl2, bool causal,
+                         const HeadMap& hm, int BH, int L, int d, float sl2, const Band& band,
                          hipStream_t s);
 
 // Scores pass: per 256x256 (key, query) tile, E = bf16(2^(y - m)) with
 // y = sl2 * q.k, m = ceil(max over the tile's keys of y) per query, plus m and
 // the sum of the stored E per (tile, query).
 hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, float* psum,
-                         const HeadMap& hm, int BH, const TwoPassDims& t, float sl2, bool causal,
-                         hipStream_t s);
+                         const HeadMap& hm, int BH, const TwoPassDims& t, float sl2,
+                         const Band& band, hipStream_t s);
 
 // Values pass: O = (sum over tiles of 2^(m_t - M) E_t V_t) / (sum_t 2^(m_t - M) psum_t).
 // With split > 1 the keys of each query tile are divided among `split`
@@ -89,11 +118,11 @@ constexpr int kValuesMaxSplit = 4;
 constexpr int kValuesMinSplitSteps = 8;  // K steps (64 keys each) per split at least
 // Splits used for BH heads: 1 unless the unsplit grid would leave at least half
 // of the compute units idle.  Depends on the shape only.
-int values_split(int64_t BH, const TwoPassDims& t, bool causal);
+int values_split(int64_t BH, const TwoPassDims& t, const Band& band);
 // lse as for launch_online.
 hipError_t launch_values(const void* v, const void* E, const float* mref, const float* psum,
                          void* out, float* lse, float* part, int split, const HeadMap& hm, int BH,
-                         const TwoPassDims& t, bool causal, hipStream_t s);
+                         const TwoPassDims& t, const Band& band, hipStream_t s);
 hipError_t launch_values_reduce(const float* part, void* out, int split, const HeadMap& hm,
                                 int BH, const TwoPassDims& t, hipStream_t s);
 

@@ -26,8 +26,11 @@
 //     registers on the way into LDS so that V^T rows hold consecutive keys.
 //   * K/V tiles are double-buffered: the next tile's loads are in flight while
 //     the current one is consumed.
-//   * Keys past L (and, when causal, past the query) are masked to -inf; loads
-//     past the end of a head return zero through the buffer resource bounds.
+//   * Keys past L, and outside the query's band (after it when causal, or
+//     beyond a sliding window), are masked to -inf; a workgroup visits only
+//     the key blocks its queries' bands meet, a wave skips blocks its own
+//     queries do not see, and loads past the end of a head return zero
+//     through the buffer resource bounds.
 //   * Heads are found through a HeadMap (any batch, head and row strides with
 //     contiguous channels; one key/value head per `group` query heads), and
 //     the merged (m, l) give each row's log-sum-exp when it is asked for.
@@ -55,13 +58,18 @@ struct OnlineSmem {
 // PLAIN: q, k, v and out are contiguous [B, H, L, D] with one key/value head
 // per query head, so head bh starts at bh * L * D (no division by H, whose
 // expansion would sit ahead of the first load of this short kernel).
-template <int D, bool CAUSAL, bool PLAIN>
+// MASK: which keys below L each query i may see -- kAllKeys: all of them;
+// kCausal: j <= i; kWindow: i - left <= j <= i + right (band.left, band.right,
+// either side possibly unbounded).  Causal has its own instantiation so that
+// it carries no left-side tests.
+enum { kAllKeys = 0, kCausal = 1, kWindow = 2 };
+template <int D, int MASK, bool PLAIN>
 __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v,
                                                           uint16_t* __restrict__ out,
                                                           float* __restrict__ lse, HeadMap hm,
-                                                          int L, int nqb, float sl2) {
+                                                          int L, int nqb, float sl2, Band band) {
   constexpr int CPR = D / 8;                       // 16-byte chunks per K row
   constexpr int SWZ = (CPR >= 8 ? 8 : CPR) - 1;    // chunk-index bits that are swizzled
   constexpr int VROW = kBN * 2 + 8;                // bytes per V^T row: 64 keys + pad
@@ -86,7 +94,10 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int bh = lid / nqb;
   int qb = lid % nqb;
-  if (CAUSAL) qb = nqb - 1 - qb;  // the longest rows start first
+  if (MASK == kCausal) qb = nqb - 1 - qb;  // the longest rows start first
+  constexpr bool BANDED = MASK != kAllKeys, HAS_LEFT = MASK == kWindow;
+  const int left = HAS_LEFT ? band.left : kNoLimit;
+  const int right = MASK == kCausal ? 0 : band.right;
 
   // Rows past L of each head read as zero: the resources end after row L - 1.
   const int ldq = PLAIN ? D : hm.q.ld, ldk = PLAIN ? D : hm.k.ld, ldv = PLAIN ? D : hm.v.ld;
@@ -104,8 +115,11 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   for (int s = 0; s < NS; ++s)
     qf[s] = __builtin_bit_cast(bf16x8, load16(rq, (uint32_t)(myq * ldq + 16 * s + 8 * h) * 2));
 
-  const int kend = CAUSAL ? min(L, qb * kBM + kBM) : L;
-  const int ntiles = (kend + kBN - 1) / kBN;
+  // Key blocks t0 .. t0 + ntiles - 1 meet the band of this workgroup's queries.
+  const int kstart = HAS_LEFT ? max(0, qb * kBM - left) : 0;
+  const int kend = BANDED ? min(L, qb * kBM + kBM + right) : L;
+  const int t0 = kstart / kBN;
+  const int ntiles = (kend + kBN - 1) / kBN - t0;
 
   auto issue_k = [&](int t, int buf) {
 #pragma unroll
@@ -146,29 +160,32 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   for (int c = 0; c < NCB; ++c) o[c] = f32x16{};
   float m = -INFINITY, lsum = 0.f;
 
-  // Group g takes key blocks t = g + kGroups * it.  Both groups run the same
-  // number of iterations (so that every wave meets every barrier); a block
-  // past the end is skipped.
+  // Group g takes key blocks t = t0 + g + kGroups * it.  Both groups run the
+  // same number of iterations (so that every wave meets every barrier); a
+  // block past the end is skipped.
   const int niter = (ntiles + kGroups - 1) / kGroups;
+  const int tend = t0 + ntiles;
   u32x4 vr[4];
   if (g < ntiles) {
-    issue_k(g, 0);
-    load_v(g, vr);
+    issue_k(t0 + g, 0);
+    load_v(t0 + g, vr);
     wait_vmem();
     store_vt(0, vr);
   }
   __syncthreads();
 
   for (int it = 0; it < niter; ++it) {
-    const int t = g + kGroups * it;
+    const int t = t0 + g + kGroups * it;
     const int buf = it & 1;
-    const bool has_next = t + kGroups < ntiles;
+    const bool has_next = t + kGroups < tend;
     if (has_next) {
       issue_k(t + kGroups, buf ^ 1);
       load_v(t + kGroups, vr);
     }
     const int kbase = t * kBN;
-    const bool active = t < ntiles && (!CAUSAL || kbase <= q0 + 31);
+    // This wave's 32 queries see some key of the block.
+    const bool active = t < tend && (!BANDED || kbase <= q0 + 31 + right) &&
+                        (!HAS_LEFT || kbase + kBN - 1 >= q0 - left);
     if (active) {
       // S^T block: 64 keys x 32 queries, two 32-key halves.
       f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -185,7 +202,8 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
       // Softmax update for this lane's query over its 32 of the 64 keys.  The
       // maximum is taken on the raw scores (scaled afterwards; the sign of sl2
       // picks max or min), and y - m is one FMA: p = 2^(s * sl2 - m).
-      const bool need_mask = (kbase + kBN > L) || (CAUSAL && kbase + kBN - 1 > q0);
+      const bool need_mask = (kbase + kBN > L) || (BANDED && kbase + kBN - 1 > q0 + right) ||
+                             (HAS_LEFT && kbase < q0 + 31 - left);
       float tmax;
       if (need_mask) {
         tmax = -INFINITY;
@@ -194,7 +212,8 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int key = kbase + kb * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-            const bool off = key >= L || (CAUSAL && key > myq);
+            const bool off = key >= L || (BANDED && key > myq + right) ||
+                             (HAS_LEFT && key < myq - left);
             s[kb][j] = off ? -INFINITY : s[kb][j] * sl2;
             tmax = fmaxf(tmax, s[kb][j]);
           }
@@ -314,38 +333,43 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   }
 }
 
-template <int D, bool C, bool PLAIN>
+template <int D, int MASK, bool PLAIN>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* out, float* lse,
-                      HeadMap hm, int BH, int L, float sl2, hipStream_t s) {
+                      HeadMap hm, int BH, int L, float sl2, Band band, hipStream_t s) {
   const int nqb = (L + kBM - 1) / kBM;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * kWaves);
   const uint16_t* qp = (const uint16_t*)q;
   const uint16_t* kp = (const uint16_t*)k;
   const uint16_t* vp = (const uint16_t*)v;
   uint16_t* op = (uint16_t*)out;
-  void* args[] = {&qp, &kp, &vp, &op, &lse, &hm, &L, (void*)&nqb, &sl2};
-  return hipLaunchKernel((const void*)&online_attn_kernel<D, C, PLAIN>, grid, block, args, 0, s);
+  void* args[] = {&qp, &kp, &vp, &op, &lse, &hm, &L, (void*)&nqb, &sl2, &band};
+  return hipLaunchKernel((const void*)&online_attn_kernel<D, MASK, PLAIN>, grid, block, args, 0, s);
 }
 
-template <int D, bool C>
+template <int D, int MASK>
+hipError_t launch_m(const void* q, const void* k, const void* v, void* out, float* lse,
+                    const HeadMap& hm, int BH, int L, float sl2, Band band, hipStream_t s) {
+  return is_plain(hm, L, D) ? launch_one<D, MASK, true>(q, k, v, out, lse, hm, BH, L, sl2, band, s)
+                            : launch_one<D, MASK, false>(q, k, v, out, lse, hm, BH, L, sl2, band, s);
+}
+
+template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* out, float* lse,
-                    const HeadMap& hm, int BH, int L, float sl2, hipStream_t s) {
-  return is_plain(hm, L, D) ? launch_one<D, C, true>(q, k, v, out, lse, hm, BH, L, sl2, s)
-                            : launch_one<D, C, false>(q, k, v, out, lse, hm, BH, L, sl2, s);
+                    const HeadMap& hm, int BH, int L, float sl2, Band band, hipStream_t s) {
+  if (band_is_full(band)) return launch_m<D, kAllKeys>(q, k, v, out, lse, hm, BH, L, sl2, band, s);
+  if (band_is_causal(band)) return launch_m<D, kCausal>(q, k, v, out, lse, hm, BH, L, sl2, band, s);
+  return launch_m<D, kWindow>(q, k, v, out, lse, hm, BH, L, sl2, band, s);
 }
 
 }  // namespace
 
 hipError_t launch_online(const void* q, const void* k, const void* v, void* out, float* lse,
-                         const HeadMap& hm, int BH, int L, int d, float sl2, bool causal,
+                         const HeadMap& hm, int BH, int L, int d, float sl2, const Band& band,
                          hipStream_t s) {
   switch (d) {
-    case 32: return causal ? launch_d<32, true>(q, k, v, out, lse, hm, BH, L, sl2, s)
-                           : launch_d<32, false>(q, k, v, out, lse, hm, BH, L, sl2, s);
-    case 64: return causal ? launch_d<64, true>(q, k, v, out, lse, hm, BH, L, sl2, s)
-                           : launch_d<64, false>(q, k, v, out, lse, hm, BH, L, sl2, s);
-    case 128: return causal ? launch_d<128, true>(q, k, v, out, lse, hm, BH, L, sl2, s)
-                            : launch_d<128, false>(q, k, v, out, lse, hm, BH, L, sl2, s);
+    case 32: return launch_d<32>(q, k, v, out, lse, hm, BH, L, sl2, band, s);
+    case 64: return launch_d<64>(q, k, v, out, lse, hm, BH, L, sl2, band, s);
+    case 128: return launch_d<128>(q, k, v, out, lse, hm, BH, L, sl2, band, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -103,37 +103,54 @@ __device__ __forceinline__ int scores_query_base(int wave) {
   return ((wave ^ (wave >> 2)) & 1) * 128 + ((wave >> 1) & 1) * 64;
 }
 
-// Tile idx of the pass: heads in order, then query tiles, then key tiles
-// (causal: only kt <= qt, row by row).
-__device__ __forceinline__ ScoresTile scores_tile(int idx, int T, int causal) {
+// Tile idx of the pass: heads in order, then query tiles, then the key tiles
+// each query tile's band meets (band_tiles; per_head tiles per head).  Closed
+// forms for no mask (all T) and causal (kt <= qt); a walk over the query tiles
+// for a sliding window.
+__device__ __forceinline__ ScoresTile scores_tile(int idx, int T, const Band& band, int per_head) {
   ScoresTile t;
-  const int per_head = causal ? T * (T + 1) / 2 : T * T;
   t.bh = idx / per_head;
-  const int r = idx - t.bh * per_head;
-  if (causal) {
+  int r = idx - t.bh * per_head;
+  if (band_is_full(band)) {
+    t.qt = r / T;
+    t.kt = r - t.qt * T;
+  } else if (band_is_causal(band)) {
     int qt = (int)((sqrtf(8.f * (float)r + 1.f) - 1.f) * 0.5f);
     while ((qt + 1) * (qt + 2) / 2 <= r) ++qt;
     while (qt * (qt + 1) / 2 > r) --qt;
     t.qt = qt;
     t.kt = r - qt * (qt + 1) / 2;
   } else {
-    t.qt = r / T;
-    t.kt = r - t.qt * T;
+    int qt = 0, lo = 0, hi = 0;
+    for (;; ++qt) {  // r < per_head: ends at a query tile below T
+      band_tiles(band, qt, T, kTile, &lo, &hi);
+      if (r <= hi - lo) break;
+      r -= hi - lo + 1;
+    }
+    t.qt = qt;
+    t.kt = lo + r;
   }
   return t;
 }
 
+// Every (query, key) pair of the tile lies inside the band and below L.
+__device__ __forceinline__ bool scores_tile_unmasked(const ScoresTile& t, const Band& band, int L) {
+  const int k0 = t.kt * kTile, q0 = t.qt * kTile;
+  return k0 + kTile <= L && k0 >= q0 + kTile - 1 - band.left && k0 + kTile - 1 <= q0 + band.right;
+}
+
 // True when every score of this wave's block in the tile is discarded: its keys
-// or its queries all lie past L, or (causal) all its keys follow all its
-// queries.  Such a wave issues its share of the loads and meets every barrier
+// or its queries all lie past L, or all its keys lie outside all its queries'
+// bands (e.g. causal: all its keys follow all its queries).  Such a wave issues its share of the loads and meets every barrier
 // but skips its fragment reads and MFMAs, and enters the epilogue with zero
 // accumulators, none of which reach memory: keys past L or after the query are
 // selected away, and rows past L are not stored (their maxima and sums are
 // exchanged only with the partner wave holding the same rows).
-__device__ __forceinline__ bool scores_wave_idle(const ScoresTile& t, int wave, int L, int causal) {
+__device__ __forceinline__ bool scores_wave_idle(const ScoresTile& t, int wave, int L,
+                                                 const Band& band) {
   const int key0 = t.kt * kTile + scores_key_half(wave) * 128;
   const int q0 = t.qt * kTile + scores_query_base(wave);
-  return key0 >= L || q0 >= L || (causal && key0 > q0 + 63);
+  return key0 >= L || q0 >= L || key0 > q0 + 63 + band.right || key0 + 127 < q0 - band.left;
 }
 
 template <bool MASK>
@@ -141,7 +158,7 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ], Sco
                                                 uint16_t* __restrict__ E,
                                                 float* __restrict__ mref,
                                                 float* __restrict__ psum, const ScoresTile& t,
-                                                int L, int Ls, int T, float sl2, int causal) {
+                                                int L, int Ls, int T, float sl2, const Band& band) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = scores_key_half(wave), c32 = lane & 31, h = lane >> 5;
   const int qbase = scores_query_base(wave);  // this wave's first query column in the tile
@@ -157,9 +174,13 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ], Sco
     const int ql = qbase + bj * 32 + c32;
     const int query = t.qt * kTile + ql;
     // Key key0 + 4h + c (c = 32 bi + 8 (j / 4) + j % 4, a constant) is allowed
-    // for this query iff c < lim.
-    int lim = (causal ? min(L, query + 1) : L) - (key0 + 4 * h);
-    auto masked = [&](int bi, int j) { return bi * 32 + 8 * (j >> 2) + (j & 3) >= lim; };
+    // for this query iff lo <= c < lim.
+    int lim = min(L, query + band.right + 1) - (key0 + 4 * h);
+    int lo = query - band.left - (key0 + 4 * h);
+    auto masked = [&](int bi, int j) {
+      const int c = bi * 32 + 8 * (j >> 2) + (j & 3);
+      return c >= lim || c < lo;
+    };
 
     // Maximum of y (interior tiles: on the raw accumulator, then scaled; the
     // sign of sl2 picks max or min).
@@ -191,7 +212,7 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ], Sco
     __syncthreads();  // both key halves' maxima for this column are in red
     // Recompute the mask below instead of keeping 64 mask bits alive across the
     // barrier (the compiler would otherwise hold them in scalar registers).
-    asm volatile("" : "+v"(lim));
+    asm volatile("" : "+v"(lim), "+v"(lo));
 
     const float tmax = fmaxf(sm.red[0][ql], sm.red[1][ql]);
     const float m2 = tmax == -INFINITY ? -INFINITY : ceilf(tmax);
@@ -254,7 +275,7 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ], Sco
 __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, uint16_t* __restrict__ E,
     float* __restrict__ mref, float* __restrict__ psum, HeadMap hm, int L, int d, int T, int Ls,
-    float sl2, int causal, int ntiles) {
+    float sl2, Band band, int per_head, int ntiles) {
   __shared__ ScoresSmem smem;
   GemmSmem& sm = smem.g;
 
@@ -277,7 +298,7 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
   int li = 0, lk = 0;
   __amdgpu_buffer_rsrc_t rk, rq;
   auto set_load_tile = [&](int i) {
-    const ScoresTile t = scores_tile(first + i * G, T, causal);
+    const ScoresTile t = scores_tile(first + i * G, T, band, per_head);
     const int k0 = t.kt * kTile, q0 = t.qt * kTile;
     // Each resource ends after the head's row L - 1: rows past L read as zero.
     rk = make_rsrc(k + hm.k_off(t.bh) + (size_t)k0 * ldk, ((uint32_t)(L - 1 - k0) * ldk + d) * 2u);
@@ -364,8 +385,8 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
 
   int s = 0;
   for (int i = 0; i < my_tiles; ++i) {
-    const ScoresTile t = scores_tile(first + i * G, T, causal);
-    if (__builtin_amdgcn_readfirstlane((int)scores_wave_idle(t, wave, L, causal))) {
+    const ScoresTile t = scores_tile(first + i * G, T, band, per_head);
+    if (__builtin_amdgcn_readfirstlane((int)scores_wave_idle(t, wave, L, band))) {
       // Fresh (zero) accumulators: nothing stays live across tiles.
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
@@ -376,11 +397,10 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
       step(std::true_type{}, s++);
       for (int kk = 1; kk < nk; ++kk) step(std::false_type{}, s++);
     }
-    const bool need_mask = (t.kt + 1) * kTile > L || (causal && t.kt >= t.qt);
-    if (need_mask)
-      scores_epilogue<true>(acc, smem, E, mref, psum, t, L, Ls, T, sl2, causal);
+    if (!scores_tile_unmasked(t, band, L))
+      scores_epilogue<true>(acc, smem, E, mref, psum, t, L, Ls, T, sl2, band);
     else
-      scores_epilogue<false>(acc, smem, E, mref, psum, t, L, Ls, T, sl2, causal);
+      scores_epilogue<false>(acc, smem, E, mref, psum, t, L, Ls, T, sl2, band);
     // The next step's first fragments: read again (its stage is not refilled
     // before that step's end) instead of holding them through the epilogue.
     read_frags(cur, la, lb, sm.a[s & 1], sm.b[s & 1], abase, bbase, lane, 0);
@@ -435,7 +455,7 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
                                                      uint16_t* __restrict__ out,
                                                      float* __restrict__ lse,
                                                      float* __restrict__ part, HeadMap hm, int L,
-                                                     int d, int T, int Ls, int Lk, int causal,
+                                                     int d, int T, int Ls, int Lk, Band band,
                                                      int ncb, int split, int nheads) {
   __shared__ ValuesSmem smem;
   GemmSmem& sm = smem.g;
@@ -452,13 +472,15 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1, c32 = lane & 31, h = lane >> 5;
 
-  const int tiles = causal ? qt + 1 : T;
-  const int kend = causal ? min(Lk, (qt + 1) * kTile) : Lk;
+  // Score tiles [tlo, thi] meet this query tile's band: keys [kbeg, kend).
+  int tlo, thi;
+  band_tiles(band, qt, T, kTile, &tlo, &thi);
+  const int kbeg = tlo * kTile, kend = min(Lk, (thi + 1) * kTile);
   // Split sp of `split` takes K steps [k_first, k_first + nk) (never empty:
   // the host keeps split <= the fewest steps of any query tile).
-  const int nk_all = kend / kStepK;
-  const int k_first = SPLIT ? nk_all * sp / split : 0;
-  const int nk = SPLIT ? nk_all * (sp + 1) / split - k_first : nk_all;
+  const int nk_all = (kend - kbeg) / kStepK;
+  const int k_first = kbeg / kStepK + (SPLIT ? nk_all * sp / split : 0);
+  const int nk = SPLIT ? kbeg / kStepK + nk_all * (sp + 1) / split - k_first : nk_all;
 
   // Thread tid owns query qt*256 + tid: M = max_t m_t, l = sum_t 2^(m_t - M) psum_t,
   // and the shift M - m_t of each tile (a nonnegative integer; -inf tiles -> 255).
@@ -468,11 +490,11 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
     const float* ph = psum + (size_t)bh * T * L;
     const int qc = min(qt * kTile + tid, L - 1);
     float M = -INFINITY, l = 0.f;
-    for (int t0 = 0; t0 < tiles; t0 += 16) {
+    for (int t0 = tlo; t0 <= thi; t0 += 16) {
       float mt[16], pt[16];
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
-        const int t = min(t0 + u, tiles - 1);
+        const int t = min(t0 + u, thi);
         mt[u] = mh[(size_t)t * L + qc];
         pt[u] = ph[(size_t)t * L + qc];
       }
@@ -482,17 +504,17 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
       l = M == -INFINITY ? 0.f : l * exp2_fast(M - Mn);
 #pragma unroll
       for (int u = 0; u < 16; ++u)
-        if (t0 + u < tiles) l += pt[u] * exp2_fast(mt[u] - Mn);
+        if (t0 + u <= thi && mt[u] != -INFINITY) l += pt[u] * exp2_fast(mt[u] - Mn);
       M = Mn;
     }
     // The shifts need the final M: a second pass over the (now cached) stats.
-    for (int t0 = 0; t0 < tiles; t0 += 16) {
+    for (int t0 = tlo; t0 <= thi; t0 += 16) {
       float mt[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) mt[u] = mh[(size_t)min(t0 + u, tiles - 1) * L + qc];
+      for (int u = 0; u < 16; ++u) mt[u] = mh[(size_t)min(t0 + u, thi) * L + qc];
 #pragma unroll
       for (int u = 0; u < 16; ++u)
-        if (t0 + u < tiles) shift_tab[t0 + u][tid] = (uint8_t)fminf(M - mt[u], 255.f);
+        if (t0 + u <= thi) shift_tab[t0 + u][tid] = (uint8_t)fminf(M - mt[u], 255.f);
     }
     inv_l[tid] = 1.f / l;
     // The row's softmax denominator is sum_j 2^(y_j) = 2^M l (y in log2 units).
@@ -624,26 +646,43 @@ static int device_cu_count() {
   return n;
 }
 
+// Score tiles of one head: the key tiles each query tile's band meets.
+int band_tiles_per_head(const Band& band, int T) {
+  int n = 0;
+  for (int qt = 0; qt < T; ++qt) {
+    int lo, hi;
+    band_tiles(band, qt, T, kTile, &lo, &hi);
+    n += hi - lo + 1;
+  }
+  return n;
+}
+
 hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, float* psum,
-                         const HeadMap& hm, int BH, const TwoPassDims& t, float sl2, bool causal,
-                         hipStream_t s) {
+                         const HeadMap& hm, int BH, const TwoPassDims& t, float sl2,
+                         const Band& band, hipStream_t s) {
   const uint16_t* qp = (const uint16_t*)q;
   const uint16_t* kp = (const uint16_t*)k;
   uint16_t* ep = (uint16_t*)E;
-  int L = t.L, d = t.d, T = t.T, Ls = t.Ls, c = causal ? 1 : 0;
-  int ntiles = BH * (causal ? T * (T + 1) / 2 : T * T);
+  int L = t.L, d = t.d, T = t.T, Ls = t.Ls;
+  int per_head = band_tiles_per_head(band, T);
+  int ntiles = BH * per_head;
   const int grid = std::min(ntiles, device_cu_count());  // one workgroup per CU (LDS-bound)
   HeadMap m = hm;
-  void* args[] = {&qp, &kp, &ep, &mref, &psum, &m, &L, &d, &T, &Ls, &sl2, &c, &ntiles};
+  Band b = band;
+  void* args[] = {&qp, &kp, &ep, &mref, &psum, &m, &L, &d, &T, &Ls, &sl2, &b, &per_head, &ntiles};
   return hipLaunchKernel((const void*)&scores_kernel, dim3((unsigned)grid),
                          dim3(64 * kScoresWaves), args, 0, s);
 }
 
-int values_split(int64_t BH, const TwoPassDims& t, bool causal) {
+int values_split(int64_t BH, const TwoPassDims& t, const Band& band) {
   const int64_t base = BH * t.T * ((t.d + kTile - 1) / kTile);  // workgroups without a split
   if (base * 2 > kValuesTargetWorkgroups) return 1;
-  const int64_t steps = t.Lk / kStepK;                       // K steps of a full query tile
-  const int64_t fewest = causal ? std::min<int64_t>(kTile / kStepK, steps) : steps;
+  int64_t fewest = t.Lk / kStepK;  // K steps of the narrowest query tile's band
+  for (int qt = 0; qt < t.T; ++qt) {
+    int lo, hi;
+    band_tiles(band, qt, t.T, kTile, &lo, &hi);
+    fewest = std::min<int64_t>(fewest, (std::min(t.Lk, (hi + 1) * kTile) - lo * kTile) / kStepK);
+  }
   // Each split keeps at least kValuesMinSplitSteps K steps: shorter loops are
   // dominated by the fixed cost of a workgroup, and the partials cost a pass.
   int64_t s = std::min<int64_t>(kValuesTargetWorkgroups / base, kValuesMaxSplit);
@@ -653,15 +692,16 @@ int values_split(int64_t BH, const TwoPassDims& t, bool causal) {
 
 hipError_t launch_values(const void* v, const void* E, const float* mref, const float* psum,
                          void* out, float* lse, float* part, int split, const HeadMap& hm, int BH,
-                         const TwoPassDims& t, bool causal, hipStream_t s) {
+                         const TwoPassDims& t, const Band& band, hipStream_t s) {
   const uint16_t* vtp = (const uint16_t*)v;
   const uint16_t* ep = (const uint16_t*)E;
   uint16_t* op = (uint16_t*)out;
-  int L = t.L, d = t.d, T = t.T, Ls = t.Ls, Lk = t.Lk, c = causal ? 1 : 0;
+  int L = t.L, d = t.d, T = t.T, Ls = t.Ls, Lk = t.Lk;
   int ncb = (t.d + kTile - 1) / kTile;
   int nheads = BH;
   HeadMap m = hm;
-  void* args[] = {&vtp, &ep, &mref, &psum, &op, &lse, &part, &m, &L, &d, &T, &Ls, &Lk, &c, &ncb,
+  Band b = band;
+  void* args[] = {&vtp, &ep, &mref, &psum, &op, &lse, &part, &m, &L, &d, &T, &Ls, &Lk, &b, &ncb,
                   &split, &nheads};
   const void* kern = split > 1 ? (const void*)&values_kernel<true> : (const void*)&values_kernel<false>;
   return hipLaunchKernel(kern, dim3((unsigned)(BH * T * ncb * split)), dim3(256), args, 0, s);

@@ -99,7 +99,8 @@ int attn_forward(const void* q, const void* k, const void* v, void* out,
  * strides, lets the query heads be a multiple of the key/value heads (each
  * key/value head broadcast over its group of consecutive query heads) and
  * optionally writes each row's log-sum-exp (log of the row sum plus the
- * scaled row maximum, stored in its epilogue).
+ * scaled row maximum, stored in its epilogue); it also takes a sliding window
+ * (window_size_left / window_size_right).
  *
  *   q, out        : [B, H, L, d] views; k, v : [B, H_kv, L, d] views.  Each is a
  *                   device pointer to its element [0,0,0,0] plus three element
@@ -115,6 +116,12 @@ int attn_forward(const void* q, const void* k, const void* v, void* out,
  *                   lse[i] = log(sum over allowed j of exp(scale * q_i . k_j)).
  *   H_kv          : key/value heads, >= 1 and dividing H; query head h reads
  *                   key/value head h / (H / H_kv) of the same batch entry.
+ *   window_left,  : a sliding window (fmha.py's window_size_left / _right):
+ *   window_right    key j is allowed for query i only if
+ *                   i - window_left <= j <= i + window_right; -1 leaves that
+ *                   side unbounded (-1, -1: no window).  causal additionally
+ *                   caps the right side at 0.  Every row keeps key i, so no
+ *                   row is empty.  Values below -1 return ATTN_ERR_BAD_SHAPE.
  *   B, H, L, d, scale, causal, stream : as for attn_forward.
  *
  * out must not overlap q, k, v (compared as the address ranges each view
@@ -126,7 +133,8 @@ int attn_forward_ex(const void* q, const void* k, const void* v, void* out, floa
                     int64_t B, int64_t H, int64_t H_kv, int64_t L, int64_t d,
                     const int64_t* q_strides, const int64_t* k_strides,
                     const int64_t* v_strides, const int64_t* o_strides,
-                    float scale, int causal, hipStream_t stream);
+                    float scale, int causal, int64_t window_left, int64_t window_right,
+                    hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 const char* attn_status_string(int status);

@@ -205,9 +205,9 @@ def st(*x):
 
 
 def fwd_ex(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, lse=None, B=1, H=1, H_kv=1,
-           L=16, d=64, qs=None, ks=None, vs=None, os_=None, scale=0.125, causal=0):
+           L=16, d=64, qs=None, ks=None, vs=None, os_=None, scale=0.125, causal=0, wl=-1, wr=-1):
     return _lib.load().attn_forward_ex(q, k, v, out, lse, B, H, H_kv, L, d, qs, ks, vs, os_,
-                                       scale, causal, None)
+                                       scale, causal, wl, wr, None)
 
 
 # A valid call would launch; these shapes pass every earlier check and are then
@@ -303,3 +303,16 @@ def test_python_binding_rejects_bad_layouts():
         attention(x, x[:, :1], x[:, :1])
     with pytest.raises(ValueError):
         attention_packed_qkv(torch.zeros(1, 1, 4, 100, dtype=torch.bfloat16))
+
+
+@pytest.mark.parametrize("wl,wr", [(-2, 0), (0, -2), (-5, -5)])
+def test_ex_bad_window(wl, wr):
+    assert fwd_ex(wl=wl, wr=wr) == _lib.ATTN_ERR_BAD_SHAPE
+
+
+def test_ex_window_is_accepted():
+    L = BIG_L
+    n = L * 64 * 2
+    for wl, wr in [(0, 0), (5, -1), (-1, 7), (L + 5, L + 5)]:
+        assert fwd_ex(q=A, k=A + n, v=A + 2 * n, out=A + 3 * n, L=L, wl=wl, wr=wr,
+                      qs=st(L * 128, L * 128, 128)) == _lib.ATTN_ERR_TOO_LARGE

@@ -1,5 +1,6 @@
 """GPU parity for attn_forward_ex: packed and permuted layouts read in place,
-grouped key/value heads, and the log-sum-exp output, against the float64 oracle.
+grouped key/value heads, sliding windows and the log-sum-exp output, against
+the float64 oracle.
 
 Output bar as in test_parity_gpu.py.  LSE bar, from the arithmetic: the kernels
 sum the bf16-rounded exponentials they multiply (bf16 keeps 8 significant
@@ -187,8 +188,86 @@ def test_ex_with_default_strides_equals_attn_forward():
         out = torch.empty_like(q)
         st = _lib.load().attn_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                          None, 2, 2, 2, 700, d, None, None, None, None,
-                                         1.0 / math.sqrt(d), 0,
+                                         1.0 / math.sqrt(d), 0, -1, -1,
                                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         torch.cuda.synchronize()
         assert st == _lib.ATTN_OK
         assert torch.equal(out, ref)
+
+
+# ---- sliding windows -------------------------------------------------------------
+
+WINDOWS = [(0, 0), (5, 3), (100, 0), (0, 100), (300, 200), (None, 70), (130, None), (1, 1000)]
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 1024])
+@pytest.mark.parametrize("window", WINDOWS)
+@pytest.mark.parametrize("causal", [False, True])
+def test_window(d, window, causal):
+    from exact_softmax_attention_bf16_amd import attention
+    B, H, L = 1, 2, 700
+    q, k, v = make_qkv(B, H, L, d, 180 + d)
+    s = 1.0 / math.sqrt(d)
+    o, lse = attention(q.to(DEV), k.to(DEV), v.to(DEV), scale=s, causal=causal, window=window,
+                       return_lse=True)
+    torch.cuda.synchronize()
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), s, causal, window)
+    ok, a, r = within_bar(to_f64(o), ref)
+    _report(f"window {window} d={d} causal={causal}", a, r)
+    assert ok, (a, r)
+    ok, err = lse_ok(lse, oracle.log_sum_exp(to_f64(q), to_f64(k), s, causal, window))
+    assert ok, err
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_window_of_width_zero_returns_v_exactly(d):
+    # one allowed key: p = e / e in fp32 times a bf16 value rounds back to it
+    from exact_softmax_attention_bf16_amd import attention
+    q, k, v = (t.to(DEV) for t in make_qkv(2, 2, 531, d, 190))
+    o = attention(q, k, v, window=(0, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(o, v)
+
+
+@pytest.mark.parametrize("d", [64, 1024])
+def test_window_limits_equal_unwindowed_and_causal_bitwise(d):
+    from exact_softmax_attention_bf16_amd import attention
+    L = 600
+    q, k, v = (t.to(DEV) for t in make_qkv(1, 2, L, d, 191))
+    full = attention(q, k, v)
+    causal = attention(q, k, v, causal=True)
+    wide = attention(q, k, v, window=(L, L))
+    left_only = attention(q, k, v, window=(None, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(wide, full)
+    assert torch.equal(left_only, causal)
+
+
+@pytest.mark.parametrize("L,d,window", [(2100, 512, (300, 200)), (1100, 256, (None, 0)),
+                                        (1500, 256, (600, None))])
+def test_window_with_key_split(L, d, window):
+    """One head: the values pass splits each query tile's band among workgroups."""
+    from exact_softmax_attention_bf16_amd import attention
+    q, k, v = make_qkv(1, 1, L, d, 192 + L)
+    s = 1.0 / math.sqrt(d)
+    o, lse = attention(q.to(DEV), k.to(DEV), v.to(DEV), scale=s, window=window, return_lse=True)
+    torch.cuda.synchronize()
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), s, False, window)
+    ok, a, r = within_bar(to_f64(o), ref)
+    _report(f"split window {window} L={L} d={d}", a, r)
+    assert ok, (a, r)
+    ok, err = lse_ok(lse, oracle.log_sum_exp(to_f64(q), to_f64(k), s, False, window))
+    assert ok, err
+
+
+def test_window_on_packed_grouped_strided_inputs():
+    from exact_softmax_attention_bf16_amd import attention
+    B, H, H_kv, L, d = 2, 4, 2, 450, 256
+    q = make_qkv(B, H, L, d, 193)[0]
+    _, k, v = make_qkv(B, H_kv, L, d, 194)
+    perm = [t.transpose(1, 2).contiguous().to(DEV).transpose(1, 2) for t in (q, k, v)]
+    o = attention(*perm, window=(40, 90), causal=True)
+    torch.cuda.synchronize()
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1.0 / math.sqrt(d), True, (40, 90))
+    ok, a, r = within_bar(to_f64(o), ref)
+    assert ok, (a, r)

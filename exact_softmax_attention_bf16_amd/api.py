@@ -80,11 +80,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | 
     else:
         _check(out, "out", (B, H, L, d), q.device)
     lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if return_lse else None
-    wl, wr = -1, -1
-    if window is not None:
-        wl, wr = (-1 if w is None else int(w) for w in window)
-        if wl < 0 and window[0] is not None or wr < 0 and window[1] is not None:
-            raise ValueError(f"window sides must be >= 0 or None, got {window}")
+    wl, wr = _window_args(window)
     lib = _lib.load()
     plain = (H_kv == H and lse is None and window is None
              and all(t.is_contiguous() for t in (q, k, v, out)))
@@ -96,6 +92,63 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | 
               lse.data_ptr() if lse is not None else None, B, H, H_kv, L, d,
               _strides(q), _strides(k), _strides(v), _strides(out), float(scale),
               1 if causal else 0, wl, wr)
+    return (out, lse) if return_lse else out
+
+
+def _window_args(window):
+    if window is None:
+        return -1, -1
+    wl, wr = (-1 if w is None else int(w) for w in window)
+    if wl < 0 and window[0] is not None or wr < 0 and window[1] is not None:
+        raise ValueError(f"window sides must be >= 0 or None, got {window}")
+    return wl, wr
+
+
+def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                     max_seqlen: int, scale: float | None = None, causal: bool = False,
+                     out: torch.Tensor | None = None, return_lse: bool = False,
+                     window: tuple | None = None):
+    """Attention over a batch of sequences of different lengths packed along the
+    tokens (the cum_seqlen interface of cuDNN's FMHA example): q is
+    [total, H, d], k and v [total, H_kv, d], cu_seqlens an int32 tensor of B + 1
+    offsets on the same device (sequence b is tokens cu_seqlens[b] ..
+    cu_seqlens[b + 1] - 1), max_seqlen >= the longest sequence.  d must be 32,
+    64 or 128.  Returns out [total, H, d] (and lse float32 [total, H] with
+    ``return_lse``); rows of tokens in no sequence are left as they were."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a 3-D tensor [total, H, d]")
+    total, H, d = q.shape
+    for t, name, heads in ((q, "q", H), (k, "k", None), (v, "v", None)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 3:
+            raise ValueError(f"{name} must be a 3-D tensor [total, heads, d]")
+        _check(t.unsqueeze(0), name)
+    H_kv = k.shape[1]
+    if tuple(k.shape) != (total, H_kv, d) or tuple(v.shape) != (total, H_kv, d):
+        raise ValueError(f"k and v must be [total, H_kv, d] = [{total}, {H_kv}, {d}]")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
+    if H_kv == 0 and H > 0 or H_kv > 0 and H % H_kv != 0:
+        raise ValueError(f"key/value heads ({H_kv}) must divide query heads ({H})")
+    if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32
+            or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device or cu_seqlens.numel() < 1):
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of B + 1 offsets on q's device")
+    cu = cu_seqlens.contiguous()
+    B = cu.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((total, H, d), dtype=torch.bfloat16, device=q.device)
+    else:
+        if not isinstance(out, torch.Tensor) or out.dim() != 3 or tuple(out.shape) != (total, H, d):
+            raise ValueError(f"out must be [total, H, d] = [{total}, {H}, {d}]")
+        _check(out.unsqueeze(0), "out", device=q.device)
+    lse = torch.empty((total, H), dtype=torch.float32, device=q.device) if return_lse else None
+    wl, wr = _window_args(window)
+    st = lambda t: (ctypes.c_int64 * 2)(*t.stride()[:2])
+    _call(_lib.load().attn_forward_varlen, q, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+          out.data_ptr(), lse.data_ptr() if lse is not None else None, cu.data_ptr(), B,
+          int(max_seqlen), total, H, H_kv, d, st(q), st(k), st(v), st(out), float(scale),
+          1 if causal else 0, wl, wr)
     return (out, lse) if return_lse else out
 
 

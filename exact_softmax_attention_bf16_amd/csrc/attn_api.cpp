@@ -222,7 +222,8 @@ int forward(const void* q, const void* k, const void* v, void* out, float* lse,
     const int64_t nqb = (L + 127) / 128;
     if (nqb * bh >= ((int64_t)1 << 31)) return ATTN_ERR_TOO_LARGE;
     const hipError_t e = timed(ATTN_KERNEL_ONLINE, stream, timing_on(), [&] {
-      return attn::launch_online(q, k, v, out, lse, hm, (int)bh, (int)L, (int)d, sl2, band, stream);
+      return attn::launch_online(q, k, v, out, lse, hm, (int)bh, (int)L, (int)d, sl2, band, nullptr,
+                                 0, stream);
     });
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
   }
@@ -385,6 +386,85 @@ int attn_forward_ex(const void* q, const void* k, const void* v, void* out, floa
   const int64_t ld_max = std::max(vq.st[2], std::max(vk.st[2], vv.st[2]));
   return forward(q, k, v, out, lse, hm, bh, L, d, ld_max, scale,
                  attn::make_band(window_left, window_right, causal != 0, L), stream);
+}
+
+int attn_forward_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                        const int32_t* cu_seqlens, int64_t B, int64_t max_seqlen, int64_t total,
+                        int64_t H, int64_t H_kv, int64_t d, const int64_t* q_strides,
+                        const int64_t* k_strides, const int64_t* v_strides,
+                        const int64_t* o_strides, float scale, int causal, int64_t window_left,
+                        int64_t window_right, hipStream_t stream) {
+  if (B < 0 || max_seqlen < 0 || total < 0 || H < 0 || H_kv < 0 || d < 0)
+    return ATTN_ERR_BAD_SHAPE;
+  if (window_left < -1 || window_right < -1) return ATTN_ERR_BAD_SHAPE;
+  int64_t rows = 0, elems = 0, bytes = 0, bh = 0, slots = 0;
+  if (__builtin_mul_overflow(total, H, &rows) || __builtin_mul_overflow(rows, d, &elems) ||
+      __builtin_mul_overflow(elems, (int64_t)2, &bytes) || __builtin_mul_overflow(B, H, &bh) ||
+      __builtin_mul_overflow(bh, max_seqlen, &slots))
+    return ATTN_ERR_BAD_SHAPE;
+  if (H > 0 && (H_kv < 1 || H % H_kv != 0)) return ATTN_ERR_BAD_SHAPE;
+  if (attn_path_for_head_dim(d) != ATTN_PATH_ONLINE) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+  if (rows == 0 || slots == 0) return ATTN_OK;
+  if (!q || !k || !v || !out || !cu_seqlens) return ATTN_ERR_NULL_PTR;
+
+  // Operands as [1, heads, total] views: strides {token, head} given, channels contiguous.
+  auto make = [&](const int64_t* st, int64_t heads) {
+    View w{{1, heads, total}, {0, d, heads * d}, d};
+    if (st) {
+      w.st[2] = st[0];
+      w.st[1] = st[1];
+    }
+    return w;
+  };
+  const View vq = make(q_strides, H), vk = make(k_strides, H_kv), vv = make(v_strides, H_kv),
+             vo = make(o_strides, H);
+  for (const View* w : {&vq, &vk, &vv, &vo}) {
+    if (!w->strides_valid()) return ATTN_ERR_BAD_STRIDE;
+    if (w->st[1] > (INT64_MAX / 8) / std::max<int64_t>(H, 1) ||
+        w->st[2] > (INT64_MAX / 8) / std::max<int64_t>(total, 1))
+      return ATTN_ERR_BAD_STRIDE;
+  }
+  if (!vo.one_to_one()) return ATTN_ERR_BAD_STRIDE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15 ||
+      ((uintptr_t)lse & 3) || ((uintptr_t)cu_seqlens & 3))
+    return ATTN_ERR_MISALIGNED;
+  const int64_t ob = vo.span() * 2, cb = (B + 1) * 4;
+  if (overlaps(out, ob, q, vq.span() * 2) || overlaps(out, ob, k, vk.span() * 2) ||
+      overlaps(out, ob, v, vv.span() * 2) || overlaps(out, ob, cu_seqlens, cb))
+    return ATTN_ERR_ALIAS;
+  if (lse) {
+    const int64_t lb = rows * 4;
+    if (overlaps(lse, lb, out, ob) || overlaps(lse, lb, q, vq.span() * 2) ||
+        overlaps(lse, lb, k, vk.span() * 2) || overlaps(lse, lb, v, vv.span() * 2) ||
+        overlaps(lse, lb, cu_seqlens, cb))
+      return ATTN_ERR_ALIAS;
+  }
+  // One sequence per 32-bit offsets (rows up to max_seqlen + 255 are formed),
+  // token indices and workgroup counts in int.
+  const int64_t ld_max = std::max(vq.st[2], std::max(vk.st[2], vv.st[2]));
+  for (const View* w : {&vq, &vk, &vv, &vo})
+    if (w->st[2] >= ((int64_t)1 << 30) || w->st[1] >= ((int64_t)1 << 30)) return ATTN_ERR_TOO_LARGE;
+  if (max_seqlen > ((int64_t)1 << 30) || total >= ((int64_t)1 << 31) - 1 ||
+      (max_seqlen + 256) * ld_max * 2 >= ((int64_t)1 << 31) || H >= ((int64_t)1 << 30) ||
+      (max_seqlen + 127) / 128 * bh >= ((int64_t)1 << 31))
+    return ATTN_ERR_TOO_LARGE;
+
+  attn::HeadMap hm;
+  hm.H = (int)H;
+  hm.group = (int)(H / H_kv);
+  hm.bh0 = 0;
+  hm.q = {0, vq.st[1], (int)vq.st[2]};
+  hm.k = {0, vk.st[1], (int)vk.st[2]};
+  hm.v = {0, vv.st[1], (int)vv.st[2]};
+  hm.o = {0, vo.st[1], (int)vo.st[2]};
+  const attn::Band band = attn::make_band(window_left, window_right, causal != 0, max_seqlen);
+  const float sl2 = scale * 1.4426950408889634f;
+  const hipError_t e = timed(ATTN_KERNEL_ONLINE, stream, timing_on(), [&] {
+    return attn::launch_online(q, k, v, out, lse, hm, (int)bh, (int)max_seqlen, (int)d, sl2, band,
+                               cu_seqlens, (int)total, stream);
+  });
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_timing_enable(int enable) {

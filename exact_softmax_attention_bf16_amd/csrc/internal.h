@@ -97,10 +97,13 @@ int64_t two_pass_head_bytes(const TwoPassDims& t);
 
 // Fused online-softmax kernel, d in {32, 64, 128}.  sl2 = scale * log2(e).
 // lse (may be null): fp32 [global head][L], the natural log of each row's
-// softmax denominator.
+// softmax denominator.  With cu non-null (device int32 [BH / hm.H + 1]) the
+// heads are sequences of different lengths packed along the tokens: sequence
+// b holds tokens [cu[b], cu[b + 1]) (clamped to [0, total]; length at most
+// L), rows hm.*.ld and heads hm.*.h elements apart, and lse is [total][H].
 hipError_t launch_online(const void* q, const void* k, const void* v, void* out, float* lse,
                          const HeadMap& hm, int BH, int L, int d, float sl2, const Band& band,
-                         hipStream_t s);
+                         const int* cu, int total, hipStream_t s);
 
 // Scores pass: per 256x256 (key, query) tile, E = bf16(2^(y - m)) with
 // y = sl2 * q.k, m = ceil(max over the tile's keys of y) per query, plus m and

@@ -32,8 +32,10 @@
 //     queries do not see, and loads past the end of a head return zero
 //     through the buffer resource bounds.
 //   * Heads are found through a HeadMap (any batch, head and row strides with
-//     contiguous channels; one key/value head per `group` query heads), and
-//     the merged (m, l) give each row's log-sum-exp when it is asked for.
+//     contiguous channels; one key/value head per `group` query heads), or,
+//     for a batch of sequences of different lengths packed along the tokens,
+//     through the sequence offsets (fmha.py's cum_seqlen); the merged (m, l)
+//     give each row's log-sum-exp when it is asked for.
 #include "device.h"
 #include "internal.h"
 
@@ -55,21 +57,27 @@ struct OnlineSmem {
   char vbuf[kGroups][2][VT_BYTES];
 };
 
-// PLAIN: q, k, v and out are contiguous [B, H, L, D] with one key/value head
-// per query head, so head bh starts at bh * L * D (no division by H, whose
-// expansion would sit ahead of the first load of this short kernel).
+// LAYOUT: where head bh's rows are.  kPlain: q, k, v and out contiguous
+// [B, H, L, D] with one key/value head per query head, so head bh starts at
+// bh * L * D (no division by H, whose expansion would sit ahead of the first
+// load of this short kernel).  kStrided: through the head map.  kVarlen:
+// sequences of different lengths packed along the token dimension; sequence
+// b = bh / H holds tokens [cu[b], cu[b + 1]) (clamped to [0, total], its length
+// to L), rows are hm.*.ld apart and heads hm.*.h apart.
+enum { kPlain = 0, kStrided = 1, kVarlen = 2 };
 // MASK: which keys below L each query i may see -- kAllKeys: all of them;
 // kCausal: j <= i; kWindow: i - left <= j <= i + right (band.left, band.right,
 // either side possibly unbounded).  Causal has its own instantiation so that
 // it carries no left-side tests.
 enum { kAllKeys = 0, kCausal = 1, kWindow = 2 };
-template <int D, int MASK, bool PLAIN>
+template <int D, int MASK, int LAYOUT>
 __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v,
                                                           uint16_t* __restrict__ out,
                                                           float* __restrict__ lse, HeadMap hm,
-                                                          int L, int nqb, float sl2, Band band) {
+                                                          int Lmax, int nqb, float sl2, Band band,
+                                                          const int* __restrict__ cu, int total) {
   constexpr int CPR = D / 8;                       // 16-byte chunks per K row
   constexpr int SWZ = (CPR >= 8 ? 8 : CPR) - 1;    // chunk-index bits that are swizzled
   constexpr int VROW = kBN * 2 + 8;                // bytes per V^T row: 64 keys + pad
@@ -99,12 +107,40 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   const int left = HAS_LEFT ? band.left : kNoLimit;
   const int right = MASK == kCausal ? 0 : band.right;
 
-  // Rows past L of each head read as zero: the resources end after row L - 1.
+  constexpr bool PLAIN = LAYOUT == kPlain;
   const int ldq = PLAIN ? D : hm.q.ld, ldk = PLAIN ? D : hm.k.ld, ldv = PLAIN ? D : hm.v.ld;
-  const int64_t plain_off = (int64_t)(hm.bh0 + bh) * L * D;
-  const auto rq = make_rsrc(q + (PLAIN ? plain_off : hm.q_off(bh)), ((uint32_t)(L - 1) * ldq + D) * 2);
-  const auto rk = make_rsrc(k + (PLAIN ? plain_off : hm.k_off(bh)), ((uint32_t)(L - 1) * ldk + D) * 2);
-  const auto rv = make_rsrc(v + (PLAIN ? plain_off : hm.v_off(bh)), ((uint32_t)(L - 1) * ldv + D) * 2);
+  const int ldo = PLAIN ? D : hm.o.ld;
+  // This head's row 0 in each operand (elements), its length, and where its
+  // log-sum-exp values go (lse_base + lse_step * query).
+  int L = Lmax;
+  int64_t qoff, koff, voff, ooff, lse_base;
+  int lse_step = 1;
+  if constexpr (LAYOUT == kVarlen) {
+    const int b = bh / hm.H, h = bh - b * hm.H;
+    const int start = min(max(cu[b], 0), total);
+    const int end = min(max(cu[b + 1], start), total);
+    L = min(end - start, Lmax);
+    if (qb * kBM >= L) return;  // the whole workgroup, before any barrier
+    qoff = (int64_t)start * ldq + (int64_t)h * hm.q.h;
+    koff = (int64_t)start * ldk + (int64_t)(h / hm.group) * hm.k.h;
+    voff = (int64_t)start * ldv + (int64_t)(h / hm.group) * hm.v.h;
+    ooff = (int64_t)start * ldo + (int64_t)h * hm.o.h;
+    lse_base = (int64_t)start * hm.H + h;  // lse is [total, H]
+    lse_step = hm.H;
+  } else if constexpr (PLAIN) {
+    qoff = koff = voff = ooff = (int64_t)(hm.bh0 + bh) * L * D;
+    lse_base = (int64_t)(hm.bh0 + bh) * L;
+  } else {
+    qoff = hm.q_off(bh);
+    koff = hm.k_off(bh);
+    voff = hm.v_off(bh);
+    ooff = hm.o_off(bh);
+    lse_base = (int64_t)(hm.bh0 + bh) * L;
+  }
+  // Rows past L of each head read as zero: the resources end after row L - 1.
+  const auto rq = make_rsrc(q + qoff, ((uint32_t)(L - 1) * ldq + D) * 2);
+  const auto rk = make_rsrc(k + koff, ((uint32_t)(L - 1) * ldk + D) * 2);
+  const auto rv = make_rsrc(v + voff, ((uint32_t)(L - 1) * ldv + D) * 2);
 
   const int q0 = qb * kBM + wave * 32;  // first query of this wave
   const int myq = q0 + c32;             // this lane's query
@@ -317,10 +353,10 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   }
   // The row's softmax denominator is sum_j 2^(y_j) = 2^m * lsum (y in log2 units).
   if (lse != nullptr && myq < L && h == 0)
-    lse[(size_t)(hm.bh0 + bh) * L + myq] = (m + log2f(lsum)) * 0.6931471805599453f;
+    lse[lse_base + (int64_t)lse_step * myq] = (m + log2f(lsum)) * 0.6931471805599453f;
   const float inv = 1.f / lsum;
   if (myq < L) {
-    uint16_t* orow = out + (PLAIN ? plain_off + (int64_t)myq * D : hm.o_off(bh) + (int64_t)myq * hm.o.ld);
+    uint16_t* orow = out + ooff + (int64_t)myq * ldo;
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
 #pragma unroll
@@ -333,43 +369,51 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   }
 }
 
-template <int D, int MASK, bool PLAIN>
+template <int D, int MASK, int LAYOUT>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* out, float* lse,
-                      HeadMap hm, int BH, int L, float sl2, Band band, hipStream_t s) {
+                      HeadMap hm, int BH, int L, float sl2, Band band, const int* cu, int total,
+                      hipStream_t s) {
   const int nqb = (L + kBM - 1) / kBM;
   const dim3 grid((unsigned)(nqb * BH)), block(64 * kWaves);
   const uint16_t* qp = (const uint16_t*)q;
   const uint16_t* kp = (const uint16_t*)k;
   const uint16_t* vp = (const uint16_t*)v;
   uint16_t* op = (uint16_t*)out;
-  void* args[] = {&qp, &kp, &vp, &op, &lse, &hm, &L, (void*)&nqb, &sl2, &band};
-  return hipLaunchKernel((const void*)&online_attn_kernel<D, MASK, PLAIN>, grid, block, args, 0, s);
+  void* args[] = {&qp, &kp, &vp, &op, &lse, &hm, &L, (void*)&nqb, &sl2, &band, &cu, &total};
+  return hipLaunchKernel((const void*)&online_attn_kernel<D, MASK, LAYOUT>, grid, block, args, 0, s);
 }
 
 template <int D, int MASK>
 hipError_t launch_m(const void* q, const void* k, const void* v, void* out, float* lse,
-                    const HeadMap& hm, int BH, int L, float sl2, Band band, hipStream_t s) {
-  return is_plain(hm, L, D) ? launch_one<D, MASK, true>(q, k, v, out, lse, hm, BH, L, sl2, band, s)
-                            : launch_one<D, MASK, false>(q, k, v, out, lse, hm, BH, L, sl2, band, s);
+                    const HeadMap& hm, int BH, int L, float sl2, Band band, const int* cu,
+                    int total, hipStream_t s) {
+  if (cu != nullptr)
+    return launch_one<D, MASK, kVarlen>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
+  if (is_plain(hm, L, D))
+    return launch_one<D, MASK, kPlain>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
+  return launch_one<D, MASK, kStrided>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
 }
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* out, float* lse,
-                    const HeadMap& hm, int BH, int L, float sl2, Band band, hipStream_t s) {
-  if (band_is_full(band)) return launch_m<D, kAllKeys>(q, k, v, out, lse, hm, BH, L, sl2, band, s);
-  if (band_is_causal(band)) return launch_m<D, kCausal>(q, k, v, out, lse, hm, BH, L, sl2, band, s);
-  return launch_m<D, kWindow>(q, k, v, out, lse, hm, BH, L, sl2, band, s);
+                    const HeadMap& hm, int BH, int L, float sl2, Band band, const int* cu,
+                    int total, hipStream_t s) {
+  if (band_is_full(band))
+    return launch_m<D, kAllKeys>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
+  if (band_is_causal(band))
+    return launch_m<D, kCausal>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
+  return launch_m<D, kWindow>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
 }
 
 }  // namespace
 
 hipError_t launch_online(const void* q, const void* k, const void* v, void* out, float* lse,
                          const HeadMap& hm, int BH, int L, int d, float sl2, const Band& band,
-                         hipStream_t s) {
+                         const int* cu, int total, hipStream_t s) {
   switch (d) {
-    case 32: return launch_d<32>(q, k, v, out, lse, hm, BH, L, sl2, band, s);
-    case 64: return launch_d<64>(q, k, v, out, lse, hm, BH, L, sl2, band, s);
-    case 128: return launch_d<128>(q, k, v, out, lse, hm, BH, L, sl2, band, s);
+    case 32: return launch_d<32>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
+    case 64: return launch_d<64>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
+    case 128: return launch_d<128>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -136,6 +136,45 @@ int attn_forward_ex(const void* q, const void* k, const void* v, void* out, floa
                     float scale, int causal, int64_t window_left, int64_t window_right,
                     hipStream_t stream);
 
+/*
+ * attn_forward_varlen -- a batch of sequences of different lengths packed
+ * along one token dimension (cuDNN native_sparse_attention fmha.py, __call__:
+ * cum_seqlen_q / cum_seqlen_k, and the epilogue's LSE store at
+ * row + cum_seqlen).  Each sequence attends to itself only.
+ *
+ *   q, out        : [total, H, d] views; k, v : [total, H_kv, d] views.  Each is
+ *                   a device pointer to element [0,0,0] plus two element strides
+ *                   (token, head) in a host array of 2 int64_t; NULL means packed
+ *                   ({heads*d, d}).  Channels contiguous; strides >= 0 and
+ *                   multiples of 8, token strides >= d; out one to one.
+ *   lse           : NULL, or a device pointer to fp32 [total, H] contiguous, as
+ *                   for attn_forward_ex (per token and head).
+ *   cu_seqlens    : device pointer to B + 1 int32 offsets: sequence b is tokens
+ *                   [cu_seqlens[b], cu_seqlens[b + 1]).  The caller guarantees
+ *                   0 <= cu_seqlens[b] <= cu_seqlens[b + 1] <= total and that no
+ *                   sequence is longer than max_seqlen; the kernels clamp every
+ *                   sequence to [0, total] and max_seqlen tokens, so accesses
+ *                   stay inside the views whatever the array holds.  Tokens in
+ *                   no sequence are neither read as queries nor written.
+ *   B, max_seqlen : sequences, and the longest one's length (sizes the grid).
+ *   total         : tokens in the views.
+ *   H, H_kv, d, scale, causal, window_left, window_right, stream : as for
+ *                   attn_forward_ex, positions counted within each sequence;
+ *                   d must be 32, 64 or 128 (the head dims fmha.py's interface
+ *                   takes), else ATTN_ERR_UNSUPPORTED_HEAD_DIM.
+ *
+ * No workspace.  out must not overlap q, k, v or cu_seqlens (address ranges),
+ * nor lse any of them.  Returns ATTN_OK (also when nothing is to be done:
+ * B, H, max_seqlen or total zero) or a status code.
+ */
+int attn_forward_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                        const int32_t* cu_seqlens, int64_t B, int64_t max_seqlen, int64_t total,
+                        int64_t H, int64_t H_kv, int64_t d,
+                        const int64_t* q_strides, const int64_t* k_strides,
+                        const int64_t* v_strides, const int64_t* o_strides,
+                        float scale, int causal, int64_t window_left, int64_t window_right,
+                        hipStream_t stream);
+
 /* Static English text for a status code (never NULL). */
 const char* attn_status_string(int status);
 

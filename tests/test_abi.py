@@ -16,6 +16,14 @@ from exact_softmax_attention_bf16_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
+# These calls pass fake device addresses and rely on a host check refusing each
+# one before any launch; where a GPU is visible a mistake in a test would send
+# them to a kernel, so the module runs only on GPU-less hosts.
+import torch  # noqa: E402
+if torch.cuda.device_count() > 0:
+    pytest.skip("host-side ABI checks with fake addresses run on GPU-less hosts",
+                allow_module_level=True)
+
 A = 0x7F0000000000          # fake, 16-byte aligned device addresses (never touched)
 MB = 1 << 20
 
@@ -33,7 +41,8 @@ def fwd(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, B=1, H=1, L=16, d=
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == sorted(["attn_forward", "attn_forward_ex", "attn_status_string",
+    assert names == sorted(["attn_forward", "attn_forward_ex", "attn_forward_varlen",
+                            "attn_status_string",
                             "attn_path_for_head_dim", "attn_workspace_bytes",
                             "attn_timing_enable", "attn_timing_collect"])
     assert set(names) == set(_lib.SIGNATURES)
@@ -316,3 +325,52 @@ def test_ex_window_is_accepted():
     for wl, wr in [(0, 0), (5, -1), (-1, 7), (L + 5, L + 5)]:
         assert fwd_ex(q=A, k=A + n, v=A + 2 * n, out=A + 3 * n, L=L, wl=wl, wr=wr,
                       qs=st(L * 128, L * 128, 128)) == _lib.ATTN_ERR_TOO_LARGE
+
+
+# ---- attn_forward_varlen: token-packed sequences of different lengths ----------
+
+def st2(*x):
+    return (ctypes.c_int64 * 2)(*x)
+
+
+def fwd_var(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, lse=None, cu=A + 256 * MB,
+            B=2, max_seqlen=16, total=32, H=1, H_kv=1, d=64, qs=None, ks=None, vs=None, os_=None,
+            scale=0.125, causal=0, wl=-1, wr=-1):
+    return _lib.load().attn_forward_varlen(q, k, v, out, lse, cu, B, max_seqlen, total, H, H_kv, d,
+                                           qs, ks, vs, os_, scale, causal, wl, wr, None)
+
+
+def test_varlen_nothing_to_do():
+    for kw in [dict(B=0), dict(total=0), dict(max_seqlen=0), dict(H=0, H_kv=0)]:
+        assert fwd_var(cu=None, **kw) == _lib.ATTN_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), "BAD_SHAPE"), (dict(max_seqlen=-1), "BAD_SHAPE"), (dict(total=-3), "BAD_SHAPE"),
+    (dict(H=4, H_kv=3), "BAD_SHAPE"), (dict(wl=-2), "BAD_SHAPE"),
+    (dict(d=256), "UNSUPPORTED_HEAD_DIM"), (dict(d=48), "UNSUPPORTED_HEAD_DIM"),
+    (dict(scale=float("nan")), "BAD_SCALE"), (dict(cu=None), "NULL_PTR"), (dict(q=None), "NULL_PTR"),
+    (dict(qs=st2(60, 64)), "BAD_STRIDE"), (dict(ks=st2(32, 64)), "BAD_STRIDE"),
+    (dict(H=2, H_kv=2, os_=st2(64, 0)), "BAD_STRIDE"),
+    (dict(cu=A + 256 * MB + 2), "MISALIGNED"), (dict(lse=A + 300 * MB + 1), "MISALIGNED"),
+    (dict(out=A + 8), "MISALIGNED"),
+    (dict(cu=A + 192 * MB + 64), "ALIAS"), (dict(lse=A + 192 * MB), "ALIAS"),
+    (dict(out=A + 64), "ALIAS"),
+])
+def test_varlen_checks(kw, code):
+    assert fwd_var(**kw) == getattr(_lib, "ATTN_ERR_" + code)
+
+
+def test_varlen_layouts_are_accepted():
+    # [total, H, d] packed, and q/k/v inside one [total, 3, H, d] tensor; a row
+    # stride too wide for 32-bit offsets shows every earlier check passed
+    big, T = 1 << 22, 1 << 40
+    assert fwd_var(q=A, k=A + T, v=A + 2 * T, out=A + 3 * T, cu=A + 4 * T, total=1024,
+                   max_seqlen=1024, H=2, H_kv=2, qs=st2(big, 64), ks=st2(big, 64),
+                   vs=st2(big, 64)) == _lib.ATTN_ERR_TOO_LARGE
+    H, d = 2, 64
+    row = 3 * H * d
+    span = 1024 * row * 2
+    assert fwd_var(q=A, k=A + H * d * 2, v=A + 2 * H * d * 2, out=A + span, cu=A + 2 * span,
+                   total=1024, max_seqlen=1 << 22, H=H, H_kv=H, qs=st2(row, d), ks=st2(row, d),
+                   vs=st2(row, d)) == _lib.ATTN_ERR_TOO_LARGE

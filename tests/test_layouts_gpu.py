@@ -1,6 +1,7 @@
-"""GPU parity for attn_forward_ex: packed and permuted layouts read in place,
-grouped key/value heads, sliding windows and the log-sum-exp output, against
-the float64 oracle.
+"""GPU parity for attn_forward_ex and attn_forward_varlen: packed and permuted
+layouts read in place, grouped key/value heads, sliding windows, token-packed
+sequences of different lengths and the log-sum-exp output, against the float64
+oracle.
 
 Output bar as in test_parity_gpu.py.  LSE bar, from the arithmetic: the kernels
 sum the bf16-rounded exponentials they multiply (bf16 keeps 8 significant
@@ -271,3 +272,85 @@ def test_window_on_packed_grouped_strided_inputs():
     ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1.0 / math.sqrt(d), True, (40, 90))
     ok, a, r = within_bar(to_f64(o), ref)
     assert ok, (a, r)
+
+
+# ---- token-packed sequences of different lengths ----------------------------------
+
+def varlen_batch(lengths, H, H_kv, d, seed, lead=0, tail=0):
+    """Per-sequence inputs [1, heads, L, d] and their token-packed [total, heads, d]
+    form; `lead` / `tail` tokens before the first and after the last sequence."""
+    seqs = []
+    for i, L in enumerate(lengths):
+        q = make_qkv(1, H, L, d, seed + 2 * i)[0]
+        _, k, v = make_qkv(1, H_kv, L, d, seed + 2 * i + 1)
+        seqs.append((q, k, v))
+    def pack(j, heads):
+        parts = [torch.zeros(lead, heads, d, dtype=torch.bfloat16)]
+        parts += [s[j][0].transpose(0, 1) for s in seqs]
+        parts += [torch.zeros(tail, heads, d, dtype=torch.bfloat16)]
+        return torch.cat(parts, dim=0).contiguous()
+    cu = torch.tensor([lead] + list(lead + np.cumsum(lengths)), dtype=torch.int32)
+    return seqs, pack(0, H), pack(1, H_kv), pack(2, H_kv), cu
+
+
+def check_varlen(seqs, o, lse, cu, s, causal, window):
+    worst = (0.0, 0.0)
+    for i, (q, k, v) in enumerate(seqs):
+        a0, a1 = int(cu[i]), int(cu[i + 1])
+        if a1 == a0:
+            continue  # an empty sequence: nothing to compare
+        got = o[a0:a1].transpose(0, 1).unsqueeze(0)
+        ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), s, causal, window)
+        ok, a, r = within_bar(to_f64(got), ref)
+        assert ok, (i, a, r)
+        worst = (max(worst[0], a), max(worst[1], r))
+        if lse is not None:
+            ok, err = lse_ok(lse[a0:a1].transpose(0, 1).unsqueeze(0),
+                             oracle.log_sum_exp(to_f64(q), to_f64(k), s, causal, window))
+            assert ok, (i, err)
+    return worst
+
+
+LENGTHS = [1, 300, 17, 129, 0, 1000, 64]
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("H,H_kv", [(4, 4), (4, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [None, (50, 10)])
+def test_varlen(d, H, H_kv, causal, window):
+    from exact_softmax_attention_bf16_amd import attention_varlen
+    seqs, q, k, v, cu = varlen_batch(LENGTHS, H, H_kv, d, 200 + d)
+    s = 1.0 / math.sqrt(d)
+    o, lse = attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), max(LENGTHS), scale=s,
+                              causal=causal, window=window, return_lse=True)
+    torch.cuda.synchronize()
+    a, r = check_varlen(seqs, o.cpu(), lse.cpu(), cu, s, causal, window)
+    _report(f"varlen d={d} H={H}/{H_kv} causal={causal} window={window}", a, r)
+
+
+def test_varlen_tokens_outside_sequences_untouched_and_strided():
+    """Sequences start after 40 unused tokens and end 24 before the last; q, k, v
+    are views into one [total, 3, H, d] tensor; out keeps its other rows."""
+    from exact_softmax_attention_bf16_amd import attention_varlen
+    H, d = 2, 64
+    seqs, q, k, v, cu = varlen_batch([200, 77, 513], H, H, d, 230, lead=40, tail=24)
+    packed = torch.stack([q, k, v], dim=1).to(DEV)  # [total, 3, H, d]
+    total = q.shape[0]
+    out = torch.full((total, H, d), 3.0, dtype=torch.bfloat16, device=DEV)
+    o = attention_varlen(packed[:, 0], packed[:, 1], packed[:, 2], cu.to(DEV), 600, out=out)
+    torch.cuda.synchronize()
+    assert bool((o[:40] == 3.0).all()) and bool((o[total - 24:] == 3.0).all())
+    check_varlen(seqs, o.cpu(), None, cu, 1.0 / math.sqrt(d), False, None)
+
+
+def test_varlen_equals_separate_calls_bitwise():
+    """Each sequence of a varlen call equals attention() on that sequence alone."""
+    from exact_softmax_attention_bf16_amd import attention, attention_varlen
+    H, d = 4, 128
+    seqs, q, k, v, cu = varlen_batch([333, 128, 5], H, H, d, 240)
+    o = attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), 333, causal=True)
+    for i, (qs, ks, vs) in enumerate(seqs):
+        ref = attention(qs.to(DEV), ks.to(DEV), vs.to(DEV), causal=True)
+        got = o[int(cu[i]):int(cu[i + 1])].transpose(0, 1).unsqueeze(0)
+        assert torch.equal(got, ref), i

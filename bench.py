@@ -19,6 +19,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -40,11 +41,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_text(text: str) -> str:
+    """Kernel source with comments and blank lines removed (a comment edit does
+    not change the kernel the counters measured)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(KERNEL_SOURCES, "*"))):
         if p.endswith((".hip", ".h", ".cpp")):
-            h.update(open(p, "rb").read())
+            h.update(code_text(open(p).read()).encode())
     return h.hexdigest()
 
 

@@ -25,6 +25,11 @@
 // attn.cu row_softmax_kernel and of the FMHA example's softmax_step; the
 // rescale by 2^(m_t - M) is that example's correction step, done once per
 // tile with exact factors.
+//
+// Masks are bands of keys per query (causal, or a sliding window): both passes
+// visit only the tiles a query tile's band meets.  Operands are found through
+// a head map (strides, key/value head groups), so packed and strided layouts
+// are read in place.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -141,11 +146,12 @@ __device__ __forceinline__ bool scores_tile_unmasked(const ScoresTile& t, const 
 
 // True when every score of this wave's block in the tile is discarded: its keys
 // or its queries all lie past L, or all its keys lie outside all its queries'
-// bands (e.g. causal: all its keys follow all its queries).  Such a wave issues its share of the loads and meets every barrier
-// but skips its fragment reads and MFMAs, and enters the epilogue with zero
-// accumulators, none of which reach memory: keys past L or after the query are
-// selected away, and rows past L are not stored (their maxima and sums are
-// exchanged only with the partner wave holding the same rows).
+// bands (e.g. causal: all its keys follow all its queries).  Such a wave issues
+// its share of the loads and meets every barrier but skips its fragment reads
+// and MFMAs, and enters the epilogue with zero accumulators, none of which
+// reach memory: keys past L or outside the band are selected away, and rows
+// past L are not stored (their maxima and sums are exchanged only with the
+// partner wave holding the same rows).
 __device__ __forceinline__ bool scores_wave_idle(const ScoresTile& t, int wave, int L,
                                                  const Band& band) {
   const int key0 = t.kt * kTile + scores_key_half(wave) * 128;

@@ -28,7 +28,7 @@ ATTN_PATH_NONE = -1
 ATTN_PATH_ONLINE = 0
 ATTN_PATH_TWO_PASS = 1
 
-KERNEL_NAMES = ("online", "scores", "values", "values_reduce")
+KERNEL_NAMES = ("online", "scores", "values", "values_reduce", "online_combine")
 
 # Every symbol include/attn.h declares, with its ctypes signature.
 SIGNATURES = {

@@ -50,6 +50,12 @@ int64_t two_pass_workspace_bytes(int64_t BH, const attn::TwoPassDims& t, const a
   return std::max(chunk_workspace_bytes(chunk, t, band), chunk_workspace_bytes(last, t, band));
 }
 
+// Online path: fp32 shares of O and their (m, l) when the keys are split.
+int64_t online_workspace_bytes(int64_t BH, int64_t L, int64_t d) {
+  const int n = attn::online_split(BH, L, (int)d);
+  return n > 1 ? round256((int64_t)n * BH * L * (d + 2) * 4) : 0;
+}
+
 bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
   const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
   return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
@@ -220,12 +226,28 @@ int forward(const void* q, const void* k, const void* v, void* out, float* lse,
 
   if (attn_path_for_head_dim(d) == ATTN_PATH_ONLINE) {
     const int64_t nqb = (L + 127) / 128;
-    if (nqb * bh >= ((int64_t)1 << 31)) return ATTN_ERR_TOO_LARGE;
-    const hipError_t e = timed(ATTN_KERNEL_ONLINE, stream, timing_on(), [&] {
+    const int nsplit = attn::online_split(bh, L, (int)d);
+    if (nqb * bh * nsplit >= ((int64_t)1 << 31)) return ATTN_ERR_TOO_LARGE;
+    const bool on = timing_on();
+    attn::KeySplit ks{nullptr, nullptr, 1, (int)bh};
+    Workspace* wsp = nullptr;
+    if (nsplit > 1) {  // few heads: the keys of each query block are split
+      if (acquire_workspace(stream, (size_t)online_workspace_bytes(bh, L, d), &wsp) != hipSuccess)
+        return ATTN_ERR_WORKSPACE;
+      ks.part = (float*)wsp->ptr;
+      ks.stats = ks.part + (size_t)nsplit * bh * L * d;
+      ks.n = nsplit;
+    }
+    hipError_t e = timed(ATTN_KERNEL_ONLINE, stream, on, [&] {
       return attn::launch_online(q, k, v, out, lse, hm, (int)bh, (int)L, (int)d, sl2, band, nullptr,
-                                 0, stream);
+                                 0, ks, stream);
     });
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    if (e == hipSuccess && nsplit > 1)
+      e = timed(ATTN_KERNEL_ONLINE_COMBINE, stream, on, [&] {
+        return attn::launch_online_combine(ks, out, lse, hm, (int)L, (int)d, stream);
+      });
+    const hipError_t rerr = wsp ? release_workspace(stream, wsp) : hipSuccess;
+    return e == hipSuccess && rerr == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
   }
   const attn::TwoPassDims t = attn::two_pass_dims(L, d);
   // E rows are addressed up to (L + 255) * Ls * 2 bytes inside a head.
@@ -298,9 +320,10 @@ int attn_path_for_head_dim(int64_t d) {
 }
 
 int64_t attn_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int causal) {
-  if (B < 0 || H < 0 || L < 0 || attn_path_for_head_dim(d) != ATTN_PATH_TWO_PASS) return 0;
+  if (B < 0 || H < 0 || L < 0 || attn_path_for_head_dim(d) == ATTN_PATH_NONE) return 0;
   if (B == 0 || H == 0 || L == 0) return 0;
   if (L > (int64_t)1 << 20) return 0;
+  if (attn_path_for_head_dim(d) == ATTN_PATH_ONLINE) return online_workspace_bytes(B * H, L, d);
   const attn::TwoPassDims t = attn::two_pass_dims(L, d);
   return two_pass_workspace_bytes(B * H, t, attn::make_band(-1, -1, causal != 0, L));
 }
@@ -462,7 +485,8 @@ int attn_forward_varlen(const void* q, const void* k, const void* v, void* out, 
   const float sl2 = scale * 1.4426950408889634f;
   const hipError_t e = timed(ATTN_KERNEL_ONLINE, stream, timing_on(), [&] {
     return attn::launch_online(q, k, v, out, lse, hm, (int)bh, (int)max_seqlen, (int)d, sl2, band,
-                               cu_seqlens, (int)total, stream);
+                               cu_seqlens, (int)total, attn::KeySplit{nullptr, nullptr, 1, (int)bh},
+                               stream);
   });
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }

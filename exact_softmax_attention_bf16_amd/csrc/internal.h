@@ -95,15 +95,33 @@ constexpr int kTwoPassMaxTiles = 124;
 // per-(tile, query) exponent reference and partial sum.
 int64_t two_pass_head_bytes(const TwoPassDims& t);
 
+// A split of each query block's keys among n workgroups (n > 1): share s of
+// head h writes its unnormalised O to part[s][h][L][d] and its (m, l) to
+// stats[s][h][L][2] (fp32); the combine kernel merges the shares.
+struct KeySplit {
+  float* part;
+  float* stats;
+  int n;      // shares per query block (<= 1: no split)
+  int heads;  // heads of the launch
+};
+constexpr int kOnlineMaxSplit = 8;
+
 // Fused online-softmax kernel, d in {32, 64, 128}.  sl2 = scale * log2(e).
 // lse (may be null): fp32 [global head][L], the natural log of each row's
 // softmax denominator.  With cu non-null (device int32 [BH / hm.H + 1]) the
 // heads are sequences of different lengths packed along the tokens: sequence
 // b holds tokens [cu[b], cu[b + 1]) (clamped to [0, total]; length at most
 // L), rows hm.*.ld and heads hm.*.h elements apart, and lse is [total][H].
+// With ks.n > 1 (never with cu) it writes the shares instead of out and lse,
+// and launch_online_combine finishes the call.
 hipError_t launch_online(const void* q, const void* k, const void* v, void* out, float* lse,
                          const HeadMap& hm, int BH, int L, int d, float sl2, const Band& band,
-                         const int* cu, int total, hipStream_t s);
+                         const int* cu, int total, const KeySplit& ks, hipStream_t s);
+hipError_t launch_online_combine(const KeySplit& ks, void* out, float* lse, const HeadMap& hm,
+                                 int L, int d, hipStream_t s);
+// Shares per query block for BH heads of length L: 1 unless the unsplit grid
+// would leave at least half of the compute units idle.  Shape only.
+int online_split(int64_t BH, int64_t L, int d);
 
 // Scores pass: per 256x256 (key, query) tile, E = bf16(2^(y - m)) with
 // y = sl2 * q.k, m = ceil(max over the tile's keys of y) per query, plus m and

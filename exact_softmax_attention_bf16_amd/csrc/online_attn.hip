@@ -36,6 +36,8 @@
 //     for a batch of sequences of different lengths packed along the tokens,
 //     through the sequence offsets (fmha.py's cum_seqlen); the merged (m, l)
 //     give each row's log-sum-exp when it is asked for.
+#include <algorithm>
+
 #include "device.h"
 #include "internal.h"
 
@@ -77,7 +79,8 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
                                                           uint16_t* __restrict__ out,
                                                           float* __restrict__ lse, HeadMap hm,
                                                           int Lmax, int nqb, float sl2, Band band,
-                                                          const int* __restrict__ cu, int total) {
+                                                          const int* __restrict__ cu, int total,
+                                                          KeySplit ks) {
   constexpr int CPR = D / 8;                       // 16-byte chunks per K row
   constexpr int SWZ = (CPR >= 8 ? 8 : CPR) - 1;    // chunk-index bits that are swizzled
   constexpr int VROW = kBN * 2 + 8;                // bytes per V^T row: 64 keys + pad
@@ -99,7 +102,11 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   auto& kbuf = smem.kbuf[g];
   auto& vbuf = smem.vbuf[g];
 
-  const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  // Workgroup = (head, query block, key split); the splits of one block are
+  // neighbours, so they run on one XCD and share its L2.
+  const uint32_t lid0 = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int split = ks.n > 1 ? (int)(lid0 % (uint32_t)ks.n) : 0;
+  const uint32_t lid = ks.n > 1 ? lid0 / (uint32_t)ks.n : lid0;
   const int bh = lid / nqb;
   int qb = lid % nqb;
   if (MASK == kCausal) qb = nqb - 1 - qb;  // the longest rows start first
@@ -154,8 +161,13 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   // Key blocks t0 .. t0 + ntiles - 1 meet the band of this workgroup's queries.
   const int kstart = HAS_LEFT ? max(0, qb * kBM - left) : 0;
   const int kend = BANDED ? min(L, qb * kBM + kBM + right) : L;
-  const int t0 = kstart / kBN;
-  const int ntiles = (kend + kBN - 1) / kBN - t0;
+  int t0 = kstart / kBN;
+  int ntiles = (kend + kBN - 1) / kBN - t0;
+  if (ks.n > 1) {  // this split's share of those blocks (possibly none)
+    const int a = t0 + ntiles * split / ks.n, b = t0 + ntiles * (split + 1) / ks.n;
+    t0 = a;
+    ntiles = b - a;
+  }
 
   auto issue_k = [&](int t, int buf) {
 #pragma unroll
@@ -351,6 +363,22 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
         o[c][j] = a0 * o[c][j] + a1 * xo[((wave * NCB + c) * 16 + j) * 64 + lane];
     m = M;
   }
+  if (ks.n > 1) {
+    // A key split: this share's unnormalised O, m and l for the combine kernel
+    // (m = -inf, l = 0 where the share holds no key the query sees).
+    if (myq < L) {
+      const size_t row = ((size_t)split * ks.heads + bh) * L + myq;
+      float* po = ks.part + row * D;
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *(f32x4*)(po + c * 32 + 8 * i + 4 * h) =
+              f32x4{o[c][4 * i], o[c][4 * i + 1], o[c][4 * i + 2], o[c][4 * i + 3]};
+      if (h == 0) *(f32x2*)(ks.stats + 2 * row) = f32x2{m, lsum};
+    }
+    return;
+  }
   // The row's softmax denominator is sum_j 2^(y_j) = 2^m * lsum (y in log2 units).
   if (lse != nullptr && myq < L && h == 0)
     lse[lse_base + (int64_t)lse_step * myq] = (m + log2f(lsum)) * 0.6931471805599453f;
@@ -369,53 +397,113 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   }
 }
 
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the key splits
+// (M = max_s m_s), rounded once to bf16; one thread per (head, row, 8 channels).
+template <int D>
+__global__ __launch_bounds__(256) void online_combine_kernel(KeySplit ks, uint16_t* __restrict__ out,
+                                                             float* __restrict__ lse, HeadMap hm,
+                                                             int L) {
+  constexpr int C8 = D / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)ks.heads * L * C8) return;
+  const int chunk = (int)(i % C8);
+  const int64_t rowall = i / C8;  // head * L + row
+  const int bh = (int)(rowall / L), row = (int)(rowall - (int64_t)bh * L);
+  const size_t plane = (size_t)ks.heads * L;  // rows per split
+  float M = -INFINITY;
+  for (int sp = 0; sp < ks.n; ++sp) M = fmaxf(M, ks.stats[2 * (sp * plane + rowall)]);
+  float den = 0.f;
+  f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < ks.n; ++sp) {
+    const size_t r = sp * plane + rowall;
+    const f32x2 ml = *(const f32x2*)(ks.stats + 2 * r);
+    const float w = ml[0] == -INFINITY ? 0.f : exp2_fast(ml[0] - M);
+    den += w * ml[1];
+    const f32x4* p = (const f32x4*)(ks.part + r * D + 8 * chunk);
+    a += w * p[0];
+    b += w * p[1];
+  }
+  const float inv = 1.f / den;
+  const u32x4 wds = {pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv),
+                     pack_bf16x2(b[0] * inv, b[1] * inv), pack_bf16x2(b[2] * inv, b[3] * inv)};
+  *(u32x4*)(out + hm.o_off(bh) + (int64_t)row * hm.o.ld + 8 * chunk) = wds;
+  if (lse != nullptr && chunk == 0)
+    lse[(int64_t)(hm.bh0 + bh) * L + row] = (M + log2f(den)) * 0.6931471805599453f;
+}
+
 template <int D, int MASK, int LAYOUT>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* out, float* lse,
                       HeadMap hm, int BH, int L, float sl2, Band band, const int* cu, int total,
-                      hipStream_t s) {
+                      KeySplit ks, hipStream_t s) {
   const int nqb = (L + kBM - 1) / kBM;
-  const dim3 grid((unsigned)(nqb * BH)), block(64 * kWaves);
+  const dim3 grid((unsigned)(nqb * BH * (ks.n > 1 ? ks.n : 1))), block(64 * kWaves);
   const uint16_t* qp = (const uint16_t*)q;
   const uint16_t* kp = (const uint16_t*)k;
   const uint16_t* vp = (const uint16_t*)v;
   uint16_t* op = (uint16_t*)out;
-  void* args[] = {&qp, &kp, &vp, &op, &lse, &hm, &L, (void*)&nqb, &sl2, &band, &cu, &total};
+  void* args[] = {&qp, &kp, &vp, &op, &lse, &hm, &L, (void*)&nqb, &sl2, &band, &cu, &total, &ks};
   return hipLaunchKernel((const void*)&online_attn_kernel<D, MASK, LAYOUT>, grid, block, args, 0, s);
 }
 
 template <int D, int MASK>
 hipError_t launch_m(const void* q, const void* k, const void* v, void* out, float* lse,
                     const HeadMap& hm, int BH, int L, float sl2, Band band, const int* cu,
-                    int total, hipStream_t s) {
+                    int total, KeySplit ks, hipStream_t s) {
   if (cu != nullptr)
-    return launch_one<D, MASK, kVarlen>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
+    return launch_one<D, MASK, kVarlen>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
   if (is_plain(hm, L, D))
-    return launch_one<D, MASK, kPlain>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
-  return launch_one<D, MASK, kStrided>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
+    return launch_one<D, MASK, kPlain>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
+  return launch_one<D, MASK, kStrided>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
 }
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* out, float* lse,
                     const HeadMap& hm, int BH, int L, float sl2, Band band, const int* cu,
-                    int total, hipStream_t s) {
+                    int total, KeySplit ks, hipStream_t s) {
   if (band_is_full(band))
-    return launch_m<D, kAllKeys>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
+    return launch_m<D, kAllKeys>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
   if (band_is_causal(band))
-    return launch_m<D, kCausal>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
-  return launch_m<D, kWindow>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
+    return launch_m<D, kCausal>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
+  return launch_m<D, kWindow>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
 }
 
 }  // namespace
 
 hipError_t launch_online(const void* q, const void* k, const void* v, void* out, float* lse,
                          const HeadMap& hm, int BH, int L, int d, float sl2, const Band& band,
-                         const int* cu, int total, hipStream_t s) {
+                         const int* cu, int total, const KeySplit& ks, hipStream_t s) {
   switch (d) {
-    case 32: return launch_d<32>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
-    case 64: return launch_d<64>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
-    case 128: return launch_d<128>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, s);
+    case 32: return launch_d<32>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
+    case 64: return launch_d<64>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
+    case 128: return launch_d<128>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_online_combine(const KeySplit& ks, void* out, float* lse, const HeadMap& hm,
+                                 int L, int d, hipStream_t s) {
+  const int64_t n = (int64_t)ks.heads * L * (d / 8);
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  KeySplit k = ks;
+  HeadMap m = hm;
+  uint16_t* op = (uint16_t*)out;
+  void* args[] = {&k, &op, &lse, &m, &L};
+  switch (d) {
+    case 32: return hipLaunchKernel((const void*)&online_combine_kernel<32>, grid, block, args, 0, s);
+    case 64: return hipLaunchKernel((const void*)&online_combine_kernel<64>, grid, block, args, 0, s);
+    case 128: return hipLaunchKernel((const void*)&online_combine_kernel<128>, grid, block, args, 0, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int online_split(int64_t BH, int64_t L, int d) {
+  const int64_t wgs = BH * ((L + kBM - 1) / kBM);  // workgroups without a split
+  if (wgs * 2 > kValuesTargetWorkgroups) return 1;
+  int64_t s = std::min<int64_t>(kValuesTargetWorkgroups / wgs, kOnlineMaxSplit);
+  // Each share keeps at least two key blocks per group.
+  s = std::min<int64_t>(s, (L + kBN - 1) / kBN / (2 * 2));
+  (void)d;
+  return s >= 2 ? (int)s : 1;
 }
 
 }  // namespace attn

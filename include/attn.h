@@ -72,7 +72,12 @@ enum {
  *   causal  : 0 = no mask; nonzero = key j allowed for query i iff j <= i.
  *   stream  : HIP stream the kernels are queued on.
  *
- * Returns ATTN_OK or one of the codes above.  For d > 128 the call uses the
+ * Returns ATTN_OK or one of the codes above.  For d <= 128 with so few heads
+ * that most compute units would idle, the keys of each 128-query block are
+ * split among up to 8 workgroups whose fp32 shares of O and (max, sum) pairs
+ * are merged by a second kernel (a split over keys with a log-sum-exp style
+ * combine); that uses the workspace buffer below too (attn_workspace_bytes
+ * gives its size).  For d > 128 the call uses the
  * workspace buffer the library keeps for (current device, stream), growing it
  * when needed (about 2*L*(256*ceil(L/256) + 128) + 8*L*ceil(L/256) bytes per
  * head, heads processed in chunks of at most 2 GiB; when so few heads would
@@ -198,7 +203,8 @@ enum {
   ATTN_KERNEL_SCORES = 1,  /* two-pass path: S = QK^T tiles -> bf16 exp + stats   */
   ATTN_KERNEL_VALUES = 2,  /* two-pass path: O = P V with the row normalisation   */
   ATTN_KERNEL_VALUES_REDUCE = 3, /* two-pass path, few heads: sum of the key splits */
-  ATTN_KERNEL_COUNT = 4
+  ATTN_KERNEL_ONLINE_COMBINE = 4, /* online path, few heads: merge of the key splits  */
+  ATTN_KERNEL_COUNT = 5
 };
 int attn_timing_enable(int enable);
 int attn_timing_collect(double* sum_ms, int64_t* launches, int n);

@@ -110,7 +110,7 @@ def test_workspace_bytes():
     assert _values_split(1, 1100, 256, False) == 2
     assert eab.workspace_bytes(1, 1, 1100, 256) == (
         r(1100 * (256 * 5 + 128) * 2) + 2 * r(5 * 1100 * 4) + r(2 * 1100 * 256 * 4))
-    assert eab.workspace_bytes(4, 8, 1024, 64) == 0       # online path: none
+    assert eab.workspace_bytes(4, 8, 1024, 64) == 0       # online path, 256 workgroups: none
     assert eab.workspace_bytes(0, 1, L, d) == 0
     big = eab.workspace_bytes(1000, 1, L, d)              # chunked under ~2 GiB
     assert per_head <= big <= (2 << 30)
@@ -374,3 +374,27 @@ def test_varlen_layouts_are_accepted():
     assert fwd_var(q=A, k=A + H * d * 2, v=A + 2 * H * d * 2, out=A + span, cu=A + 2 * span,
                    total=1024, max_seqlen=1 << 22, H=H, H_kv=H, qs=st2(row, d), ks=st2(row, d),
                    vs=st2(row, d)) == _lib.ATTN_ERR_TOO_LARGE
+
+
+def _online_split(n, L):
+    """Key splits of the online kernel for n heads: 1 unless the unsplit grid
+    (n * ceil(L/128) workgroups) would fill at most half of 256 CUs; then as many
+    as fit in 256, at most 8, each share keeping >= 2 key blocks (64 keys) per
+    group (two groups); below 2, no split."""
+    base = n * -(-L // 128)
+    if 2 * base > 256:
+        return 1
+    s = min(256 // base, 8, -(-L // 64) // 4)
+    return s if s >= 2 else 1
+
+
+@pytest.mark.parametrize("B,H,L,d,split", [(1, 1, 4096, 64, 8), (1, 2, 1000, 128, 4),
+                                           (1, 1, 300, 32, 1), (4, 8, 1024, 64, 1),
+                                           (2, 4, 1024, 64, 4), (1, 1, 128, 64, 1)])
+def test_online_split_workspace(B, H, L, d, split):
+    # split shares: fp32 O [split, heads, L, d] and (m, l) [split, heads, L, 2]
+    assert _online_split(B * H, L) == split
+    r = lambda x: (x + 255) // 256 * 256
+    want = r(split * B * H * L * (d + 2) * 4) if split > 1 else 0
+    assert eab.workspace_bytes(B, H, L, d) == want
+    assert eab.workspace_bytes(B, H, L, d, True) == want

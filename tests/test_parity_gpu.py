@@ -236,3 +236,43 @@ def test_two_streams_do_not_share_workspace():
         _report("two streams", am, r)
         assert ok
     assert all(torch.equal(p[0], outs[-1][0]) and torch.equal(p[1], outs[-1][1]) for p in outs)
+
+
+# ---- online path with few heads: keys split among workgroups, then combined ----
+
+@pytest.mark.parametrize("B,H,L,d", [(1, 1, 4096, 64), (1, 2, 1000, 128), (2, 4, 1024, 64),
+                                     (1, 1, 777, 32)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_key_split(B, H, L, d, causal):
+    """Shares 8, 4, 4 and 3: each writes fp32 O and (m, l); the combine kernel
+    merges them (and writes the LSE)."""
+    from exact_softmax_attention_bf16_amd import attention, kernel_timing
+    q, k, v = make_qkv(B, H, L, d, 300 + L + d)
+    s = 1.0 / math.sqrt(d)
+    res = {}
+    with kernel_timing(res):
+        o, lse = attention(q.cuda(), k.cuda(), v.cuda(), scale=s, causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    assert set(res) == {"online", "online_combine"}
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), s, causal)
+    ok, a, r = within_bar(to_f64(o), ref)
+    _report(f"online split B={B} H={H} L={L} d={d} causal={causal}", a, r)
+    assert ok, (a, r)
+    err = np.abs(to_f64(lse) - oracle.log_sum_exp(to_f64(q), to_f64(k), s, causal))
+    assert float(err.max()) <= 4e-3 + 1e-5 * float(np.abs(to_f64(lse)).max())
+
+
+def test_online_key_split_window_strided_out_deterministic():
+    from exact_softmax_attention_bf16_amd import attention
+    L, d = 3000, 64
+    q, k, v = make_qkv(1, 1, L, d, 310)
+    big = torch.full((1, 1, L, 2 * d), 5.0, dtype=torch.bfloat16, device="cuda")
+    out = big[..., d:]
+    o1 = attention(q.cuda(), k.cuda(), v.cuda(), window=(700, 90), out=out).clone()
+    o2 = attention(q.cuda(), k.cuda(), v.cuda(), window=(700, 90))
+    torch.cuda.synchronize()
+    assert bool((big[..., :d] == 5.0).all())
+    assert torch.equal(o1, o2)
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1.0 / math.sqrt(d), False, (700, 90))
+    ok, a, r = within_bar(to_f64(o1), ref)
+    assert ok, (a, r)

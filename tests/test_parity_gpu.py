@@ -276,3 +276,13 @@ def test_online_key_split_window_strided_out_deterministic():
     ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1.0 / math.sqrt(d), False, (700, 90))
     ok, a, r = within_bar(to_f64(o1), ref)
     assert ok, (a, r)
+
+
+@pytest.mark.parametrize("d", list(range(192, 1025, 64)))
+@pytest.mark.parametrize("causal", [False, True])
+def test_every_two_pass_head_dim(d, causal):
+    """Every multiple of 64 in (128, 1024]: the last 256-channel tile of the
+    values pass is partly past d for most of them."""
+    ok, a, r, *_ = check_full(1, 2, 300, d, 1.0 / math.sqrt(d), causal, seed=400 + d)
+    _report(f"d={d} causal={causal}", a, r)
+    assert ok, (a, r)

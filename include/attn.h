@@ -187,8 +187,12 @@ const char* attn_status_string(int status);
  * Host-only; makes no HIP call. */
 int attn_path_for_head_dim(int64_t d);
 
-/* Workspace bytes attn_forward draws for one chunk of this problem (0 on the
- * online path or for an invalid shape).  Host-only; makes no HIP call. */
+/* Workspace bytes attn_forward draws for one chunk of this problem: the
+ * two-pass path's staging (d > 128), or the online path's key-split shares
+ * when few heads split (d <= 128); 0 when none is needed or for an invalid
+ * shape.  attn_forward_ex draws at most this for the same B, H, L, d and
+ * causal flag (a window can only narrow the key split); attn_forward_varlen
+ * draws nothing.  Host-only; makes no HIP call. */
 int64_t attn_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int causal);
 
 /*

@@ -23,6 +23,12 @@ What it computes, and where the pages define it:
     sliding-window mask.  Its body is not on the page; the reading taken is
     key j allowed for query i iff i - left <= j <= i + right (None: that side
     unbounded), applied on top of the causal mask.
+  * same page, __call__ problem_size (s_q, s_k) and cum_seqlen_q / cum_seqlen_k:
+    the query and key lengths may differ.  Reading taken: bottom-right
+    alignment, query i standing at key position i + (Lk - Lq) for the causal
+    and window masks (the last query sees the last key, as in decoding against
+    a cache); a row that then sees no key (Lq > Lk) outputs 0 and its LSE is
+    -inf, as that page's softmax_step guard for an all -inf row gives.
 
 The method reaches exactly the plain definition (up to rounding order), so this
 oracle is that definition written out, one step per function, in the pages'
@@ -45,7 +51,8 @@ closed forms (constant V, equal keys, causal row 0, scale 0, L = 1, a one-hot
 limit with huge logits, a hand-worked example in tests/golden, log L and
 log(i + 1) for the LSE of equal keys, one constant value per key/value head
 for the head groups, O = V for a window of width zero, window means of V for
-equal keys), invariants (rows of P sum to 1, key-shift invariance,
+equal keys, one query against all keys, zero rows when Lq > Lk), invariants
+(the last Lq rows of a square causal problem equal the Lq < Lk one), (rows of P sum to 1, key-shift invariance,
 permutation equivariance, linearity in V, the LSE's exact shift when every
 key moves by the same vector) and a cross-check against torch's CPU float64
 attention.  No function here is unpinned.
@@ -82,12 +89,16 @@ def window_mask(Z: np.ndarray, query_index: np.ndarray, left, right) -> np.ndarr
     return Z
 
 
-def softmax_rows(Z: np.ndarray) -> np.ndarray:
-    """Numerically stable row softmax: exp(Z - rowmax) / rowsum."""
+def softmax_rows(Z: np.ndarray, allow_empty: bool = False) -> np.ndarray:
+    """Numerically stable row softmax: exp(Z - rowmax) / rowsum.  A row with
+    every key masked is an error unless allow_empty, when it becomes all 0."""
     m = Z.max(axis=1, keepdims=True)
-    assert np.all(np.isfinite(m)), "a row with every key masked"
-    E = np.exp(Z - m)
-    return E / E.sum(axis=1, keepdims=True)
+    empty = ~np.isfinite(m[:, 0])
+    assert allow_empty or not empty.any(), "a row with every key masked"
+    E = np.exp(Z - np.where(np.isfinite(m), m, 0.0))
+    E[empty] = 0.0
+    tot = E.sum(axis=1, keepdims=True)
+    return E / np.where(tot > 0, tot, 1.0)
 
 
 def weighted_values(P: np.ndarray, V: np.ndarray) -> np.ndarray:
@@ -95,12 +106,17 @@ def weighted_values(P: np.ndarray, V: np.ndarray) -> np.ndarray:
     return P @ V
 
 
-def row_log_sum_exp(Z: np.ndarray) -> np.ndarray:
+def row_log_sum_exp(Z: np.ndarray, allow_empty: bool = False) -> np.ndarray:
     """log(sum_j exp(Z[r, j])) per row, as the row maximum plus the log of the
-    row sum of exp(Z - max) (the LSE the FMHA epilogue stores)."""
+    row sum of exp(Z - max) (the LSE the FMHA epilogue stores); -inf for a row
+    with every key masked (only with allow_empty)."""
     m = Z.max(axis=1)
-    assert np.all(np.isfinite(m)), "a row with every key masked"
-    return m + np.log(np.exp(Z - m[:, None]).sum(axis=1))
+    empty = ~np.isfinite(m)
+    assert allow_empty or not empty.any(), "a row with every key masked"
+    mm = np.where(empty, 0.0, m)
+    out = mm + np.log(np.exp(Z - mm[:, None]).sum(axis=1))
+    out[empty] = -np.inf
+    return out
 
 
 def _head(x, b: int, h: int) -> np.ndarray:
@@ -109,15 +125,21 @@ def _head(x, b: int, h: int) -> np.ndarray:
 
 
 def _dims(q, k, v):
-    """(B, H, L, group): q is [B, H, L, d]; k and v are [B, H_kv, L, .] with
+    """(B, H, Lq, group): q is [B, H, Lq, d]; k and v are [B, H_kv, Lk, .] with
     H_kv dividing H, and query head h reads key/value head h // group."""
     sq, sk, sv = np.shape(q), np.shape(k), np.shape(v)
     if not (len(sq) == 4 and len(sk) == 4 and len(sv) == 4 and sq[0] == sk[0] == sv[0]
-            and sq[2] == sk[2] == sv[2] and sq[3] == sk[3] and sk[1] == sv[1]
+            and sk[2] == sv[2] and sq[3] == sk[3] and sk[1] == sv[1]
             and sk[1] >= 1 and sq[1] % sk[1] == 0):
-        raise ValueError("q must be [B, H, L, d] and k, v [B, H_kv, L, .] with H_kv dividing H "
+        raise ValueError("q must be [B, H, Lq, d] and k, v [B, H_kv, Lk, .] with H_kv dividing H "
                          "(q, k share d)")
     return sq[0], sq[1], sq[2], sq[1] // sk[1]
+
+
+def _query_positions(Lq: int, Lk: int, rows=None) -> np.ndarray:
+    """Key position of each query row: bottom-right alignment, i + (Lk - Lq)."""
+    i = np.arange(Lq) if rows is None else np.asarray(rows)
+    return i + (Lk - Lq)
 
 
 def _masked_logits(Q, K, scale, causal, window, query_index):
@@ -131,30 +153,35 @@ def _masked_logits(Q, K, scale, causal, window, query_index):
 
 
 def probabilities(q, k, scale: float, causal: bool = False, window=None) -> np.ndarray:
-    """P = softmax(s * Q K^T) (masked when causal / windowed), shape [B, H, L, L]."""
+    """P = softmax(s * Q K^T) (masked when causal / windowed), shape [B, H, Lq, Lk]."""
     B, H, L, g = _dims(q, k, k)
-    P = np.empty((B, H, L, L), dtype=np.float64)
+    Lk = np.shape(k)[2]
+    P = np.empty((B, H, L, Lk), dtype=np.float64)
     for b in range(B):
         for h in range(H):
             Z = _masked_logits(_head(q, b, h), _head(k, b, h // g), scale, causal, window,
-                               np.arange(L))
-            P[b, h] = softmax_rows(Z)
+                               _query_positions(L, Lk))
+            P[b, h] = (softmax_rows(Z, allow_empty=True) if L > Lk else softmax_rows(Z))
     return P
 
 
 def attention(q, k, v, scale: float, causal: bool = False, window=None) -> np.ndarray:
-    """O = softmax(s * Q K^T) V for every (batch, head); float64 [B, H, L, dv].
+    """O = softmax(s * Q K^T) V for every (batch, head); float64 [B, H, Lq, dv].
 
     k and v may have fewer heads than q (H_kv dividing H): query head h then
-    reads key/value head h // (H / H_kv).  window = (left, right) restricts
-    query i to keys i - left .. i + right (None on a side: unbounded)."""
+    reads key/value head h // (H / H_kv), and Lk keys (Lk may differ from Lq:
+    query i stands at key position p = i + Lk - Lq).  window = (left, right)
+    restricts query i to keys p - left .. p + right (None on a side:
+    unbounded); causal to keys <= p.  A query with no key left gives 0."""
     B, H, L, g = _dims(q, k, v)
+    Lk = np.shape(k)[2]
     O = np.empty((B, H, L, np.shape(v)[-1]), dtype=np.float64)
     for b in range(B):
         for h in range(H):
             Z = _masked_logits(_head(q, b, h), _head(k, b, h // g), scale, causal, window,
-                               np.arange(L))
-            O[b, h] = weighted_values(softmax_rows(Z), _head(v, b, h // g))
+                               _query_positions(L, Lk))
+            P = softmax_rows(Z, allow_empty=True) if L > Lk else softmax_rows(Z)
+            O[b, h] = weighted_values(P, _head(v, b, h // g))
     return O
 
 
@@ -162,12 +189,13 @@ def log_sum_exp(q, k, scale: float, causal: bool = False, window=None) -> np.nda
     """lse[b, h, i] = log(sum over allowed keys j of exp(s * q_i . k_j)); float64
     [B, H, L].  Key heads and the window as in attention()."""
     B, H, L, g = _dims(q, k, k)
+    Lk = np.shape(k)[2]
     out = np.empty((B, H, L), dtype=np.float64)
     for b in range(B):
         for h in range(H):
             Z = _masked_logits(_head(q, b, h), _head(k, b, h // g), scale, causal, window,
-                               np.arange(L))
-            out[b, h] = row_log_sum_exp(Z)
+                               _query_positions(L, Lk))
+            out[b, h] = (row_log_sum_exp(Z, allow_empty=True) if L > Lk else row_log_sum_exp(Z))
     return out
 
 
@@ -185,7 +213,9 @@ def attention_rows(q, k, v, scale: float, causal: bool, rows, window=None) -> np
             cache.clear()  # one head's K and V in float64 at a time
             cache[(b, h // g)] = (_head(k, b, h // g), _head(v, b, h // g))
         K, V = cache[(b, h // g)]
+        Lq, Lk = np.shape(q)[2], np.shape(k)[2]
         Z = _masked_logits(np.asarray(q[b, h, i : i + 1], dtype=np.float64), K, scale, causal,
-                           window, np.array([i]))
-        out[r] = weighted_values(softmax_rows(Z), V)[0]
+                           window, _query_positions(Lq, Lk, [i]))
+        P = softmax_rows(Z, allow_empty=True) if Lq > Lk else softmax_rows(Z)
+        out[r] = weighted_values(P, V)[0]
     return out

@@ -546,3 +546,81 @@ def test_window_pins_pass_unmutated():
 def test_window_pins_catch_planted_mistake(name, monkeypatch):
     monkeypatch.setattr(oa, "window_mask", WINDOW_MUTANTS[name])
     assert not _window_pins_pass(), f"pins did not catch mutant {name}"
+
+
+# ---- query and key lengths that differ (bottom-right alignment) -----------------
+
+def brute_force_qk(q, k, v, scale, causal, window):
+    """Scalar loops for Lq != Lk: query i stands at key position i + Lk - Lq; a
+    row with no allowed key is 0."""
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    out = np.zeros((B, H, Lq, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            for i in range(Lq):
+                p = i + Lk - Lq
+                lo, hi = 0, Lk - 1
+                if window is not None and window[0] is not None:
+                    lo = max(lo, p - window[0])
+                if window is not None and window[1] is not None:
+                    hi = min(hi, p + window[1])
+                if causal:
+                    hi = min(hi, p)
+                keys = range(lo, hi + 1)
+                if len(keys) == 0:
+                    continue
+                z = [scale * math.fsum(q[b, h, i, c] * k[b, h, j, c] for c in range(d)) for j in keys]
+                m = max(z)
+                e = [math.exp(x - m) for x in z]
+                tot = math.fsum(e)
+                for c in range(v.shape[-1]):
+                    out[b, h, i, c] = math.fsum(e[t] * v[b, h, j, c] for t, j in enumerate(keys)) / tot
+    return out
+
+
+@pytest.mark.parametrize("Lq,Lk", [(3, 9), (1, 7), (9, 4), (6, 6)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [None, (2, 1)])
+def test_qk_lengths_brute_force(Lq, Lk, causal, window):
+    q, k, v = rnd((1, 2, Lq, 4), 120 + Lq), rnd((1, 2, Lk, 4), 121 + Lk), rnd((1, 2, Lk, 3), 122)
+    assert close(oracle.attention(q, k, v, 0.7, causal, window),
+                 brute_force_qk(q, k, v, 0.7, causal, window))
+
+
+@pytest.mark.parametrize("window", [None, (3, 2)])
+def test_qk_last_rows_of_square_problem(window):
+    # bottom-right alignment: Lq queries against Lk keys are the last Lq rows of
+    # the square problem over the same keys
+    Lq, Lk = 5, 12
+    qf, k, v = rnd((1, 2, Lk, 4), 123), rnd((1, 2, Lk, 4), 124), rnd((1, 2, Lk, 4), 125)
+    full = oracle.attention(qf, k, v, 0.6, True, window)
+    part = oracle.attention(qf[:, :, Lk - Lq:], k, v, 0.6, True, window)
+    assert close(part, full[:, :, Lk - Lq:])
+    lf = oracle.log_sum_exp(qf, k, 0.6, True, window)
+    assert close(oracle.log_sum_exp(qf[:, :, Lk - Lq:], k, 0.6, True, window), lf[:, :, Lk - Lq:])
+
+
+def test_single_query_sees_every_key_when_causal():
+    q, k, v = rnd((2, 2, 1, 5), 126), rnd((2, 2, 17, 5), 127), rnd((2, 2, 17, 5), 128)
+    assert close(oracle.attention(q, k, v, 0.4, True), oracle.attention(q, k, v, 0.4, False))
+
+
+def test_rows_without_keys_are_zero_and_lse_minus_inf():
+    Lq, Lk = 7, 3
+    q, k, v = rnd((1, 1, Lq, 4), 129), rnd((1, 1, Lk, 4), 130), rnd((1, 1, Lk, 4), 131)
+    o = oracle.attention(q, k, v, 0.5, True)
+    lse = oracle.log_sum_exp(q, k, 0.5, True)
+    assert np.array_equal(o[0, 0, : Lq - Lk], np.zeros((Lq - Lk, 4)))
+    assert np.all(lse[0, 0, : Lq - Lk] == -np.inf) and np.all(np.isfinite(lse[0, 0, Lq - Lk:]))
+    assert close(o[0, 0, Lq - Lk:], oracle.attention(q[:, :, Lq - Lk:], k, v, 0.5, True)[0, 0])
+
+
+def test_qk_pins_catch_top_left_alignment(monkeypatch):
+    def top_left(Lq, Lk, rows=None):
+        return np.arange(Lq) if rows is None else np.asarray(rows)
+    q, k, v = rnd((1, 1, 3, 4), 132), rnd((1, 1, 9, 4), 133), rnd((1, 1, 9, 3), 134)
+    want = brute_force_qk(q, k, v, 0.7, True, None)
+    assert close(oracle.attention(q, k, v, 0.7, True), want)
+    monkeypatch.setattr(oa, "_query_positions", top_left)
+    assert not close(oracle.attention(q, k, v, 0.7, True), want)

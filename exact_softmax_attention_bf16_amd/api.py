@@ -107,24 +107,31 @@ def _window_args(window):
 def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                      max_seqlen: int, scale: float | None = None, causal: bool = False,
                      out: torch.Tensor | None = None, return_lse: bool = False,
-                     window: tuple | None = None):
+                     window: tuple | None = None, cu_seqlens_k: torch.Tensor | None = None,
+                     max_seqlen_k: int | None = None):
     """Attention over a batch of sequences of different lengths packed along the
     tokens (the cum_seqlen interface of cuDNN's FMHA example): q is
-    [total, H, d], k and v [total, H_kv, d], cu_seqlens an int32 tensor of B + 1
-    offsets on the same device (sequence b is tokens cu_seqlens[b] ..
-    cu_seqlens[b + 1] - 1), max_seqlen >= the longest sequence.  d must be 32,
-    64 or 128.  Returns out [total, H, d] (and lse float32 [total, H] with
-    ``return_lse``); rows of tokens in no sequence are left as they were."""
+    [total, H, d], k and v [total_k, H_kv, d], cu_seqlens an int32 tensor of
+    B + 1 offsets on the same device (sequence b's queries are tokens
+    cu_seqlens[b] .. cu_seqlens[b + 1] - 1), max_seqlen >= the longest.  With
+    ``cu_seqlens_k`` (and ``max_seqlen_k``) the keys have offsets of their own
+    (cross-attention, or a few queries against a cache; query i then stands at
+    key position i + Lk - Lq for causal and windows); otherwise they share the
+    query offsets.  d must be 32, 64 or 128.  Returns out [total, H, d] (and lse
+    float32 [total, H] with ``return_lse``); rows of tokens in no sequence are
+    left as they were, rows that see no key are 0."""
     if not isinstance(q, torch.Tensor) or q.dim() != 3:
         raise ValueError("q must be a 3-D tensor [total, H, d]")
     total, H, d = q.shape
-    for t, name, heads in ((q, "q", H), (k, "k", None), (v, "v", None)):
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
         if not isinstance(t, torch.Tensor) or t.dim() != 3:
-            raise ValueError(f"{name} must be a 3-D tensor [total, heads, d]")
+            raise ValueError(f"{name} must be a 3-D tensor [tokens, heads, d]")
         _check(t.unsqueeze(0), name)
-    H_kv = k.shape[1]
-    if tuple(k.shape) != (total, H_kv, d) or tuple(v.shape) != (total, H_kv, d):
-        raise ValueError(f"k and v must be [total, H_kv, d] = [{total}, {H_kv}, {d}]")
+    total_k, H_kv = k.shape[0], k.shape[1]
+    if cu_seqlens_k is None and total_k != total:
+        raise ValueError("without cu_seqlens_k, k and v must have q's token count")
+    if tuple(k.shape) != (total_k, H_kv, d) or tuple(v.shape) != (total_k, H_kv, d):
+        raise ValueError(f"k and v must be [total_k, H_kv, d] = [{total_k}, {H_kv}, {d}]")
     if k.device != q.device or v.device != q.device:
         raise ValueError("q, k, v must be on one device")
     if H_kv == 0 and H > 0 or H_kv > 0 and H % H_kv != 0:
@@ -134,6 +141,14 @@ def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
         raise ValueError("cu_seqlens must be a 1-D int32 tensor of B + 1 offsets on q's device")
     cu = cu_seqlens.contiguous()
     B = cu.numel() - 1
+    cuk = None
+    if cu_seqlens_k is not None:
+        if (not isinstance(cu_seqlens_k, torch.Tensor) or cu_seqlens_k.dtype != torch.int32
+                or tuple(cu_seqlens_k.shape) != (B + 1,) or cu_seqlens_k.device != q.device):
+            raise ValueError("cu_seqlens_k must be an int32 tensor like cu_seqlens")
+        if max_seqlen_k is None:
+            raise ValueError("cu_seqlens_k needs max_seqlen_k")
+        cuk = cu_seqlens_k.contiguous()
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -147,8 +162,9 @@ def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
     st = lambda t: (ctypes.c_int64 * 2)(*t.stride()[:2])
     _call(_lib.load().attn_forward_varlen, q, q.data_ptr(), k.data_ptr(), v.data_ptr(),
           out.data_ptr(), lse.data_ptr() if lse is not None else None, cu.data_ptr(), B,
-          int(max_seqlen), total, H, H_kv, d, st(q), st(k), st(v), st(out), float(scale),
-          1 if causal else 0, wl, wr)
+          int(max_seqlen), total, cuk.data_ptr() if cuk is not None else None,
+          int(max_seqlen_k) if cuk is not None else 0, total_k, H, H_kv, d, st(q), st(k), st(v),
+          st(out), float(scale), 1 if causal else 0, wl, wr)
     return (out, lse) if return_lse else out
 
 

@@ -239,8 +239,8 @@ int forward(const void* q, const void* k, const void* v, void* out, float* lse,
       ks.n = nsplit;
     }
     hipError_t e = timed(ATTN_KERNEL_ONLINE, stream, on, [&] {
-      return attn::launch_online(q, k, v, out, lse, hm, (int)bh, (int)L, (int)d, sl2, band, nullptr,
-                                 0, ks, stream);
+      return attn::launch_online(q, k, v, out, lse, hm, (int)bh, (int)L, (int)d, sl2, band,
+                                 attn::VarSeqs{nullptr, nullptr, 0, 0, 0}, ks, stream);
     });
     if (e == hipSuccess && nsplit > 1)
       e = timed(ATTN_KERNEL_ONLINE_COMBINE, stream, on, [&] {
@@ -413,11 +413,17 @@ int attn_forward_ex(const void* q, const void* k, const void* v, void* out, floa
 
 int attn_forward_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                         const int32_t* cu_seqlens, int64_t B, int64_t max_seqlen, int64_t total,
+                        const int32_t* cu_seqlens_k, int64_t max_seqlen_k, int64_t total_k,
                         int64_t H, int64_t H_kv, int64_t d, const int64_t* q_strides,
                         const int64_t* k_strides, const int64_t* v_strides,
                         const int64_t* o_strides, float scale, int causal, int64_t window_left,
                         int64_t window_right, hipStream_t stream) {
-  if (B < 0 || max_seqlen < 0 || total < 0 || H < 0 || H_kv < 0 || d < 0)
+  if (!cu_seqlens_k) {  // keys share the query offsets and lengths
+    max_seqlen_k = max_seqlen;
+    total_k = total;
+  }
+  if (B < 0 || max_seqlen < 0 || total < 0 || H < 0 || H_kv < 0 || d < 0 || max_seqlen_k < 0 ||
+      total_k < 0)
     return ATTN_ERR_BAD_SHAPE;
   if (window_left < -1 || window_right < -1) return ATTN_ERR_BAD_SHAPE;
   int64_t rows = 0, elems = 0, bytes = 0, bh = 0, slots = 0;
@@ -431,45 +437,50 @@ int attn_forward_varlen(const void* q, const void* k, const void* v, void* out, 
   if (rows == 0 || slots == 0) return ATTN_OK;
   if (!q || !k || !v || !out || !cu_seqlens) return ATTN_ERR_NULL_PTR;
 
-  // Operands as [1, heads, total] views: strides {token, head} given, channels contiguous.
-  auto make = [&](const int64_t* st, int64_t heads) {
-    View w{{1, heads, total}, {0, d, heads * d}, d};
+  // Operands as [1, heads, tokens] views: strides {token, head} given, channels contiguous.
+  auto make = [&](const int64_t* st, int64_t heads, int64_t tokens) {
+    View w{{1, heads, tokens}, {0, d, heads * d}, d};
     if (st) {
       w.st[2] = st[0];
       w.st[1] = st[1];
     }
     return w;
   };
-  const View vq = make(q_strides, H), vk = make(k_strides, H_kv), vv = make(v_strides, H_kv),
-             vo = make(o_strides, H);
+  const View vq = make(q_strides, H, total), vk = make(k_strides, H_kv, total_k),
+             vv = make(v_strides, H_kv, total_k), vo = make(o_strides, H, total);
   for (const View* w : {&vq, &vk, &vv, &vo}) {
     if (!w->strides_valid()) return ATTN_ERR_BAD_STRIDE;
     if (w->st[1] > (INT64_MAX / 8) / std::max<int64_t>(H, 1) ||
-        w->st[2] > (INT64_MAX / 8) / std::max<int64_t>(total, 1))
+        w->st[2] > (INT64_MAX / 8) / std::max<int64_t>(std::max(total, total_k), 1))
       return ATTN_ERR_BAD_STRIDE;
   }
   if (!vo.one_to_one()) return ATTN_ERR_BAD_STRIDE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15 ||
-      ((uintptr_t)lse & 3) || ((uintptr_t)cu_seqlens & 3))
+      ((uintptr_t)lse & 3) || ((uintptr_t)cu_seqlens & 3) || ((uintptr_t)cu_seqlens_k & 3))
     return ATTN_ERR_MISALIGNED;
   const int64_t ob = vo.span() * 2, cb = (B + 1) * 4;
-  if (overlaps(out, ob, q, vq.span() * 2) || overlaps(out, ob, k, vk.span() * 2) ||
-      overlaps(out, ob, v, vv.span() * 2) || overlaps(out, ob, cu_seqlens, cb))
+  // Empty key views (total_k == 0) address nothing.
+  const int64_t kb = total_k > 0 ? vk.span() * 2 : 0, vb = total_k > 0 ? vv.span() * 2 : 0;
+  const int64_t ckb = cu_seqlens_k ? cb : 0;
+  if (overlaps(out, ob, q, vq.span() * 2) || overlaps(out, ob, k, kb) || overlaps(out, ob, v, vb) ||
+      overlaps(out, ob, cu_seqlens, cb) || overlaps(out, ob, cu_seqlens_k, ckb))
     return ATTN_ERR_ALIAS;
   if (lse) {
     const int64_t lb = rows * 4;
     if (overlaps(lse, lb, out, ob) || overlaps(lse, lb, q, vq.span() * 2) ||
-        overlaps(lse, lb, k, vk.span() * 2) || overlaps(lse, lb, v, vv.span() * 2) ||
-        overlaps(lse, lb, cu_seqlens, cb))
+        overlaps(lse, lb, k, kb) || overlaps(lse, lb, v, vb) ||
+        overlaps(lse, lb, cu_seqlens, cb) || overlaps(lse, lb, cu_seqlens_k, ckb))
       return ATTN_ERR_ALIAS;
   }
   // One sequence per 32-bit offsets (rows up to max_seqlen + 255 are formed),
   // token indices and workgroup counts in int.
-  const int64_t ld_max = std::max(vq.st[2], std::max(vk.st[2], vv.st[2]));
+  const int64_t ld_kv = std::max(vk.st[2], vv.st[2]);
   for (const View* w : {&vq, &vk, &vv, &vo})
     if (w->st[2] >= ((int64_t)1 << 30) || w->st[1] >= ((int64_t)1 << 30)) return ATTN_ERR_TOO_LARGE;
-  if (max_seqlen > ((int64_t)1 << 30) || total >= ((int64_t)1 << 31) - 1 ||
-      (max_seqlen + 256) * ld_max * 2 >= ((int64_t)1 << 31) || H >= ((int64_t)1 << 30) ||
+  if (max_seqlen > ((int64_t)1 << 30) || max_seqlen_k > ((int64_t)1 << 30) ||
+      total >= ((int64_t)1 << 31) - 1 || total_k >= ((int64_t)1 << 31) - 1 ||
+      (max_seqlen + 256) * vq.st[2] * 2 >= ((int64_t)1 << 31) ||
+      (max_seqlen_k + 256) * ld_kv * 2 >= ((int64_t)1 << 31) || H >= ((int64_t)1 << 30) ||
       (max_seqlen + 127) / 128 * bh >= ((int64_t)1 << 31))
     return ATTN_ERR_TOO_LARGE;
 
@@ -481,12 +492,14 @@ int attn_forward_varlen(const void* q, const void* k, const void* v, void* out, 
   hm.k = {0, vk.st[1], (int)vk.st[2]};
   hm.v = {0, vv.st[1], (int)vv.st[2]};
   hm.o = {0, vo.st[1], (int)vo.st[2]};
-  const attn::Band band = attn::make_band(window_left, window_right, causal != 0, max_seqlen);
+  const attn::Band band =
+      attn::make_band(window_left, window_right, causal != 0, std::max(max_seqlen, max_seqlen_k) + 1);
   const float sl2 = scale * 1.4426950408889634f;
   const hipError_t e = timed(ATTN_KERNEL_ONLINE, stream, timing_on(), [&] {
     return attn::launch_online(q, k, v, out, lse, hm, (int)bh, (int)max_seqlen, (int)d, sl2, band,
-                               cu_seqlens, (int)total, attn::KeySplit{nullptr, nullptr, 1, (int)bh},
-                               stream);
+                               attn::VarSeqs{cu_seqlens, cu_seqlens_k, (int)total, (int)total_k,
+                                             (int)max_seqlen_k},
+                               attn::KeySplit{nullptr, nullptr, 1, (int)bh}, stream);
   });
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }

@@ -106,17 +106,28 @@ struct KeySplit {
 };
 constexpr int kOnlineMaxSplit = 8;
 
+// Sequences of different lengths packed along the tokens (cu_q null: none).
+// Sequence b holds query tokens [cu_q[b], cu_q[b + 1]) and key/value tokens
+// [cu_k[b], cu_k[b + 1]) (cu_k null: the query offsets), clamped to
+// [0, total_q] / [0, total_k] and to L / max_k tokens.
+struct VarSeqs {
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
+  int max_k;
+};
+
 // Fused online-softmax kernel, d in {32, 64, 128}.  sl2 = scale * log2(e).
 // lse (may be null): fp32 [global head][L], the natural log of each row's
-// softmax denominator.  With cu non-null (device int32 [BH / hm.H + 1]) the
-// heads are sequences of different lengths packed along the tokens: sequence
-// b holds tokens [cu[b], cu[b + 1]) (clamped to [0, total]; length at most
-// L), rows hm.*.ld and heads hm.*.h elements apart, and lse is [total][H].
+// softmax denominator.  With vs.cu_q non-null the heads are the sequences of
+// vs (L: the longest query length), rows hm.*.ld and heads hm.*.h elements
+// apart, and lse is [total_q][H]; query i of a sequence stands at key
+// position i + Lk - Lq for the band.
 // With ks.n > 1 (never with cu) it writes the shares instead of out and lse,
 // and launch_online_combine finishes the call.
 hipError_t launch_online(const void* q, const void* k, const void* v, void* out, float* lse,
                          const HeadMap& hm, int BH, int L, int d, float sl2, const Band& band,
-                         const int* cu, int total, const KeySplit& ks, hipStream_t s);
+                         const VarSeqs& vs, const KeySplit& ks, hipStream_t s);
 hipError_t launch_online_combine(const KeySplit& ks, void* out, float* lse, const HeadMap& hm,
                                  int L, int d, hipStream_t s);
 // Shares per query block for BH heads of length L: 1 unless the unsplit grid

@@ -64,8 +64,10 @@ struct OnlineSmem {
 // bh * L * D (no division by H, whose expansion would sit ahead of the first
 // load of this short kernel).  kStrided: through the head map.  kVarlen:
 // sequences of different lengths packed along the token dimension; sequence
-// b = bh / H holds tokens [cu[b], cu[b + 1]) (clamped to [0, total], its length
-// to L), rows are hm.*.ld apart and heads hm.*.h apart.
+// b = bh / H holds query tokens [vs.cu_q[b], vs.cu_q[b + 1]) and key/value
+// tokens [vs.cu_k[b], vs.cu_k[b + 1]) (cu_k null: the same), clamped to the
+// views and to the longest lengths; rows are hm.*.ld apart and heads hm.*.h
+// apart.  Query i of a sequence stands at key position i + Lk - Lq.
 enum { kPlain = 0, kStrided = 1, kVarlen = 2 };
 // MASK: which keys below L each query i may see -- kAllKeys: all of them;
 // kCausal: j <= i; kWindow: i - left <= j <= i + right (band.left, band.right,
@@ -79,8 +81,7 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
                                                           uint16_t* __restrict__ out,
                                                           float* __restrict__ lse, HeadMap hm,
                                                           int Lmax, int nqb, float sl2, Band band,
-                                                          const int* __restrict__ cu, int total,
-                                                          KeySplit ks) {
+                                                          VarSeqs vs, KeySplit ks) {
   constexpr int CPR = D / 8;                       // 16-byte chunks per K row
   constexpr int SWZ = (CPR >= 8 ? 8 : CPR) - 1;    // chunk-index bits that are swizzled
   constexpr int VROW = kBN * 2 + 8;                // bytes per V^T row: 64 keys + pad
@@ -111,28 +112,37 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   int qb = lid % nqb;
   if (MASK == kCausal) qb = nqb - 1 - qb;  // the longest rows start first
   constexpr bool BANDED = MASK != kAllKeys, HAS_LEFT = MASK == kWindow;
-  const int left = HAS_LEFT ? band.left : kNoLimit;
-  const int right = MASK == kCausal ? 0 : band.right;
+  int left = HAS_LEFT ? band.left : kNoLimit;
+  int right = MASK == kCausal ? 0 : band.right;
 
   constexpr bool PLAIN = LAYOUT == kPlain;
   const int ldq = PLAIN ? D : hm.q.ld, ldk = PLAIN ? D : hm.k.ld, ldv = PLAIN ? D : hm.v.ld;
   const int ldo = PLAIN ? D : hm.o.ld;
-  // This head's row 0 in each operand (elements), its length, and where its
-  // log-sum-exp values go (lse_base + lse_step * query).
-  int L = Lmax;
+  // This head's row 0 in each operand (elements), its query and key lengths,
+  // and where its log-sum-exp values go (lse_base + lse_step * query).
+  int L = Lmax, Lk = Lmax;
   int64_t qoff, koff, voff, ooff, lse_base;
   int lse_step = 1;
   if constexpr (LAYOUT == kVarlen) {
     const int b = bh / hm.H, h = bh - b * hm.H;
-    const int start = min(max(cu[b], 0), total);
-    const int end = min(max(cu[b + 1], start), total);
-    L = min(end - start, Lmax);
+    const int qs = min(max(vs.cu_q[b], 0), vs.total_q);
+    const int qe = min(max(vs.cu_q[b + 1], qs), vs.total_q);
+    L = min(qe - qs, Lmax);
     if (qb * kBM >= L) return;  // the whole workgroup, before any barrier
-    qoff = (int64_t)start * ldq + (int64_t)h * hm.q.h;
-    koff = (int64_t)start * ldk + (int64_t)(h / hm.group) * hm.k.h;
-    voff = (int64_t)start * ldv + (int64_t)(h / hm.group) * hm.v.h;
-    ooff = (int64_t)start * ldo + (int64_t)h * hm.o.h;
-    lse_base = (int64_t)start * hm.H + h;  // lse is [total, H]
+    const int* cuk = vs.cu_k != nullptr ? vs.cu_k : vs.cu_q;
+    const int tk = vs.cu_k != nullptr ? vs.total_k : vs.total_q;
+    const int ks0 = min(max(cuk[b], 0), tk);
+    const int ke = min(max(cuk[b + 1], ks0), tk);
+    Lk = min(ke - ks0, vs.max_k);
+    // Query i stands at key position i + Lk - L: shift the band by that.
+    const int shift = Lk - L;
+    if (left < kNoLimit) left -= shift;
+    if (right < kNoLimit) right += shift;
+    qoff = (int64_t)qs * ldq + (int64_t)h * hm.q.h;
+    koff = (int64_t)ks0 * ldk + (int64_t)(h / hm.group) * hm.k.h;
+    voff = (int64_t)ks0 * ldv + (int64_t)(h / hm.group) * hm.v.h;
+    ooff = (int64_t)qs * ldo + (int64_t)h * hm.o.h;
+    lse_base = (int64_t)qs * hm.H + h;  // lse is [total_q, H]
     lse_step = hm.H;
   } else if constexpr (PLAIN) {
     qoff = koff = voff = ooff = (int64_t)(hm.bh0 + bh) * L * D;
@@ -144,10 +154,11 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
     ooff = hm.o_off(bh);
     lse_base = (int64_t)(hm.bh0 + bh) * L;
   }
-  // Rows past L of each head read as zero: the resources end after row L - 1.
+  // Rows past the end of each head read as zero: the resources end after its
+  // last row (and are empty for a sequence without keys).
   const auto rq = make_rsrc(q + qoff, ((uint32_t)(L - 1) * ldq + D) * 2);
-  const auto rk = make_rsrc(k + koff, ((uint32_t)(L - 1) * ldk + D) * 2);
-  const auto rv = make_rsrc(v + voff, ((uint32_t)(L - 1) * ldv + D) * 2);
+  const auto rk = make_rsrc(k + koff, Lk > 0 ? ((uint32_t)(Lk - 1) * ldk + D) * 2 : 0u);
+  const auto rv = make_rsrc(v + voff, Lk > 0 ? ((uint32_t)(Lk - 1) * ldv + D) * 2 : 0u);
 
   const int q0 = qb * kBM + wave * 32;  // first query of this wave
   const int myq = q0 + c32;             // this lane's query
@@ -160,9 +171,9 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
 
   // Key blocks t0 .. t0 + ntiles - 1 meet the band of this workgroup's queries.
   const int kstart = HAS_LEFT ? max(0, qb * kBM - left) : 0;
-  const int kend = BANDED ? min(L, qb * kBM + kBM + right) : L;
+  const int kend = BANDED ? min(Lk, qb * kBM + kBM + right) : Lk;
   int t0 = kstart / kBN;
-  int ntiles = (kend + kBN - 1) / kBN - t0;
+  int ntiles = max(0, (kend + kBN - 1) / kBN - t0);
   if (ks.n > 1) {  // this split's share of those blocks (possibly none)
     const int a = t0 + ntiles * split / ks.n, b = t0 + ntiles * (split + 1) / ks.n;
     t0 = a;
@@ -250,7 +261,7 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
       // Softmax update for this lane's query over its 32 of the 64 keys.  The
       // maximum is taken on the raw scores (scaled afterwards; the sign of sl2
       // picks max or min), and y - m is one FMA: p = 2^(s * sl2 - m).
-      const bool need_mask = (kbase + kBN > L) || (BANDED && kbase + kBN - 1 > q0 + right) ||
+      const bool need_mask = (kbase + kBN > Lk) || (BANDED && kbase + kBN - 1 > q0 + right) ||
                              (HAS_LEFT && kbase < q0 + 31 - left);
       float tmax;
       if (need_mask) {
@@ -260,7 +271,7 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int key = kbase + kb * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-            const bool off = key >= L || (BANDED && key > myq + right) ||
+            const bool off = key >= Lk || (BANDED && key > myq + right) ||
                              (HAS_LEFT && key < myq - left);
             s[kb][j] = off ? -INFINITY : s[kb][j] * sl2;
             tmax = fmaxf(tmax, s[kb][j]);
@@ -382,7 +393,7 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   // The row's softmax denominator is sum_j 2^(y_j) = 2^m * lsum (y in log2 units).
   if (lse != nullptr && myq < L && h == 0)
     lse[lse_base + (int64_t)lse_step * myq] = (m + log2f(lsum)) * 0.6931471805599453f;
-  const float inv = 1.f / lsum;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;  // a row that sees no key gives 0
   if (myq < L) {
     uint16_t* orow = out + ooff + (int64_t)myq * ldo;
 #pragma unroll
@@ -433,7 +444,7 @@ __global__ __launch_bounds__(256) void online_combine_kernel(KeySplit ks, uint16
 
 template <int D, int MASK, int LAYOUT>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* out, float* lse,
-                      HeadMap hm, int BH, int L, float sl2, Band band, const int* cu, int total,
+                      HeadMap hm, int BH, int L, float sl2, Band band, VarSeqs vs,
                       KeySplit ks, hipStream_t s) {
   const int nqb = (L + kBM - 1) / kBM;
   const dim3 grid((unsigned)(nqb * BH * (ks.n > 1 ? ks.n : 1))), block(64 * kWaves);
@@ -441,41 +452,41 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* out, fl
   const uint16_t* kp = (const uint16_t*)k;
   const uint16_t* vp = (const uint16_t*)v;
   uint16_t* op = (uint16_t*)out;
-  void* args[] = {&qp, &kp, &vp, &op, &lse, &hm, &L, (void*)&nqb, &sl2, &band, &cu, &total, &ks};
+  void* args[] = {&qp, &kp, &vp, &op, &lse, &hm, &L, (void*)&nqb, &sl2, &band, &vs, &ks};
   return hipLaunchKernel((const void*)&online_attn_kernel<D, MASK, LAYOUT>, grid, block, args, 0, s);
 }
 
 template <int D, int MASK>
 hipError_t launch_m(const void* q, const void* k, const void* v, void* out, float* lse,
-                    const HeadMap& hm, int BH, int L, float sl2, Band band, const int* cu,
-                    int total, KeySplit ks, hipStream_t s) {
-  if (cu != nullptr)
-    return launch_one<D, MASK, kVarlen>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
+                    const HeadMap& hm, int BH, int L, float sl2, Band band,
+                    const VarSeqs& vs, KeySplit ks, hipStream_t s) {
+  if (vs.cu_q != nullptr)
+    return launch_one<D, MASK, kVarlen>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
   if (is_plain(hm, L, D))
-    return launch_one<D, MASK, kPlain>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
-  return launch_one<D, MASK, kStrided>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
+    return launch_one<D, MASK, kPlain>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
+  return launch_one<D, MASK, kStrided>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
 }
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* out, float* lse,
-                    const HeadMap& hm, int BH, int L, float sl2, Band band, const int* cu,
-                    int total, KeySplit ks, hipStream_t s) {
+                    const HeadMap& hm, int BH, int L, float sl2, Band band,
+                    const VarSeqs& vs, KeySplit ks, hipStream_t s) {
   if (band_is_full(band))
-    return launch_m<D, kAllKeys>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
+    return launch_m<D, kAllKeys>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
   if (band_is_causal(band))
-    return launch_m<D, kCausal>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
-  return launch_m<D, kWindow>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
+    return launch_m<D, kCausal>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
+  return launch_m<D, kWindow>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
 }
 
 }  // namespace
 
 hipError_t launch_online(const void* q, const void* k, const void* v, void* out, float* lse,
                          const HeadMap& hm, int BH, int L, int d, float sl2, const Band& band,
-                         const int* cu, int total, const KeySplit& ks, hipStream_t s) {
+                         const VarSeqs& vs, const KeySplit& ks, hipStream_t s) {
   switch (d) {
-    case 32: return launch_d<32>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
-    case 64: return launch_d<64>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
-    case 128: return launch_d<128>(q, k, v, out, lse, hm, BH, L, sl2, band, cu, total, ks, s);
+    case 32: return launch_d<32>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
+    case 64: return launch_d<64>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
+    case 128: return launch_d<128>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
     default: return hipErrorInvalidValue;
   }
 }

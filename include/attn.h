@@ -145,9 +145,14 @@ int attn_forward_ex(const void* q, const void* k, const void* v, void* out, floa
  * attn_forward_varlen -- a batch of sequences of different lengths packed
  * along one token dimension (cuDNN native_sparse_attention fmha.py, __call__:
  * cum_seqlen_q / cum_seqlen_k, and the epilogue's LSE store at
- * row + cum_seqlen).  Each sequence attends to itself only.
+ * row + cum_seqlen).  Sequence b's queries attend to its own keys only; the
+ * two may differ in number (cross-attention, or decoding a few queries against
+ * a cache), query i standing at key position i + Lk - Lq (bottom-right
+ * alignment, so the last query sees the last key) for the causal and window
+ * masks.  A query left with no key (possible when Lq > Lk) gives 0 and an LSE
+ * of -inf.
  *
- *   q, out        : [total, H, d] views; k, v : [total, H_kv, d] views.  Each is
+ *   q, out        : [total, H, d] views; k, v : [total_k, H_kv, d] views.  Each is
  *                   a device pointer to element [0,0,0] plus two element strides
  *                   (token, head) in a host array of 2 int64_t; NULL means packed
  *                   ({heads*d, d}).  Channels contiguous; strides >= 0 and
@@ -161,19 +166,24 @@ int attn_forward_ex(const void* q, const void* k, const void* v, void* out, floa
  *                   sequence to [0, total] and max_seqlen tokens, so accesses
  *                   stay inside the views whatever the array holds.  Tokens in
  *                   no sequence are neither read as queries nor written.
- *   B, max_seqlen : sequences, and the longest one's length (sizes the grid).
- *   total         : tokens in the views.
+ *   B, max_seqlen : sequences, and the longest one's query length (sizes the grid).
+ *   total         : query tokens in the q and out views.
+ *   cu_seqlens_k, : key/value offsets (device int32 [B + 1], same contract as
+ *   max_seqlen_k,   cu_seqlens), the longest key length and the key tokens in
+ *   total_k         the k and v views; cu_seqlens_k NULL: keys use cu_seqlens,
+ *                   max_seqlen and total (self-attention), the other two ignored.
  *   H, H_kv, d, scale, causal, window_left, window_right, stream : as for
  *                   attn_forward_ex, positions counted within each sequence;
  *                   d must be 32, 64 or 128 (the head dims fmha.py's interface
  *                   takes), else ATTN_ERR_UNSUPPORTED_HEAD_DIM.
  *
- * No workspace.  out must not overlap q, k, v or cu_seqlens (address ranges),
- * nor lse any of them.  Returns ATTN_OK (also when nothing is to be done:
+ * No workspace.  out must not overlap q, k, v or either offsets array (address
+ * ranges), nor lse any of them.  Returns ATTN_OK (also when nothing is to be done:
  * B, H, max_seqlen or total zero) or a status code.
  */
 int attn_forward_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                         const int32_t* cu_seqlens, int64_t B, int64_t max_seqlen, int64_t total,
+                        const int32_t* cu_seqlens_k, int64_t max_seqlen_k, int64_t total_k,
                         int64_t H, int64_t H_kv, int64_t d,
                         const int64_t* q_strides, const int64_t* k_strides,
                         const int64_t* v_strides, const int64_t* o_strides,

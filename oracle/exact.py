@@ -114,7 +114,8 @@ def row_log_sum_exp(Z: np.ndarray, allow_empty: bool = False) -> np.ndarray:
     empty = ~np.isfinite(m)
     assert allow_empty or not empty.any(), "a row with every key masked"
     mm = np.where(empty, 0.0, m)
-    out = mm + np.log(np.exp(Z - mm[:, None]).sum(axis=1))
+    with np.errstate(divide="ignore"):  # log(0) = -inf for the empty rows
+        out = mm + np.log(np.exp(Z - mm[:, None]).sum(axis=1))
     out[empty] = -np.inf
     return out
 

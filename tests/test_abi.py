@@ -335,9 +335,10 @@ def st2(*x):
 
 def fwd_var(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, lse=None, cu=A + 256 * MB,
             B=2, max_seqlen=16, total=32, H=1, H_kv=1, d=64, qs=None, ks=None, vs=None, os_=None,
-            scale=0.125, causal=0, wl=-1, wr=-1):
-    return _lib.load().attn_forward_varlen(q, k, v, out, lse, cu, B, max_seqlen, total, H, H_kv, d,
-                                           qs, ks, vs, os_, scale, causal, wl, wr, None)
+            scale=0.125, causal=0, wl=-1, wr=-1, cuk=None, max_k=0, total_k=0):
+    return _lib.load().attn_forward_varlen(q, k, v, out, lse, cu, B, max_seqlen, total, cuk, max_k,
+                                           total_k, H, H_kv, d, qs, ks, vs, os_, scale, causal, wl,
+                                           wr, None)
 
 
 def test_varlen_nothing_to_do():
@@ -398,3 +399,21 @@ def test_online_split_workspace(B, H, L, d, split):
     want = r(split * B * H * L * (d + 2) * 4) if split > 1 else 0
     assert eab.workspace_bytes(B, H, L, d) == want
     assert eab.workspace_bytes(B, H, L, d, True) == want
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cuk=A + 300 * MB, max_k=-1, total_k=10), "BAD_SHAPE"),
+    (dict(cuk=A + 300 * MB, max_k=10, total_k=-1), "BAD_SHAPE"),
+    (dict(cuk=A + 300 * MB + 2, max_k=10, total_k=10), "MISALIGNED"),
+    (dict(cuk=A + 192 * MB + 16, max_k=10, total_k=10), "ALIAS"),
+])
+def test_varlen_key_offsets_checks(kw, code):
+    assert fwd_var(**kw) == getattr(_lib, "ATTN_ERR_" + code)
+
+
+def test_varlen_key_offsets_layout_accepted():
+    # q: 8 tokens, keys: a long cache with a row stride too wide for 32-bit offsets
+    T = 1 << 40
+    assert fwd_var(q=A, k=A + T, v=A + 2 * T, out=A + 3 * T, cu=A + 4 * T, cuk=A + 5 * T,
+                   B=1, max_seqlen=8, total=8, max_k=1 << 22, total_k=1 << 22,
+                   ks=st2(1024, 64), vs=st2(1024, 64)) == _lib.ATTN_ERR_TOO_LARGE

@@ -354,3 +354,84 @@ def test_varlen_equals_separate_calls_bitwise():
         ref = attention(qs.to(DEV), ks.to(DEV), vs.to(DEV), causal=True)
         got = o[int(cu[i]):int(cu[i + 1])].transpose(0, 1).unsqueeze(0)
         assert torch.equal(got, ref), i
+
+
+# ---- query and key lengths that differ (cross-attention, decoding) -----------
+
+def qk_batch(q_lengths, k_lengths, H, H_kv, d, seed):
+    seqs = []
+    for i, (lq, lk) in enumerate(zip(q_lengths, k_lengths)):
+        q = make_qkv(1, H, lq, d, seed + 3 * i)[0]
+        _, k, v = make_qkv(1, H_kv, lk, d, seed + 3 * i + 1)
+        seqs.append((q, k, v))
+    def pack(j, heads):
+        return torch.cat([s[j][0].transpose(0, 1) for s in seqs], dim=0).reshape(-1, heads, d).contiguous()
+    cu_q = torch.tensor([0] + list(np.cumsum(q_lengths)), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(np.cumsum(k_lengths)), dtype=torch.int32)
+    return seqs, pack(0, H), pack(1, H_kv), pack(2, H_kv), cu_q, cu_k
+
+
+def check_qk(seqs, o, lse, cu_q, s, causal, window):
+    for i, (q, k, v) in enumerate(seqs):
+        a0, a1 = int(cu_q[i]), int(cu_q[i + 1])
+        if a1 == a0:
+            continue
+        got = o[a0:a1].transpose(0, 1).unsqueeze(0)
+        gl = lse[a0:a1].transpose(0, 1).unsqueeze(0)
+        if k.shape[2] == 0:  # no keys at all: every row is 0
+            assert bool((got == 0).all()) and bool(torch.isneginf(gl).all()), i
+            continue
+        ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), s, causal, window)
+        ok, a, r = within_bar(to_f64(got), ref)
+        assert ok, (i, a, r)
+        lref = oracle.log_sum_exp(to_f64(q), to_f64(k), s, causal, window)
+        lg = to_f64(gl)
+        empty = np.isneginf(lref)
+        assert np.array_equal(np.isneginf(lg), empty), i
+        assert bool((to_f64(got)[..., empty[0, :, :], :] == 0).all()) if empty.any() else True
+        ok, err = lse_ok(torch.from_numpy(np.where(empty, 0.0, lg)), np.where(empty, 0.0, lref))
+        assert ok, (i, err)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [None, (40, 20)])
+def test_varlen_separate_key_lengths(d, causal, window):
+    from exact_softmax_attention_bf16_amd import attention_varlen
+    q_len = [1, 37, 300, 128, 0, 90, 200]
+    k_len = [500, 37, 64, 700, 10, 0, 130]
+    H, H_kv = 4, 2
+    seqs, q, k, v, cu_q, cu_k = qk_batch(q_len, k_len, H, H_kv, d, 500 + d)
+    s = 1.0 / math.sqrt(d)
+    o, lse = attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu_q.to(DEV), max(q_len), scale=s,
+                              causal=causal, window=window, return_lse=True,
+                              cu_seqlens_k=cu_k.to(DEV), max_seqlen_k=max(k_len))
+    torch.cuda.synchronize()
+    check_qk(seqs, o.cpu(), lse.cpu(), cu_q, s, causal, window)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_one_query_per_sequence(d):
+    """One new token per sequence against caches of different lengths."""
+    from exact_softmax_attention_bf16_amd import attention_varlen
+    k_len = [1, 17, 1000, 4096, 2500, 64, 333, 2048]
+    q_len = [1] * len(k_len)
+    H, H_kv = 8, 2
+    seqs, q, k, v, cu_q, cu_k = qk_batch(q_len, k_len, H, H_kv, d, 600 + d)
+    s = 1.0 / math.sqrt(d)
+    o, lse = attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu_q.to(DEV), 1, scale=s,
+                              causal=True, return_lse=True, cu_seqlens_k=cu_k.to(DEV),
+                              max_seqlen_k=max(k_len))
+    torch.cuda.synchronize()
+    check_qk(seqs, o.cpu(), lse.cpu(), cu_q, s, True, None)
+
+
+def test_queries_past_the_keys_are_zero():
+    """Lq > Lk with causal: the first Lq - Lk queries see no key."""
+    from exact_softmax_attention_bf16_amd import attention_varlen
+    seqs, q, k, v, cu_q, cu_k = qk_batch([300], [100], 2, 2, 64, 700)
+    o, lse = attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu_q.to(DEV), 300, causal=True,
+                              return_lse=True, cu_seqlens_k=cu_k.to(DEV), max_seqlen_k=100)
+    torch.cuda.synchronize()
+    assert bool((o[:200] == 0).all()) and bool(torch.isneginf(lse[:200]).all())
+    check_qk(seqs, o.cpu(), lse.cpu(), cu_q, 0.125, True, None)

@@ -52,7 +52,7 @@ int64_t two_pass_workspace_bytes(int64_t BH, const attn::TwoPassDims& t, const a
 
 // Online path: fp32 shares of O and their (m, l) when the keys are split.
 int64_t online_workspace_bytes(int64_t BH, int64_t L, int64_t d) {
-  const int n = attn::online_split(BH, L, (int)d);
+  const int n = attn::online_split(BH, L, L);
   return n > 1 ? round256((int64_t)n * BH * L * (d + 2) * 4) : 0;
 }
 
@@ -226,7 +226,7 @@ int forward(const void* q, const void* k, const void* v, void* out, float* lse,
 
   if (attn_path_for_head_dim(d) == ATTN_PATH_ONLINE) {
     const int64_t nqb = (L + 127) / 128;
-    const int nsplit = attn::online_split(bh, L, (int)d);
+    const int nsplit = attn::online_split(bh, L, L);
     if (nqb * bh * nsplit >= ((int64_t)1 << 31)) return ATTN_ERR_TOO_LARGE;
     const bool on = timing_on();
     attn::KeySplit ks{nullptr, nullptr, 1, (int)bh};
@@ -244,7 +244,8 @@ int forward(const void* q, const void* k, const void* v, void* out, float* lse,
     });
     if (e == hipSuccess && nsplit > 1)
       e = timed(ATTN_KERNEL_ONLINE_COMBINE, stream, on, [&] {
-        return attn::launch_online_combine(ks, out, lse, hm, (int)L, (int)d, stream);
+        return attn::launch_online_combine(ks, out, lse, hm, (int)L, (int)d,
+                                           attn::VarSeqs{nullptr, nullptr, 0, 0, 0}, stream);
       });
     const hipError_t rerr = wsp ? release_workspace(stream, wsp) : hipSuccess;
     return e == hipSuccess && rerr == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -495,13 +496,30 @@ int attn_forward_varlen(const void* q, const void* k, const void* v, void* out, 
   const attn::Band band =
       attn::make_band(window_left, window_right, causal != 0, std::max(max_seqlen, max_seqlen_k) + 1);
   const float sl2 = scale * 1.4426950408889634f;
-  const hipError_t e = timed(ATTN_KERNEL_ONLINE, stream, timing_on(), [&] {
+  const attn::VarSeqs vs{cu_seqlens, cu_seqlens_k, (int)total, (int)total_k, (int)max_seqlen_k};
+  // Few (sequence, head) pairs -- e.g. decoding against long caches: split the keys.
+  const int nsplit = attn::online_split(bh, max_seqlen, max_seqlen_k);
+  if ((max_seqlen + 127) / 128 * bh * nsplit >= ((int64_t)1 << 31)) return ATTN_ERR_TOO_LARGE;
+  const bool on = timing_on();
+  attn::KeySplit ks{nullptr, nullptr, 1, (int)bh};
+  Workspace* wsp = nullptr;
+  if (nsplit > 1) {
+    const int64_t bytes = round256((int64_t)nsplit * bh * max_seqlen * (d + 2) * 4);
+    if (acquire_workspace(stream, (size_t)bytes, &wsp) != hipSuccess) return ATTN_ERR_WORKSPACE;
+    ks.part = (float*)wsp->ptr;
+    ks.stats = ks.part + (size_t)nsplit * bh * max_seqlen * d;
+    ks.n = nsplit;
+  }
+  hipError_t e = timed(ATTN_KERNEL_ONLINE, stream, on, [&] {
     return attn::launch_online(q, k, v, out, lse, hm, (int)bh, (int)max_seqlen, (int)d, sl2, band,
-                               attn::VarSeqs{cu_seqlens, cu_seqlens_k, (int)total, (int)total_k,
-                                             (int)max_seqlen_k},
-                               attn::KeySplit{nullptr, nullptr, 1, (int)bh}, stream);
+                               vs, ks, stream);
   });
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  if (e == hipSuccess && nsplit > 1)
+    e = timed(ATTN_KERNEL_ONLINE_COMBINE, stream, on, [&] {
+      return attn::launch_online_combine(ks, out, lse, hm, (int)max_seqlen, (int)d, vs, stream);
+    });
+  const hipError_t rerr = wsp ? release_workspace(stream, wsp) : hipSuccess;
+  return e == hipSuccess && rerr == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 int attn_timing_enable(int enable) {

@@ -123,16 +123,18 @@ struct VarSeqs {
 // vs (L: the longest query length), rows hm.*.ld and heads hm.*.h elements
 // apart, and lse is [total_q][H]; query i of a sequence stands at key
 // position i + Lk - Lq for the band.
-// With ks.n > 1 (never with cu) it writes the shares instead of out and lse,
-// and launch_online_combine finishes the call.
+// With ks.n > 1 it writes the shares ([split][head][L] rows, L the longest
+// query length) instead of out and lse, and launch_online_combine finishes the
+// call.
 hipError_t launch_online(const void* q, const void* k, const void* v, void* out, float* lse,
                          const HeadMap& hm, int BH, int L, int d, float sl2, const Band& band,
                          const VarSeqs& vs, const KeySplit& ks, hipStream_t s);
 hipError_t launch_online_combine(const KeySplit& ks, void* out, float* lse, const HeadMap& hm,
-                                 int L, int d, hipStream_t s);
-// Shares per query block for BH heads of length L: 1 unless the unsplit grid
-// would leave at least half of the compute units idle.  Shape only.
-int online_split(int64_t BH, int64_t L, int d);
+                                 int L, int d, const VarSeqs& vs, hipStream_t s);
+// Shares per query block for BH heads of (longest) query length Lq and key
+// length Lk: 1 unless the unsplit grid would leave at least half of the
+// compute units idle.  Shape only.
+int online_split(int64_t BH, int64_t Lq, int64_t Lk);
 
 // Scores pass: per 256x256 (key, query) tile, E = bf16(2^(y - m)) with
 // y = sl2 * q.k, m = ceil(max over the tile's keys of y) per query, plus m and

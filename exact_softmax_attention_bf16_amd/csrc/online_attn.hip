@@ -378,7 +378,7 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
     // A key split: this share's unnormalised O, m and l for the combine kernel
     // (m = -inf, l = 0 where the share holds no key the query sees).
     if (myq < L) {
-      const size_t row = ((size_t)split * ks.heads + bh) * L + myq;
+      const size_t row = ((size_t)split * ks.heads + bh) * Lmax + myq;  // [split][head][Lmax]
       float* po = ks.part + row * D;
 #pragma unroll
       for (int c = 0; c < NCB; ++c)
@@ -409,17 +409,32 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
 }
 
 // O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the key splits
-// (M = max_s m_s), rounded once to bf16; one thread per (head, row, 8 channels).
+// (M = max_s m_s), rounded once to bf16; one thread per (head, row, 8 channels)
+// of the shares' [head][L] rows.  Token-packed sequences (vs.cu_q non-null)
+// place row `row` of head bh = b * H + h at token cu_q[b] + row, up to that
+// sequence's length.  A row that saw no key gives 0 and an LSE of -inf.
 template <int D>
 __global__ __launch_bounds__(256) void online_combine_kernel(KeySplit ks, uint16_t* __restrict__ out,
                                                              float* __restrict__ lse, HeadMap hm,
-                                                             int L) {
+                                                             int L, VarSeqs vs) {
   constexpr int C8 = D / 8;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)ks.heads * L * C8) return;
   const int chunk = (int)(i % C8);
   const int64_t rowall = i / C8;  // head * L + row
   const int bh = (int)(rowall / L), row = (int)(rowall - (int64_t)bh * L);
+  int64_t orow, lrow;  // out element offset of the row, lse index
+  if (vs.cu_q != nullptr) {
+    const int b = bh / hm.H, h = bh - b * hm.H;
+    const int qs = min(max(vs.cu_q[b], 0), vs.total_q);
+    const int qe = min(max(vs.cu_q[b + 1], qs), vs.total_q);
+    if (row >= min(qe - qs, L)) return;  // past this sequence's queries
+    orow = (int64_t)(qs + row) * hm.o.ld + (int64_t)h * hm.o.h;
+    lrow = (int64_t)(qs + row) * hm.H + h;
+  } else {
+    orow = hm.o_off(bh) + (int64_t)row * hm.o.ld;
+    lrow = (int64_t)(hm.bh0 + bh) * L + row;
+  }
   const size_t plane = (size_t)ks.heads * L;  // rows per split
   float M = -INFINITY;
   for (int sp = 0; sp < ks.n; ++sp) M = fmaxf(M, ks.stats[2 * (sp * plane + rowall)]);
@@ -434,12 +449,11 @@ __global__ __launch_bounds__(256) void online_combine_kernel(KeySplit ks, uint16
     a += w * p[0];
     b += w * p[1];
   }
-  const float inv = 1.f / den;
+  const float inv = den > 0.f ? 1.f / den : 0.f;
   const u32x4 wds = {pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv),
                      pack_bf16x2(b[0] * inv, b[1] * inv), pack_bf16x2(b[2] * inv, b[3] * inv)};
-  *(u32x4*)(out + hm.o_off(bh) + (int64_t)row * hm.o.ld + 8 * chunk) = wds;
-  if (lse != nullptr && chunk == 0)
-    lse[(int64_t)(hm.bh0 + bh) * L + row] = (M + log2f(den)) * 0.6931471805599453f;
+  *(u32x4*)(out + orow + 8 * chunk) = wds;
+  if (lse != nullptr && chunk == 0) lse[lrow] = (M + log2f(den)) * 0.6931471805599453f;
 }
 
 template <int D, int MASK, int LAYOUT>
@@ -492,13 +506,14 @@ hipError_t launch_online(const void* q, const void* k, const void* v, void* out,
 }
 
 hipError_t launch_online_combine(const KeySplit& ks, void* out, float* lse, const HeadMap& hm,
-                                 int L, int d, hipStream_t s) {
+                                 int L, int d, const VarSeqs& vs, hipStream_t s) {
   const int64_t n = (int64_t)ks.heads * L * (d / 8);
   const dim3 grid((unsigned)((n + 255) / 256)), block(256);
   KeySplit k = ks;
   HeadMap m = hm;
+  VarSeqs v = vs;
   uint16_t* op = (uint16_t*)out;
-  void* args[] = {&k, &op, &lse, &m, &L};
+  void* args[] = {&k, &op, &lse, &m, &L, &v};
   switch (d) {
     case 32: return hipLaunchKernel((const void*)&online_combine_kernel<32>, grid, block, args, 0, s);
     case 64: return hipLaunchKernel((const void*)&online_combine_kernel<64>, grid, block, args, 0, s);
@@ -507,13 +522,12 @@ hipError_t launch_online_combine(const KeySplit& ks, void* out, float* lse, cons
   }
 }
 
-int online_split(int64_t BH, int64_t L, int d) {
-  const int64_t wgs = BH * ((L + kBM - 1) / kBM);  // workgroups without a split
+int online_split(int64_t BH, int64_t Lq, int64_t Lk) {
+  const int64_t wgs = BH * ((Lq + kBM - 1) / kBM);  // workgroups without a split
   if (wgs * 2 > kValuesTargetWorkgroups) return 1;
   int64_t s = std::min<int64_t>(kValuesTargetWorkgroups / wgs, kOnlineMaxSplit);
   // Each share keeps at least two key blocks per group.
-  s = std::min<int64_t>(s, (L + kBN - 1) / kBN / (2 * 2));
-  (void)d;
+  s = std::min<int64_t>(s, (Lk + kBN - 1) / kBN / (2 * 2));
   return s >= 2 ? (int)s : 1;
 }
 

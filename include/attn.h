@@ -177,8 +177,12 @@ int attn_forward_ex(const void* q, const void* k, const void* v, void* out, floa
  *                   d must be 32, 64 or 128 (the head dims fmha.py's interface
  *                   takes), else ATTN_ERR_UNSUPPORTED_HEAD_DIM.
  *
- * No workspace.  out must not overlap q, k, v or either offsets array (address
- * ranges), nor lse any of them.  Returns ATTN_OK (also when nothing is to be done:
+ * When B * H * ceil(max_seqlen / 128) workgroups would leave most compute
+ * units idle (e.g. decoding a few sequences against long caches) the keys are
+ * split as for attn_forward, using the per-stream workspace buffer:
+ * splits * B * H * max_seqlen * (d + 2) * 4 bytes, splits <= 8.  out must not
+ * overlap q, k, v or either offsets array (address ranges), nor lse any of
+ * them.  Returns ATTN_OK (also when nothing is to be done:
  * B, H, max_seqlen or total zero) or a status code.
  */
 int attn_forward_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -202,7 +206,7 @@ int attn_path_for_head_dim(int64_t d);
  * when few heads split (d <= 128); 0 when none is needed or for an invalid
  * shape.  attn_forward_ex draws at most this for the same B, H, L, d and
  * causal flag (a window can only narrow the key split); attn_forward_varlen
- * draws nothing.  Host-only; makes no HIP call. */
+ * draws what its own comment states.  Host-only; makes no HIP call. */
 int64_t attn_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int causal);
 
 /*

@@ -8,6 +8,7 @@ from .exact import (
     attention,
     attention_rows,
     causal_mask,
+    compressed_causal_mask,
     log_sum_exp,
     logits,
     probabilities,
@@ -21,6 +22,7 @@ __all__ = [
     "attention",
     "attention_rows",
     "causal_mask",
+    "compressed_causal_mask",
     "log_sum_exp",
     "logits",
     "probabilities",

@@ -29,6 +29,9 @@ What it computes, and where the pages define it:
     and window masks (the last query sees the last key, as in decoding against
     a cache); a row that then sees no key (Lq > Lk) outputs 0 and its LSE is
     -inf, as that page's softmax_step guard for an all -inf row gives.
+  * same page, the compressed causal mask of its softmax: with the keys a
+    compression of the queries by cf = Lq // Lk, query i (counted from 0)
+    sees keys j <= (i + 1) // cf - 1; cf = 1 is the causal mask.
 
 The method reaches exactly the plain definition (up to rounding order), so this
 oracle is that definition written out, one step per function, in the pages'
@@ -89,6 +92,16 @@ def window_mask(Z: np.ndarray, query_index: np.ndarray, left, right) -> np.ndarr
     return Z
 
 
+def compressed_causal_mask(Z: np.ndarray, query_index: np.ndarray, cf: int) -> np.ndarray:
+    """Set Z[r, j] = -inf where j > (query_index[r] + 1) // cf - 1 (keys that
+    compress cf queries each, none after the query's own block)."""
+    Z = Z.copy()
+    keys = np.arange(Z.shape[1])[None, :]
+    last = (np.asarray(query_index)[:, None] + 1) // cf - 1
+    Z[keys > last] = -np.inf
+    return Z
+
+
 def softmax_rows(Z: np.ndarray, allow_empty: bool = False) -> np.ndarray:
     """Numerically stable row softmax: exp(Z - rowmax) / rowsum.  A row with
     every key masked is an error unless allow_empty, when it becomes all 0."""
@@ -143,9 +156,28 @@ def _query_positions(Lq: int, Lk: int, rows=None) -> np.ndarray:
     return i + (Lk - Lq)
 
 
+def _positions(causal, Lq: int, Lk: int, rows=None):
+    """What _masked_logits needs to place the rows: key positions, or for the
+    compressed causal mask the rows counted from 0 with the query count."""
+    if isinstance(causal, str):
+        return (np.arange(Lq) if rows is None else np.asarray(rows), Lq)
+    return _query_positions(Lq, Lk, rows)
+
+
+def _may_be_empty(causal, Lq: int, Lk: int) -> bool:
+    """Whether a row can be left with no key (then it is 0, its LSE -inf)."""
+    return Lq > Lk or isinstance(causal, str)
+
+
 def _masked_logits(Q, K, scale, causal, window, query_index):
-    """Logits of the rows at query_index with the causal and window masks."""
+    """Logits of the rows at query_index with the causal and window masks.
+    causal == "compressed": the compressed causal mask; query_index is then a
+    pair (rows counted from 0, Lq) and cf = Lq // Lk."""
     Z = logits(Q, K, scale)
+    if isinstance(causal, str):
+        assert causal == "compressed" and window is None, "compressed causal takes no window"
+        rows, Lq = query_index
+        return compressed_causal_mask(Z, rows, max(1, Lq // max(1, K.shape[0])))
     if causal:
         Z = causal_mask(Z, query_index)
     if window is not None:
@@ -161,8 +193,9 @@ def probabilities(q, k, scale: float, causal: bool = False, window=None) -> np.n
     for b in range(B):
         for h in range(H):
             Z = _masked_logits(_head(q, b, h), _head(k, b, h // g), scale, causal, window,
-                               _query_positions(L, Lk))
-            P[b, h] = (softmax_rows(Z, allow_empty=True) if L > Lk else softmax_rows(Z))
+                               _positions(causal, L, Lk))
+            empty_ok = _may_be_empty(causal, L, Lk)
+            P[b, h] = softmax_rows(Z, allow_empty=True) if empty_ok else softmax_rows(Z)
     return P
 
 
@@ -173,15 +206,16 @@ def attention(q, k, v, scale: float, causal: bool = False, window=None) -> np.nd
     reads key/value head h // (H / H_kv), and Lk keys (Lk may differ from Lq:
     query i stands at key position p = i + Lk - Lq).  window = (left, right)
     restricts query i to keys p - left .. p + right (None on a side:
-    unbounded); causal to keys <= p.  A query with no key left gives 0."""
+    unbounded); causal to keys <= p; causal="compressed" to keys
+    j <= (i + 1) // cf - 1, cf = Lq // Lk.  A query with no key left gives 0."""
     B, H, L, g = _dims(q, k, v)
     Lk = np.shape(k)[2]
     O = np.empty((B, H, L, np.shape(v)[-1]), dtype=np.float64)
     for b in range(B):
         for h in range(H):
             Z = _masked_logits(_head(q, b, h), _head(k, b, h // g), scale, causal, window,
-                               _query_positions(L, Lk))
-            P = softmax_rows(Z, allow_empty=True) if L > Lk else softmax_rows(Z)
+                               _positions(causal, L, Lk))
+            P = softmax_rows(Z, allow_empty=True) if _may_be_empty(causal, L, Lk) else softmax_rows(Z)
             O[b, h] = weighted_values(P, _head(v, b, h // g))
     return O
 
@@ -195,8 +229,9 @@ def log_sum_exp(q, k, scale: float, causal: bool = False, window=None) -> np.nda
     for b in range(B):
         for h in range(H):
             Z = _masked_logits(_head(q, b, h), _head(k, b, h // g), scale, causal, window,
-                               _query_positions(L, Lk))
-            out[b, h] = (row_log_sum_exp(Z, allow_empty=True) if L > Lk else row_log_sum_exp(Z))
+                               _positions(causal, L, Lk))
+            empty_ok = _may_be_empty(causal, L, Lk)
+            out[b, h] = row_log_sum_exp(Z, allow_empty=True) if empty_ok else row_log_sum_exp(Z)
     return out
 
 
@@ -216,7 +251,7 @@ def attention_rows(q, k, v, scale: float, causal: bool, rows, window=None) -> np
         K, V = cache[(b, h // g)]
         Lq, Lk = np.shape(q)[2], np.shape(k)[2]
         Z = _masked_logits(np.asarray(q[b, h, i : i + 1], dtype=np.float64), K, scale, causal,
-                           window, _query_positions(Lq, Lk, [i]))
-        P = softmax_rows(Z, allow_empty=True) if Lq > Lk else softmax_rows(Z)
+                           window, _positions(causal, Lq, Lk, [i]))
+        P = softmax_rows(Z, allow_empty=True) if _may_be_empty(causal, Lq, Lk) else softmax_rows(Z)
         out[r] = weighted_values(P, V)[0]
     return out

@@ -624,3 +624,66 @@ def test_qk_pins_catch_top_left_alignment(monkeypatch):
     assert close(oracle.attention(q, k, v, 0.7, True), want)
     monkeypatch.setattr(oa, "_query_positions", top_left)
     assert not close(oracle.attention(q, k, v, 0.7, True), want)
+
+
+# ---- compressed causal mask (keys compress cf = Lq // Lk queries each) --------
+
+def brute_force_compressed(q, k, v, scale):
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    cf = max(1, Lq // Lk)
+    out = np.zeros((B, H, Lq, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            for i in range(Lq):
+                keys = range(0, min(Lk, (i + 1) // cf))
+                if len(keys) == 0:
+                    continue
+                z = [scale * math.fsum(q[b, h, i, c] * k[b, h, j, c] for c in range(d)) for j in keys]
+                m = max(z)
+                e = [math.exp(x - m) for x in z]
+                tot = math.fsum(e)
+                for c in range(v.shape[-1]):
+                    out[b, h, i, c] = math.fsum(e[t] * v[b, h, j, c] for t, j in enumerate(keys)) / tot
+    return out
+
+
+@pytest.mark.parametrize("Lq,Lk", [(12, 4), (10, 3), (7, 7), (9, 2)])
+def test_compressed_causal_brute_force(Lq, Lk):
+    q, k, v = rnd((1, 2, Lq, 4), 140 + Lq), rnd((1, 2, Lk, 4), 141 + Lk), rnd((1, 2, Lk, 3), 142)
+    assert close(oracle.attention(q, k, v, 0.6, "compressed"), brute_force_compressed(q, k, v, 0.6))
+
+
+def test_compressed_causal_with_cf_one_is_causal():
+    q, k, v = rnd((1, 2, 9, 4), 143), rnd((1, 2, 9, 4), 144), rnd((1, 2, 9, 4), 145)
+    assert close(oracle.attention(q, k, v, 0.5, "compressed"), oracle.attention(q, k, v, 0.5, True))
+    assert close(oracle.log_sum_exp(q, k, 0.5, "compressed"), oracle.log_sum_exp(q, k, 0.5, True))
+
+
+def test_compressed_causal_closed_forms():
+    # cf = 3: query i sees keys 0 .. (i + 1) // 3 - 1; rows 0 and 1 see none;
+    # at scale 0 each other row is the mean of that prefix of V, its LSE the
+    # log of the prefix length
+    Lq, Lk = 12, 4
+    q, k, v = rnd((1, 1, Lq, 4), 146), rnd((1, 1, Lk, 4), 147), rnd((1, 1, Lk, 4), 148)
+    o = oracle.attention(q, k, v, 0.0, "compressed")[0, 0]
+    lse = oracle.log_sum_exp(q, k, 0.0, "compressed")[0, 0]
+    for i in range(Lq):
+        n = (i + 1) // 3
+        if n == 0:
+            assert np.array_equal(o[i], np.zeros(4)) and lse[i] == -np.inf
+        else:
+            assert close(o[i], v[0, 0, :n].mean(axis=0)) and close(lse[i], np.log(n))
+
+
+@pytest.mark.parametrize("shift", [-1, 1])
+def test_compressed_causal_pins_catch_off_by_one(shift, monkeypatch):
+    q, k, v = rnd((1, 1, 12, 4), 149), rnd((1, 1, 4, 4), 150), rnd((1, 1, 4, 3), 151)
+    want = brute_force_compressed(q, k, v, 0.6)
+    assert close(oracle.attention(q, k, v, 0.6, "compressed"), want)
+    ref = oa.compressed_causal_mask
+
+    def shifted(Z, qi, cf):
+        return ref(Z, np.asarray(qi) + shift * cf, cf)
+    monkeypatch.setattr(oa, "compressed_causal_mask", shifted)
+    assert not close(oracle.attention(q, k, v, 0.6, "compressed"), want)

@@ -23,6 +23,11 @@ ATTN_ERR_WORKSPACE = 7
 ATTN_ERR_HIP = 8
 ATTN_ERR_TOO_LARGE = 9
 ATTN_ERR_BAD_STRIDE = 10
+ATTN_ERR_BAD_MASK = 11
+
+ATTN_MASK_NONE = 0
+ATTN_MASK_CAUSAL = 1
+ATTN_MASK_COMPRESSED_CAUSAL = 2
 
 ATTN_PATH_NONE = -1
 ATTN_PATH_ONLINE = 0

@@ -105,7 +105,7 @@ def _window_args(window):
 
 
 def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
-                     max_seqlen: int, scale: float | None = None, causal: bool = False,
+                     max_seqlen: int, scale: float | None = None, causal: bool | str = False,
                      out: torch.Tensor | None = None, return_lse: bool = False,
                      window: tuple | None = None, cu_seqlens_k: torch.Tensor | None = None,
                      max_seqlen_k: int | None = None):
@@ -117,9 +117,18 @@ def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
     ``cu_seqlens_k`` (and ``max_seqlen_k``) the keys have offsets of their own
     (cross-attention, or a few queries against a cache; query i then stands at
     key position i + Lk - Lq for causal and windows); otherwise they share the
-    query offsets.  d must be 32, 64 or 128.  Returns out [total, H, d] (and lse
-    float32 [total, H] with ``return_lse``); rows of tokens in no sequence are
-    left as they were, rows that see no key are 0."""
+    query offsets.  ``causal="compressed"`` is that example's compressed causal
+    mask: with cf = max(1, Lq // Lk) per sequence, query i sees keys
+    j <= (i + 1) // cf - 1 (no window allowed).  d must be 32, 64 or 128.
+    Returns out [total, H, d] (and lse float32 [total, H] with ``return_lse``);
+    rows of tokens in no sequence are left as they were, rows that see no key
+    are 0."""
+    if isinstance(causal, str):
+        if causal != "compressed":
+            raise ValueError(f"causal must be a bool or 'compressed', got {causal!r}")
+        mask = _lib.ATTN_MASK_COMPRESSED_CAUSAL
+    else:
+        mask = _lib.ATTN_MASK_CAUSAL if causal else _lib.ATTN_MASK_NONE
     if not isinstance(q, torch.Tensor) or q.dim() != 3:
         raise ValueError("q must be a 3-D tensor [total, H, d]")
     total, H, d = q.shape
@@ -164,7 +173,7 @@ def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqle
           out.data_ptr(), lse.data_ptr() if lse is not None else None, cu.data_ptr(), B,
           int(max_seqlen), total, cuk.data_ptr() if cuk is not None else None,
           int(max_seqlen_k) if cuk is not None else 0, total_k, H, H_kv, d, st(q), st(k), st(v),
-          st(out), float(scale), 1 if causal else 0, wl, wr)
+          st(out), float(scale), mask, wl, wr)
     return (out, lse) if return_lse else out
 
 

@@ -307,6 +307,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_WORKSPACE: return "workspace allocation failed";
     case ATTN_ERR_HIP: return "a HIP launch or runtime call failed";
     case ATTN_ERR_TOO_LARGE: return "problem too large: one head exceeds 32-bit byte offsets, or L > 31744 with d > 128";
+    case ATTN_ERR_BAD_MASK: return "the compressed causal mask takes no window";
     case ATTN_ERR_BAD_STRIDE:
       return "bad strides: negative, not a multiple of 8 elements, a row stride below d, or an "
              "output layout whose elements overlap";
@@ -427,6 +428,8 @@ int attn_forward_varlen(const void* q, const void* k, const void* v, void* out, 
       total_k < 0)
     return ATTN_ERR_BAD_SHAPE;
   if (window_left < -1 || window_right < -1) return ATTN_ERR_BAD_SHAPE;
+  const bool compressed = causal == ATTN_MASK_COMPRESSED_CAUSAL;
+  if (compressed && (window_left != -1 || window_right != -1)) return ATTN_ERR_BAD_MASK;
   int64_t rows = 0, elems = 0, bytes = 0, bh = 0, slots = 0;
   if (__builtin_mul_overflow(total, H, &rows) || __builtin_mul_overflow(rows, d, &elems) ||
       __builtin_mul_overflow(elems, (int64_t)2, &bytes) || __builtin_mul_overflow(B, H, &bh) ||
@@ -436,7 +439,8 @@ int attn_forward_varlen(const void* q, const void* k, const void* v, void* out, 
   if (attn_path_for_head_dim(d) != ATTN_PATH_ONLINE) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
   if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
   if (rows == 0 || slots == 0) return ATTN_OK;
-  if (!q || !k || !v || !out || !cu_seqlens) return ATTN_ERR_NULL_PTR;
+  // With no key tokens at all, k and v are never read and may be NULL.
+  if (!q || !out || !cu_seqlens || (total_k > 0 && (!k || !v))) return ATTN_ERR_NULL_PTR;
 
   // Operands as [1, heads, tokens] views: strides {token, head} given, channels contiguous.
   auto make = [&](const int64_t* st, int64_t heads, int64_t tokens) {
@@ -493,8 +497,9 @@ int attn_forward_varlen(const void* q, const void* k, const void* v, void* out, 
   hm.k = {0, vk.st[1], (int)vk.st[2]};
   hm.v = {0, vv.st[1], (int)vv.st[2]};
   hm.o = {0, vo.st[1], (int)vo.st[2]};
-  const attn::Band band =
+  attn::Band band =
       attn::make_band(window_left, window_right, causal != 0, std::max(max_seqlen, max_seqlen_k) + 1);
+  band.compressed = compressed ? 1 : 0;
   const float sl2 = scale * 1.4426950408889634f;
   const attn::VarSeqs vs{cu_seqlens, cu_seqlens_k, (int)total, (int)total_k, (int)max_seqlen_k};
   // Few (sequence, head) pairs -- e.g. decoding against long caches: split the keys.

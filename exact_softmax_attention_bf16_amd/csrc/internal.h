@@ -49,15 +49,20 @@ inline bool is_plain(const HeadMap& m, int L, int d) {
 // Keys each query sees: key j is allowed for query i iff
 // i - left <= j <= i + right (and j < L).  An unbounded side holds kNoLimit;
 // causal attention is {kNoLimit, 0}.
+// compressed != 0 selects the compressed causal mask instead (token-packed
+// sequences only): with cf = max(1, Lq / Lk), key j is allowed for query i iff
+// j <= (i + 1) / cf - 1, positions counted from 0 within the sequence.
 constexpr int kNoLimit = 1 << 30;
 struct Band {
   int left, right;
+  int compressed;
 };
 inline Band make_band(int64_t left, int64_t right, bool causal, int64_t L) {
   Band b;
   b.left = (left < 0 || left >= L) ? kNoLimit : (int)left;
   b.right = (right < 0 || right >= L) ? kNoLimit : (int)right;
   if (causal) b.right = 0;
+  b.compressed = 0;
   return b;
 }
 __host__ __device__ inline bool band_is_full(const Band& b) {

@@ -71,9 +71,11 @@ struct OnlineSmem {
 enum { kPlain = 0, kStrided = 1, kVarlen = 2 };
 // MASK: which keys below L each query i may see -- kAllKeys: all of them;
 // kCausal: j <= i; kWindow: i - left <= j <= i + right (band.left, band.right,
-// either side possibly unbounded).  Causal has its own instantiation so that
-// it carries no left-side tests.
-enum { kAllKeys = 0, kCausal = 1, kWindow = 2 };
+// either side possibly unbounded); kCompressed (token-packed sequences only):
+// j <= (i + 1) / cf - 1 with cf = max(1, Lq / Lk), the compressed causal mask
+// of fmha.py's softmax, each key standing for cf consecutive queries.  Causal
+// has its own instantiation so that it carries no left-side tests.
+enum { kAllKeys = 0, kCausal = 1, kWindow = 2, kCompressed = 3 };
 template <int D, int MASK, int LAYOUT>
 __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
@@ -110,10 +112,11 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   const uint32_t lid = ks.n > 1 ? lid0 / (uint32_t)ks.n : lid0;
   const int bh = lid / nqb;
   int qb = lid % nqb;
-  if (MASK == kCausal) qb = nqb - 1 - qb;  // the longest rows start first
+  if (MASK == kCausal || MASK == kCompressed) qb = nqb - 1 - qb;  // the longest rows start first
   constexpr bool BANDED = MASK != kAllKeys, HAS_LEFT = MASK == kWindow;
   int left = HAS_LEFT ? band.left : kNoLimit;
   int right = MASK == kCausal ? 0 : band.right;
+  int cf = 1;  // kCompressed: queries per key
 
   constexpr bool PLAIN = LAYOUT == kPlain;
   const int ldq = PLAIN ? D : hm.q.ld, ldk = PLAIN ? D : hm.k.ld, ldv = PLAIN ? D : hm.v.ld;
@@ -134,10 +137,14 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
     const int ks0 = min(max(cuk[b], 0), tk);
     const int ke = min(max(cuk[b + 1], ks0), tk);
     Lk = min(ke - ks0, vs.max_k);
-    // Query i stands at key position i + Lk - L: shift the band by that.
-    const int shift = Lk - L;
-    if (left < kNoLimit) left -= shift;
-    if (right < kNoLimit) right += shift;
+    if constexpr (MASK == kCompressed) {
+      cf = Lk > 0 && L / Lk > 1 ? L / Lk : 1;
+    } else {
+      // Query i stands at key position i + Lk - L: shift the band by that.
+      const int shift = Lk - L;
+      if (left < kNoLimit) left -= shift;
+      if (right < kNoLimit) right += shift;
+    }
     qoff = (int64_t)qs * ldq + (int64_t)h * hm.q.h;
     koff = (int64_t)ks0 * ldk + (int64_t)(h / hm.group) * hm.k.h;
     voff = (int64_t)ks0 * ldv + (int64_t)(h / hm.group) * hm.v.h;
@@ -162,6 +169,9 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
 
   const int q0 = qb * kBM + wave * 32;  // first query of this wave
   const int myq = q0 + c32;             // this lane's query
+  // The last key query i may see (kNoLimit-sized when unbounded).
+  auto last_key = [&](int i) { return MASK == kCompressed ? (i + 1) / cf - 1 : i + right; };
+  const int my_last = last_key(myq);
 
   // Q fragments: B operand of S^T, lane holds Q[myq][16 s + 8 h .. + 8].
   bf16x8 qf[NS];
@@ -171,7 +181,7 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
 
   // Key blocks t0 .. t0 + ntiles - 1 meet the band of this workgroup's queries.
   const int kstart = HAS_LEFT ? max(0, qb * kBM - left) : 0;
-  const int kend = BANDED ? min(Lk, qb * kBM + kBM + right) : Lk;
+  const int kend = BANDED ? min(Lk, last_key(qb * kBM + kBM - 1) + 1) : Lk;
   int t0 = kstart / kBN;
   int ntiles = max(0, (kend + kBN - 1) / kBN - t0);
   if (ks.n > 1) {  // this split's share of those blocks (possibly none)
@@ -243,7 +253,7 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
     }
     const int kbase = t * kBN;
     // This wave's 32 queries see some key of the block.
-    const bool active = t < tend && (!BANDED || kbase <= q0 + 31 + right) &&
+    const bool active = t < tend && (!BANDED || kbase <= last_key(q0 + 31)) &&
                         (!HAS_LEFT || kbase + kBN - 1 >= q0 - left);
     if (active) {
       // S^T block: 64 keys x 32 queries, two 32-key halves.
@@ -261,7 +271,7 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
       // Softmax update for this lane's query over its 32 of the 64 keys.  The
       // maximum is taken on the raw scores (scaled afterwards; the sign of sl2
       // picks max or min), and y - m is one FMA: p = 2^(s * sl2 - m).
-      const bool need_mask = (kbase + kBN > Lk) || (BANDED && kbase + kBN - 1 > q0 + right) ||
+      const bool need_mask = (kbase + kBN > Lk) || (BANDED && kbase + kBN - 1 > last_key(q0)) ||
                              (HAS_LEFT && kbase < q0 + 31 - left);
       float tmax;
       if (need_mask) {
@@ -271,7 +281,7 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int key = kbase + kb * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-            const bool off = key >= Lk || (BANDED && key > myq + right) ||
+            const bool off = key >= Lk || (BANDED && key > my_last) ||
                              (HAS_LEFT && key < myq - left);
             s[kb][j] = off ? -INFINITY : s[kb][j] * sl2;
             tmax = fmaxf(tmax, s[kb][j]);
@@ -476,15 +486,21 @@ hipError_t launch_m(const void* q, const void* k, const void* v, void* out, floa
                     const VarSeqs& vs, KeySplit ks, hipStream_t s) {
   if (vs.cu_q != nullptr)
     return launch_one<D, MASK, kVarlen>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
-  if (is_plain(hm, L, D))
-    return launch_one<D, MASK, kPlain>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
-  return launch_one<D, MASK, kStrided>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
+  if constexpr (MASK == kCompressed) {
+    return hipErrorInvalidValue;  // token-packed sequences only
+  } else {
+    if (is_plain(hm, L, D))
+      return launch_one<D, MASK, kPlain>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
+    return launch_one<D, MASK, kStrided>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
+  }
 }
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* out, float* lse,
                     const HeadMap& hm, int BH, int L, float sl2, Band band,
                     const VarSeqs& vs, KeySplit ks, hipStream_t s) {
+  if (band.compressed)
+    return launch_m<D, kCompressed>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
   if (band_is_full(band))
     return launch_m<D, kAllKeys>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
   if (band_is_causal(band))

@@ -50,8 +50,20 @@ enum {
   ATTN_ERR_WORKSPACE = 7,            /* the stream-ordered workspace allocation failed */
   ATTN_ERR_HIP = 8,                  /* a HIP launch or runtime call failed       */
   ATTN_ERR_TOO_LARGE = 9,            /* one head exceeds the kernels' 32-bit byte offsets */
-  ATTN_ERR_BAD_STRIDE = 10           /* attn_forward_ex: a stride is negative or not a multiple
+  ATTN_ERR_BAD_STRIDE = 10,          /* attn_forward_ex: a stride is negative or not a multiple
                                         of 8, a row stride is below d, or out's elements overlap */
+  ATTN_ERR_BAD_MASK = 11             /* attn_forward_varlen: the compressed causal mask
+                                        combined with a window                   */
+};
+
+/* Values of the `causal` argument.  attn_forward and attn_forward_ex treat
+ * every nonzero value as ATTN_MASK_CAUSAL (with equal query and key lengths the
+ * compressed causal mask is the causal mask); attn_forward_varlen also takes
+ * ATTN_MASK_COMPRESSED_CAUSAL. */
+enum {
+  ATTN_MASK_NONE = 0,
+  ATTN_MASK_CAUSAL = 1,
+  ATTN_MASK_COMPRESSED_CAUSAL = 2
 };
 
 /* Kernel paths chosen by head dimension. */
@@ -152,6 +164,14 @@ int attn_forward_ex(const void* q, const void* k, const void* v, void* out, floa
  * masks.  A query left with no key (possible when Lq > Lk) gives 0 and an LSE
  * of -inf.
  *
+ * causal == ATTN_MASK_COMPRESSED_CAUSAL selects the compressed causal mask of
+ * fmha.py's softmax (its compressed-causal mask type), where the keys compress
+ * the queries: with cf = Lq / Lk (integer division, at least 1) per sequence,
+ * key j is allowed for query i iff j <= (i + 1) / cf - 1, positions counted
+ * from 0 within the sequence (no bottom-right shift).  The first cf - 1
+ * queries see no key and give 0 (LSE -inf).  It takes no window
+ * (ATTN_ERR_BAD_MASK otherwise).  Any other nonzero value is the causal mask.
+ *
  *   q, out        : [total, H, d] views; k, v : [total_k, H_kv, d] views.  Each is
  *                   a device pointer to element [0,0,0] plus two element strides
  *                   (token, head) in a host array of 2 int64_t; NULL means packed
@@ -172,6 +192,8 @@ int attn_forward_ex(const void* q, const void* k, const void* v, void* out, floa
  *   max_seqlen_k,   cu_seqlens), the longest key length and the key tokens in
  *   total_k         the k and v views; cu_seqlens_k NULL: keys use cu_seqlens,
  *                   max_seqlen and total (self-attention), the other two ignored.
+ *                   With total_k == 0, k and v may be NULL (never read): every
+ *                   query sees no key and gives 0.
  *   H, H_kv, d, scale, causal, window_left, window_right, stream : as for
  *                   attn_forward_ex, positions counted within each sequence;
  *                   d must be 32, 64 or 128 (the head dims fmha.py's interface

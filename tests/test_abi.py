@@ -58,7 +58,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(11):
+    for code in range(12):
         s = eab.status_string(code)
         assert s and s != "unknown status"
     assert eab.status_string(99) == "unknown status"
@@ -357,6 +357,8 @@ def test_varlen_nothing_to_do():
     (dict(out=A + 8), "MISALIGNED"),
     (dict(cu=A + 192 * MB + 64), "ALIAS"), (dict(lse=A + 192 * MB), "ALIAS"),
     (dict(out=A + 64), "ALIAS"),
+    (dict(causal=2, wl=5), "BAD_MASK"), (dict(causal=2, wr=0), "BAD_MASK"),
+    (dict(causal=2, wl=0, wr=7, B=-1), "BAD_SHAPE"),
 ])
 def test_varlen_checks(kw, code):
     assert fwd_var(**kw) == getattr(_lib, "ATTN_ERR_" + code)
@@ -417,3 +419,30 @@ def test_varlen_key_offsets_layout_accepted():
     assert fwd_var(q=A, k=A + T, v=A + 2 * T, out=A + 3 * T, cu=A + 4 * T, cuk=A + 5 * T,
                    B=1, max_seqlen=8, total=8, max_k=1 << 22, total_k=1 << 22,
                    ks=st2(1024, 64), vs=st2(1024, 64)) == _lib.ATTN_ERR_TOO_LARGE
+
+
+def test_varlen_compressed_causal_is_accepted():
+    # every check passes; a row stride too wide for 32-bit offsets shows it
+    T = 1 << 40
+    assert fwd_var(q=A, k=A + T, v=A + 2 * T, out=A + 3 * T, cu=A + 4 * T, cuk=A + 5 * T,
+                   causal=_lib.ATTN_MASK_COMPRESSED_CAUSAL, B=1, max_seqlen=8, total=8,
+                   max_k=1 << 22, total_k=1 << 22, ks=st2(1024, 64),
+                   vs=st2(1024, 64)) == _lib.ATTN_ERR_TOO_LARGE
+
+
+def test_python_varlen_rejects_unknown_mask_names():
+    import torch
+    t = torch.zeros(4, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="compressed"):
+        eab.attention_varlen(t, t, t, torch.zeros(2, dtype=torch.int32), 4, causal="sliding")
+
+
+def test_varlen_without_key_tokens_takes_null_keys():
+    # total_k == 0: k and v are never read, NULL is accepted (the too-wide q row
+    # stride shows every earlier check passed); with keys, NULL k is an error
+    T = 1 << 40
+    kw = dict(q=A, out=A + 3 * T, cu=A + 4 * T, cuk=A + 5 * T, B=1, max_seqlen=8, total=8,
+              max_k=0, total_k=0, qs=st2(1 << 22, 64))
+    assert fwd_var(k=None, v=None, **kw) == _lib.ATTN_ERR_TOO_LARGE
+    kw.update(max_k=4, total_k=4)
+    assert fwd_var(k=None, v=A + T, **kw) == _lib.ATTN_ERR_NULL_PTR

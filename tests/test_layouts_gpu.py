@@ -435,3 +435,45 @@ def test_queries_past_the_keys_are_zero():
     torch.cuda.synchronize()
     assert bool((o[:200] == 0).all()) and bool(torch.isneginf(lse[:200]).all())
     check_qk(seqs, o.cpu(), lse.cpu(), cu_q, 0.125, True, None)
+
+
+# ---- the compressed causal mask (keys compress the queries) ------------------
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_varlen_compressed_causal(d):
+    """cf = Lq // Lk per sequence (1 when Lq < Lk or Lq == Lk): query i sees keys
+    j <= (i + 1) // cf - 1; the first cf - 1 queries see none and give 0."""
+    from exact_softmax_attention_bf16_amd import attention_varlen
+    q_len = [300, 1000, 128, 37, 64, 257, 1, 0, 95]
+    k_len = [100, 64, 128, 500, 0, 16, 1, 7, 32]
+    H, H_kv = 4, 2
+    seqs, q, k, v, cu_q, cu_k = qk_batch(q_len, k_len, H, H_kv, d, 800 + d)
+    s = 1.0 / math.sqrt(d)
+    o, lse = attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu_q.to(DEV), max(q_len), scale=s,
+                              causal="compressed", return_lse=True, cu_seqlens_k=cu_k.to(DEV),
+                              max_seqlen_k=max(k_len))
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    check_qk(seqs, o, lse, cu_q, s, "compressed", None)
+    # sequence 0 (cf = 3): queries 0 and 1 see no key, query 2 sees key 0 alone
+    assert bool((o[:2] == 0).all()) and bool(torch.isneginf(lse[:2]).all())
+    assert torch.equal(o[2], seqs[0][2][0, :, 0].repeat_interleave(H // H_kv, 0))
+
+
+def test_varlen_compressed_causal_with_key_split():
+    """One long sequence: few workgroups, so its keys are split; cf = 4."""
+    from exact_softmax_attention_bf16_amd import attention_varlen
+    seqs, q, k, v, cu_q, cu_k = qk_batch([4096], [1024], 1, 1, 64, 900)
+    o, lse = attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu_q.to(DEV), 4096,
+                              causal="compressed", return_lse=True, cu_seqlens_k=cu_k.to(DEV),
+                              max_seqlen_k=1024)
+    torch.cuda.synchronize()
+    check_qk(seqs, o.cpu(), lse.cpu(), cu_q, 0.125, "compressed", None)
+
+
+def test_varlen_compressed_causal_equal_lengths_is_causal_bitwise():
+    from exact_softmax_attention_bf16_amd import attention_varlen
+    seqs, q, k, v, cu = varlen_batch([333, 128, 5], 2, 2, 64, 950)
+    a = attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), 333, causal=True)
+    b = attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), 333, causal="compressed")
+    assert torch.equal(a, b)

@@ -128,3 +128,48 @@ def test_random_varlen(case):
         ok, a, r = within_bar(to_f64(got), ref)
         assert ok, (i, a, r)
         assert _lse_ok(gl, oracle.log_sum_exp(to_f64(q), to_f64(k), s, causal, window)), i
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_random_varlen_compressed(case):
+    """The compressed causal mask on random batches: each sequence's keys are
+    about Lq / cf of its queries (cf random in 1..16, lengths not multiples)."""
+    from exact_softmax_attention_bf16_amd import attention_varlen
+    rng = np.random.default_rng(9700 + case)
+    d = int(rng.choice([32, 64, 128]))
+    nseq = int(rng.integers(1, 6))
+    H_kv = int(rng.integers(1, 3))
+    H = H_kv * int(rng.integers(1, 4))
+    q_len = [int(x) for x in rng.integers(0, 700, nseq)]
+    k_len = [max(0, lq // int(rng.integers(1, 17)) + int(rng.integers(-2, 3))) for lq in q_len]
+    seqs = []
+    for i in range(nseq):
+        q = make_qkv(1, H, q_len[i], d, 50000 + 10 * case + i)[0]
+        _, k, v = make_qkv(1, H_kv, k_len[i], d, 60000 + 10 * case + i)
+        seqs.append((q, k, v))
+    if sum(q_len) == 0:
+        return
+    pack = lambda j, heads: torch.cat([s[j][0].transpose(0, 1) for s in seqs], 0).reshape(-1, heads, d).contiguous()
+    cu_q = torch.tensor([0] + list(np.cumsum(q_len)), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(np.cumsum(k_len)), dtype=torch.int32)
+    print(f"[random compressed {case}] d={d} H={H}/{H_kv} q={q_len} k={k_len}", flush=True)
+    o, lse = attention_varlen(pack(0, H).to(DEV), pack(1, H_kv).to(DEV), pack(2, H_kv).to(DEV),
+                              cu_q.to(DEV), max(q_len), causal="compressed", return_lse=True,
+                              cu_seqlens_k=cu_k.to(DEV), max_seqlen_k=max(k_len + [1]))
+    torch.cuda.synchronize()
+    s = 1.0 / math.sqrt(d)
+    for i, (q, k, v) in enumerate(seqs):
+        a0, a1 = int(cu_q[i]), int(cu_q[i + 1])
+        if a1 == a0:
+            continue
+        got = o[a0:a1].transpose(0, 1).unsqueeze(0).cpu()
+        gl = to_f64(lse[a0:a1].transpose(0, 1).unsqueeze(0))
+        if k_len[i] == 0:
+            assert bool((got == 0).all()) and bool(np.isneginf(gl).all()), i
+            continue
+        ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), s, "compressed")
+        ok, a, r = within_bar(to_f64(got), ref)
+        assert ok, (i, a, r)
+        lref = oracle.log_sum_exp(to_f64(q), to_f64(k), s, "compressed")
+        assert bool((to_f64(got)[0][np.isneginf(lref)[0]] == 0).all()), i  # rows with no key
+        assert _lse_ok(gl, lref), i

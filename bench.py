@@ -235,6 +235,22 @@ def main() -> int:
         log("[bench] non-finite output")
         return 1
 
+    # Per-call spread, after the timed region: K more calls, each between two
+    # events on the stream the kernels run on.
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
+        attention(qd, kd, vd, scale=w.scale, causal=w.causal, out=out)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(a.elapsed_time(b) for a, b in ev)
+    med = per_call[len(per_call) // 2] if len(per_call) % 2 else \
+        0.5 * (per_call[len(per_call) // 2 - 1] + per_call[len(per_call) // 2])
+    log(f"[bench] per call over {len(per_call)} more calls: median {med:.4f} ms, "
+        f"min {per_call[0]:.4f} ms")
+
     # Roofline of the dominant kernel.
     dom = max((n for n in kt if kernel_flops(n, w) > 0), key=lambda n: kt[n][0])
     tot, cnt = kt[dom]
@@ -266,6 +282,10 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "ms_per_call_median": round(med, 5),
+        "ms_per_call_min": round(per_call[0], 5),
+        "pct_bf16_mfma_peak_at_min": round(100.0 * flops / (per_call[0] * 1e-3) / 1e12
+                                           / PEAK_BF16_TFLOPS, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": vs,

@@ -15,9 +15,13 @@
 // run.  In the last sub-step the wave waits for its own loads of the next
 // stage, the workgroup meets at one barrier (next stage complete everywhere,
 // current stage no longer read), the first fragments of the next step are
-// read, and the loads two steps ahead go into the stage just drained, one
-// after each pair of the sub-step's MFMAs (issued as one burst they hold up
-// the MFMAs behind them while the address queue drains).
+// read, and the A loads two steps ahead go into the stage just drained, one
+// after each pair of the sub-step's MFMAs; the matching B loads follow the
+// same way in the next step's first sub-step (issued as one burst they hold
+// up the MFMAs behind them while the address queue drains; measured on the
+// values pass: all 16 in the last sub-step 789 us, A there and B in the next
+// first sub-step 771 us, B spread further into the second sub-step 808 us --
+// later loads leave too little of the step to cover their latency).
 //
 // The compiler guards LDS reads against direct-to-LDS loads still in flight:
 // a read it cannot prove disjoint from them gets a wait for all of them.
@@ -267,13 +271,33 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
   read_a_step(f, sm.a[0]);
   read_b(f[0].b, sm.b[0], 0);
   la.issue(k1, sm.a[1], wave);
-  lb.issue(k1, sm.b[1], wave);
+  // The B loads of step kt + 1 are issued during step kt's first sub-step
+  // (into the stage step kt does not read; step 1's from step 0), so that each
+  // sub-step carries at most 8 loads per wave: 16 at once, from all four waves
+  // right after the barrier, back up the address queue and hold the MFMAs
+  // behind them.
+  int kb_pend = k1;  // K offset of the B loads the next first sub-step issues
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
     const char* sb = sm.b[st];
     bx.step(k_first + kt, kt == 0);
+    read_b(f[1].b, sb, 1);
+    {
+      bf16x8 b0[4];
 #pragma unroll
-    for (int ss = 0; ss < 3; ++ss) {
+      for (int j = 0; j < 4; ++j) b0[j] = bx(f[0].b[j], j);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int i = p >> 1, j0 = 2 * (p & 1);
+        acc[i][j0] = mfma32x32x16(f[0].a[i], b0[j0], acc[i][j0]);
+        acc[i][j0 + 1] = mfma32x32x16(f[0].a[i], b0[j0 + 1], acc[i][j0 + 1]);
+        lb.issue_one(lb.r, kb_pend, sm.b[st ^ 1], wave, p);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int ss = 1; ss < 3; ++ss) {
       read_b(f[ss + 1].b, sb, ss + 1);
       mma_substep(acc, f[ss], bx);
       sched_substep_b_only();
@@ -285,8 +309,9 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
     read_a_step(f, sm.a[st ^ 1]);
     read_b(f[0].b, sm.b[st ^ 1], 0);
     const int k2 = kb + (kt + 2 < nk ? kt + 2 : nk - 1) * kStepK;  // past the end: reload, unused
-    // The reads above, then the sub-step's MFMAs in pairs with one load of each
-    // operand after each pair.
+    // The reads above, then the sub-step's MFMAs in pairs with one A load
+    // after each pair; the B loads follow in the next step's first sub-step
+    // (none after the last step).
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 lbf[4];
 #pragma unroll
@@ -298,9 +323,9 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
       acc[i][j0] = mfma32x32x16(last.a[i], lbf[j0], acc[i][j0]);
       acc[i][j0 + 1] = mfma32x32x16(last.a[i], lbf[j0 + 1], acc[i][j0 + 1]);
       la.issue_one(k2, sm.a[st], wave, p);
-      lb.issue_one(lb.r, k2, sm.b[st], wave, p);
     }
     __builtin_amdgcn_sched_barrier(0);
+    kb_pend = k2;
   }
   wait_vmem();  // no LDS writes in flight past the loop
 }

@@ -15,13 +15,15 @@
 // run.  In the last sub-step the wave waits for its own loads of the next
 // stage, the workgroup meets at one barrier (next stage complete everywhere,
 // current stage no longer read), the first fragments of the next step are
-// read, and the A loads two steps ahead go into the stage just drained, one
-// after each pair of the sub-step's MFMAs; the matching B loads follow the
+// read, and the B loads two steps ahead go into the stage just drained, one
+// after each pair of the sub-step's MFMAs; the matching A loads follow the
 // same way in the next step's first sub-step (issued as one burst they hold
-// up the MFMAs behind them while the address queue drains; measured on the
-// values pass: all 16 in the last sub-step 789 us, A there and B in the next
-// first sub-step 771 us, B spread further into the second sub-step 808 us --
-// later loads leave too little of the step to cover their latency).
+// up the MFMAs behind them while the address queue drains).  Measured on the
+// values pass, 31 frames: all 16 loads in the last sub-step 789 us; A there
+// and B in the next first sub-step 771 us; B there and A in the next first
+// sub-step 747 us (E, read by fewer workgroups than V, gets the longer lead);
+// loads spread into the second sub-step 808 us (too little of the step left
+// to cover their latency).
 //
 // The compiler guards LDS reads against direct-to-LDS loads still in flight:
 // a read it cannot prove disjoint from them gets a wait for all of them.
@@ -270,13 +272,13 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
   };
   read_a_step(f, sm.a[0]);
   read_b(f[0].b, sm.b[0], 0);
-  la.issue(k1, sm.a[1], wave);
-  // The B loads of step kt + 1 are issued during step kt's first sub-step
+  lb.issue(k1, sm.b[1], wave);
+  // The A loads of step kt + 1 are issued during step kt's first sub-step
   // (into the stage step kt does not read; step 1's from step 0), so that each
   // sub-step carries at most 8 loads per wave: 16 at once, from all four waves
   // right after the barrier, back up the address queue and hold the MFMAs
   // behind them.
-  int kb_pend = k1;  // K offset of the B loads the next first sub-step issues
+  int kb_pend = k1;  // K offset of the A loads the next first sub-step issues
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
     const char* sb = sm.b[st];
@@ -292,7 +294,7 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
         const int i = p >> 1, j0 = 2 * (p & 1);
         acc[i][j0] = mfma32x32x16(f[0].a[i], b0[j0], acc[i][j0]);
         acc[i][j0 + 1] = mfma32x32x16(f[0].a[i], b0[j0 + 1], acc[i][j0 + 1]);
-        lb.issue_one(lb.r, kb_pend, sm.b[st ^ 1], wave, p);
+        la.issue_one(kb_pend, sm.a[st ^ 1], wave, p);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -309,8 +311,8 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
     read_a_step(f, sm.a[st ^ 1]);
     read_b(f[0].b, sm.b[st ^ 1], 0);
     const int k2 = kb + (kt + 2 < nk ? kt + 2 : nk - 1) * kStepK;  // past the end: reload, unused
-    // The reads above, then the sub-step's MFMAs in pairs with one A load
-    // after each pair; the B loads follow in the next step's first sub-step
+    // The reads above, then the sub-step's MFMAs in pairs with one B load
+    // after each pair; the A loads follow in the next step's first sub-step
     // (none after the last step).
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 lbf[4];
@@ -322,7 +324,7 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], __amdgpu_buffer_r
       const int i = p >> 1, j0 = 2 * (p & 1);
       acc[i][j0] = mfma32x32x16(last.a[i], lbf[j0], acc[i][j0]);
       acc[i][j0 + 1] = mfma32x32x16(last.a[i], lbf[j0 + 1], acc[i][j0 + 1]);
-      la.issue_one(k2, sm.a[st], wave, p);
+      lb.issue_one(lb.r, k2, sm.b[st], wave, p);
     }
     __builtin_amdgcn_sched_barrier(0);
     kb_pend = k2;

@@ -322,10 +322,20 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
     advance();
   };
 
+  // The K loads of a load step go out one step after its Q loads, in the first
+  // sub-step of the next step (or at the start of an idle step); these hold
+  // the cursor of the last load step served.  At the start, and after a step
+  // whose wave issued both at once, they repeat loads already issued (same
+  // bytes into the same place).
+  __amdgpu_buffer_rsrc_t rk_pend;
+  int lk_pend;
+
   set_load_tile(0);
   issue_next(sm.a[0], sm.b[0]);
   wait_vmem();
   block_sync();
+  rk_pend = rk;
+  lk_pend = lk;
   issue_next(sm.a[1], sm.b[1]);  // total >= nk >= 3
 
   f32x16 acc[4][kScoresNJ];
@@ -339,13 +349,23 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
     const int st = s & 1;
     const char* sa = sm.a[st];
     const char* sb = sm.b[st];
+    // Sub-step 0: its MFMAs in pairs, each followed by one of the K loads the
+    // previous step deferred (the next step's, into the stage this step does
+    // not read).
+    read_frags(nxt, la, lb, sa, sb, abase, bbase, lane, 1);
 #pragma unroll
-    for (int ss = 0; ss < 3; ++ss) {
+    for (int p = 0; p < 4; ++p) {
+      __builtin_amdgcn_sched_barrier(0);
+      acc[p][0] = mfma32x32x16(cur.a[p], cur.b[0], FIRST ? f32x16{} : acc[p][0]);
+      acc[p][1] = mfma32x32x16(cur.a[p], cur.b[1], FIRST ? f32x16{} : acc[p][1]);
+      la.issue_one(rk_pend, lk_pend * kStepK, sm.a[st ^ 1], wave, p);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    cur = nxt;
+#pragma unroll
+    for (int ss = 1; ss < 3; ++ss) {
       read_frags(nxt, la, lb, sa, sb, abase, bbase, lane, ss + 1);
-      if (FIRST && ss == 0)
-        mma_substep_first(acc, cur);
-      else
-        mma_substep(acc, cur, nx);
+      mma_substep(acc, cur, nx);
       sched_substep<kScoresNJ>();
       cur = nxt;
     }
@@ -367,11 +387,12 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
       acc[p][0] = mfma32x32x16(cur.a[p], cur.b[0], acc[p][0]);
       acc[p][1] = mfma32x32x16(cur.a[p], cur.b[1], acc[p][1]);
       static_assert(kLoads == 4, "one load of each operand per MFMA pair");
-      la.issue_one(rk, lk * kStepK, sm.a[st], wave, p);
       lb.issue_one(rq, lk * kStepK, sm.b[st], wave, p);
     }
     __builtin_amdgcn_sched_barrier(0);
     cur = nxt;
+    rk_pend = rk;
+    lk_pend = lk;
     if (s + 2 < total) advance();
   };
 
@@ -379,6 +400,10 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
   // barrier only.
   auto idle_step = [&](int s) {
     const int st = s & 1;
+    // The K loads the previous step deferred to this one (the next step reads
+    // them), then both operands of the step two ahead at once.
+#pragma unroll
+    for (int p = 0; p < 4; ++p) la.issue_one(rk_pend, lk_pend * kStepK, sm.a[st ^ 1], wave, p);
     wait_vmem();
     block_sync();
 #pragma unroll
@@ -386,6 +411,8 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
       la.issue_one(rk, lk * kStepK, sm.a[st], wave, p);
       lb.issue_one(rq, lk * kStepK, sm.b[st], wave, p);
     }
+    rk_pend = rk;
+    lk_pend = lk;
     if (s + 2 < total) advance();
   };
 

@@ -196,7 +196,7 @@ def main() -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the heads are independent; see the sharding notes in DESIGN.md). "
+              "(the heads are independent: several GPUs would each take whole heads). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 

@@ -180,15 +180,6 @@ __device__ __forceinline__ void mma_substep(f32x16 (&acc)[4][NJ], const FragsT<N
     for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(f.a[i], b[j], acc[i][j]);
 }
 
-// The first sub-step of a tile: accumulators start from zero.
-template <int NJ>
-__device__ __forceinline__ void mma_substep_first(f32x16 (&acc)[4][NJ], const FragsT<NJ>& f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(f.a[i], f.b[j], f32x16{});
-}
-
 // Interleave a sub-step's 4 NJ MFMAs with the 4 + NJ LDS reads of the next.
 template <int NJ>
 __device__ __forceinline__ void sched_substep() {

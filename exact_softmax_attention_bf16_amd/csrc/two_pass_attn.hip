@@ -386,7 +386,7 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
       __builtin_amdgcn_sched_barrier(0);
       acc[p][0] = mfma32x32x16(cur.a[p], cur.b[0], acc[p][0]);
       acc[p][1] = mfma32x32x16(cur.a[p], cur.b[1], acc[p][1]);
-      static_assert(kLoads == 4, "one load of each operand per MFMA pair");
+      static_assert(kLoads == 4, "one load per MFMA pair");
       lb.issue_one(rq, lk * kStepK, sm.b[st], wave, p);
     }
     __builtin_amdgcn_sched_barrier(0);

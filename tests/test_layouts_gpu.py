@@ -477,3 +477,12 @@ def test_varlen_compressed_causal_equal_lengths_is_causal_bitwise():
     a = attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), 333, causal=True)
     b = attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), 333, causal="compressed")
     assert torch.equal(a, b)
+
+
+def test_varlen_compressed_causal_rejects_a_window():
+    from exact_softmax_attention_bf16_amd import _lib, attention_varlen
+    seqs, q, k, v, cu_q, cu_k = qk_batch([64], [16], 1, 1, 64, 960)
+    with pytest.raises(_lib.AttnError) as err:
+        attention_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cu_q.to(DEV), 64, causal="compressed",
+                         window=(8, 0), cu_seqlens_k=cu_k.to(DEV), max_seqlen_k=16)
+    assert err.value.status == _lib.ATTN_ERR_BAD_MASK

@@ -238,6 +238,46 @@ def test_two_streams_do_not_share_workspace():
     assert all(torch.equal(p[0], outs[-1][0]) and torch.equal(p[1], outs[-1][1]) for p in outs)
 
 
+def test_concurrent_host_threads_each_on_its_own_stream():
+    """Four host threads call at once, each on a stream of its own, mixing the
+    two-pass path and the online path with and without a key split; every call
+    equals the same call made alone (the library's workspace map and pools are
+    shared between the threads)."""
+    import threading
+
+    from exact_softmax_attention_bf16_amd import attention
+    dev = torch.device("cuda:0")
+    cases = [(1, 1, 700, 64, True), (2, 1, 600, 1024, False), (1, 2, 900, 128, False),
+             (1, 1, 1300, 256, True)]
+    ins = [tuple(t.to(dev) for t in make_qkv(B, H, L, d, 40 + i))
+           for i, (B, H, L, d, _) in enumerate(cases)]
+    refs = [attention(q, k, v, causal=c) for (q, k, v), (*_, c) in zip(ins, cases)]
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def work(i):
+        try:
+            stream = torch.cuda.Stream()
+            q, k, v = ins[i]
+            with torch.cuda.stream(stream):
+                outs = [attention(q, k, v, causal=cases[i][4]) for _ in range(6)]
+            stream.synchronize()
+            results[i] = outs
+        except Exception as e:  # re-raised below, in the test's own thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    if errors:
+        raise errors[0]
+    for i, ref in enumerate(refs):
+        assert all(torch.equal(o, ref) for o in results[i]), cases[i]
+
+
 # ---- online path with few heads: keys split among workgroups, then combined ----
 
 @pytest.mark.parametrize("B,H,L,d", [(1, 1, 4096, 64), (1, 2, 1000, 128), (2, 4, 1024, 64),

@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "internal.h"
+#include "workspace.h"
 
 namespace {
 
@@ -61,61 +62,39 @@ bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
   return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
 }
 
-// ---- workspace: one buffer per (device, stream), kept between calls.
-//
-// Work on one stream runs in order, so the stream's buffer can be reused by the
-// next call without any host wait; calls on different streams get different
-// buffers.  After each use an event is recorded on the stream; the next use
-// makes the stream wait for it (a no-op on the same stream, an ordering edge if
-// a new stream ever reuses a destroyed stream's handle), and growing the buffer
-// waits for it on the host before freeing the old one.
-struct Workspace {
-  void* ptr = nullptr;
-  size_t bytes = 0;
-  hipEvent_t done = nullptr;
-  bool recorded = false;
+// ---- workspace: one buffer per (device, stream), kept between calls and
+// leased for the whole of a call (csrc/workspace.h states the invariants).
+struct HipBackend {
+  using Stream = hipStream_t;
+  using Event = hipEvent_t;
+  int create_event(hipEvent_t* e) { return hipEventCreateWithFlags(e, hipEventDisableTiming); }
+  int record(hipEvent_t e, hipStream_t s) { return hipEventRecord(e, s); }
+  int stream_wait(hipStream_t s, hipEvent_t e) { return hipStreamWaitEvent(s, e, 0); }
+  int malloc_async(void** p, size_t n, hipStream_t s) { return hipMallocAsync(p, n, s); }
+  int free_async(void* p, hipStream_t s) { return hipFreeAsync(p, s); }
 };
-std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+HipBackend g_hip_backend;
+attn::WorkspaceCache<HipBackend> g_ws(g_hip_backend);
 
-hipError_t acquire_workspace(hipStream_t stream, size_t bytes, Workspace** out) {
-  int dev = 0;
-  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  Workspace& w = g_ws[{dev, stream}];
-  if (!w.done) {
-    e = hipEventCreateWithFlags(&w.done, hipEventDisableTiming);
-    if (e != hipSuccess) {
-      w.done = nullptr;
-      return e;
-    }
+// A lease of the calling stream's buffer for one call: acquire() before the
+// first launch, release() after the last (also on every error path).
+class WorkspaceLease {
+ public:
+  explicit WorkspaceLease(hipStream_t s) : s_(s) {}
+  ~WorkspaceLease() { (void)release(); }
+  hipError_t acquire(size_t bytes) {
+    int dev = 0;
+    hipError_t e = s_ ? hipStreamGetDevice(s_, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    return (hipError_t)g_ws.acquire(dev, s_, bytes, &l_);
   }
-  if (w.bytes < bytes) {
-    if (w.ptr) {
-      if (w.recorded && (e = hipEventSynchronize(w.done)) != hipSuccess) return e;
-      (void)hipFree(w.ptr);
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
-    if ((e = hipMalloc(&w.ptr, bytes)) != hipSuccess) {
-      w.ptr = nullptr;
-      return e;
-    }
-    w.bytes = bytes;
-  } else if (w.recorded && (e = hipStreamWaitEvent(stream, w.done, 0)) != hipSuccess) {
-    return e;
-  }
-  *out = &w;
-  return hipSuccess;
-}
+  void* ptr() const { return l_.ptr; }
+  hipError_t release() { return (hipError_t)g_ws.release(s_, &l_); }
 
-hipError_t release_workspace(hipStream_t stream, Workspace* w) {
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  const hipError_t e = hipEventRecord(w->done, stream);
-  w->recorded = e == hipSuccess;
-  return e;
-}
+ private:
+  hipStream_t s_;
+  attn::WorkspaceCache<HipBackend>::Lease l_;
+};
 
 // ---- kernel timing (benchmarks only).
 struct TimingRecord {
@@ -176,11 +155,10 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, float* 
   const int64_t chunk = heads_per_chunk(BH, per_head);
   const bool on = timing_on();
 
-  Workspace* wsp = nullptr;
-  if (acquire_workspace(stream, (size_t)two_pass_workspace_bytes(BH, t, band), &wsp) !=
-      hipSuccess)
+  WorkspaceLease ws(stream);
+  if (ws.acquire((size_t)two_pass_workspace_bytes(BH, t, band)) != hipSuccess)
     return ATTN_ERR_WORKSPACE;
-  char* base = (char*)wsp->ptr;
+  char* base = (char*)ws.ptr();
 
   hipError_t err = hipSuccess;
   for (int64_t h0 = 0; h0 < BH && err == hipSuccess; h0 += chunk) {
@@ -207,7 +185,7 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, float* 
         return attn::launch_values_reduce(part, out, split, hm, n, t, stream);
       });
   }
-  const hipError_t rerr = release_workspace(stream, wsp);
+  const hipError_t rerr = ws.release();
   if (err != hipSuccess || rerr != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -230,11 +208,11 @@ int forward(const void* q, const void* k, const void* v, void* out, float* lse,
     if (nqb * bh * nsplit >= ((int64_t)1 << 31)) return ATTN_ERR_TOO_LARGE;
     const bool on = timing_on();
     attn::KeySplit ks{nullptr, nullptr, 1, (int)bh};
-    Workspace* wsp = nullptr;
+    WorkspaceLease ws(stream);
     if (nsplit > 1) {  // few heads: the keys of each query block are split
-      if (acquire_workspace(stream, (size_t)online_workspace_bytes(bh, L, d), &wsp) != hipSuccess)
+      if (ws.acquire((size_t)online_workspace_bytes(bh, L, d)) != hipSuccess)
         return ATTN_ERR_WORKSPACE;
-      ks.part = (float*)wsp->ptr;
+      ks.part = (float*)ws.ptr();
       ks.stats = ks.part + (size_t)nsplit * bh * L * d;
       ks.n = nsplit;
     }
@@ -247,7 +225,7 @@ int forward(const void* q, const void* k, const void* v, void* out, float* lse,
         return attn::launch_online_combine(ks, out, lse, hm, (int)L, (int)d,
                                            attn::VarSeqs{nullptr, nullptr, 0, 0, 0}, stream);
       });
-    const hipError_t rerr = wsp ? release_workspace(stream, wsp) : hipSuccess;
+    const hipError_t rerr = ws.release();
     return e == hipSuccess && rerr == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
   }
   const attn::TwoPassDims t = attn::two_pass_dims(L, d);
@@ -507,11 +485,11 @@ int attn_forward_varlen(const void* q, const void* k, const void* v, void* out, 
   if ((max_seqlen + 127) / 128 * bh * nsplit >= ((int64_t)1 << 31)) return ATTN_ERR_TOO_LARGE;
   const bool on = timing_on();
   attn::KeySplit ks{nullptr, nullptr, 1, (int)bh};
-  Workspace* wsp = nullptr;
+  WorkspaceLease ws(stream);
   if (nsplit > 1) {
     const int64_t bytes = round256((int64_t)nsplit * bh * max_seqlen * (d + 2) * 4);
-    if (acquire_workspace(stream, (size_t)bytes, &wsp) != hipSuccess) return ATTN_ERR_WORKSPACE;
-    ks.part = (float*)wsp->ptr;
+    if (ws.acquire((size_t)bytes) != hipSuccess) return ATTN_ERR_WORKSPACE;
+    ks.part = (float*)ws.ptr();
     ks.stats = ks.part + (size_t)nsplit * bh * max_seqlen * d;
     ks.n = nsplit;
   }
@@ -523,7 +501,7 @@ int attn_forward_varlen(const void* q, const void* k, const void* v, void* out, 
     e = timed(ATTN_KERNEL_ONLINE_COMBINE, stream, on, [&] {
       return attn::launch_online_combine(ks, out, lse, hm, (int)max_seqlen, (int)d, vs, stream);
     });
-  const hipError_t rerr = wsp ? release_workspace(stream, wsp) : hipSuccess;
+  const hipError_t rerr = ws.release();
   return e == hipSuccess && rerr == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

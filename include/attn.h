@@ -21,11 +21,16 @@
  *     entry point synchronises the device.
  *   - Every argument is checked on the host before any HIP call; a failed check
  *     returns its status code and queues nothing.  No exception crosses the ABI.
- *   - Thread safety: any number of host threads may call concurrently.  Calls on
- *     different streams are independent: the two-pass path keeps one workspace
- *     buffer per (device, stream), reused by later calls on that stream (work on
- *     a stream runs in order), so two calls in flight never share scratch memory.
- *     The buffers live until the process ends.
+ *   - Thread safety: any number of host threads may call concurrently, on the
+ *     same stream or on different ones.  A call that needs scratch memory leases
+ *     the workspace buffer the library keeps for (device, stream) from before
+ *     its first launch until after its last, under that buffer's lock: calls on
+ *     one stream queue their kernels one call after another (never interleaved
+ *     over the buffer), calls on different streams never wait for each other.
+ *     A buffer grows stream-ordered (hipFreeAsync of the old one and
+ *     hipMallocAsync of the new one on the caller's stream), so no call
+ *     synchronises the device or waits on the host for the GPU.  The buffers
+ *     live until the process ends.
  */
 #ifndef ATTN_MI355X_ATTN_H
 #define ATTN_MI355X_ATTN_H
@@ -95,8 +100,8 @@ enum {
  * head, heads processed in chunks of at most 2 GiB; when so few heads would
  * leave most compute units idle, also up to 4 fp32 copies of the output for
  * a split over the keys -- attn_workspace_bytes gives the exact figure).
- * Growing waits on the host for the stream's previous use of the buffer;
- * reuse does not.
+ * Neither growing nor reusing the buffer waits on the host (see the thread
+ * safety note above).
  */
 int attn_forward(const void* q, const void* k, const void* v, void* out,
                  int64_t B, int64_t H, int64_t L, int64_t d,

@@ -12,6 +12,14 @@ import numpy as np
 MAX_ABS_TOL = 2e-2
 REL_RMS_TOL = 5e-3
 
+# Expected error band of a correct kernel (tests only): rounding the exact
+# result once to bf16 alone gives rel_rms = 1.61e-3 .. 1.66e-3 on every
+# workload shape (the floor no bf16 output can beat), and rounding P to bf16
+# before the second contraction adds about 1.2e-3 in quadrature (emulated:
+# 2.0e-3 .. 2.3e-3 in total).  3e-3 keeps ~30% margin over that, so an error
+# twice the expected one fails while the 5e-3 bar would still pass it.
+REL_RMS_BAND = 3e-3
+
 
 def max_abs(out, ref) -> float:
     out = np.asarray(out, dtype=np.float64)

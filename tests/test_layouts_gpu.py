@@ -18,7 +18,7 @@ import torch
 
 import oracle
 from synth import make_qkv
-from synth.metrics import within_bar
+from synth.metrics import REL_RMS_BAND, within_bar
 
 from gpu_util import to_f64
 
@@ -64,21 +64,19 @@ def test_packed_qkv_in_place(C, causal):
     assert ok, (a, r)
 
 
-def test_packed_qkv_wan_frames_sampled():
+def test_packed_qkv_wan_frames():
     """The decoder's packed layout at its real size: 4 frames of 44 x 78
-    positions, C = 1024, checked on sampled rows of every frame."""
+    positions, C = 1024, every output element against the oracle."""
     from exact_softmax_attention_bf16_amd import attention_packed_qkv
     T, HW, C = 4, 3432, 1024
     qkv, (q, k, v) = packed(T, HW, C, 104)
     o = attention_packed_qkv(qkv.to(DEV), scale=1.0 / 32, causal=False)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(5)
-    rows = [(t, 0, int(i)) for t in range(T) for i in list(rng.choice(HW, 6, replace=False)) + [0, HW - 1]]
-    ref = oracle.attention_rows(to_f64(q), to_f64(k), to_f64(v), 1.0 / 32, False, rows)
-    got = np.stack([to_f64(o[t, h, i]) for t, h, i in rows])
-    ok, a, r = within_bar(got, ref)
-    _report("packed qkv 4 x 3432 x 1024 (sampled rows)", a, r)
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1.0 / 32, False)
+    ok, a, r = within_bar(to_f64(o), ref)
+    _report("packed qkv 4 x 3432 x 1024", a, r)
     assert ok, (a, r)
+    assert r <= REL_RMS_BAND, (r, REL_RMS_BAND)
 
 
 @pytest.mark.parametrize("d", [64, 256])

@@ -7,10 +7,15 @@ one head, L = 3432 (44x78), d = 1024, scale 1/32, no mask (1.4956 TFLOP).
 
 Prints one JSON line:  TFLOP/s (value), ms per call, % of the bf16 dense MFMA
 peak, the dominant kernel's roofline figures (its FLOPs per launch over its
-average HIP-event duration inside the timed region) and the CPU float64
-oracle's rate on a bounded sample of the same workload.
+average HIP-event duration inside the timed region), the CPU float64 oracle's
+rate on every head of the same workload, and the timed output's error against
+that oracle.  Under "runs", the other five workloads (the tiny d = 256 head,
+4 x 8 heads at d = 64 with and without the causal mask, 1 and 4 Wan frames),
+each timed the same way (events on the kernels' stream around K calls, then
+per-call events) and checked against the oracle, with the oracle's time.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--no-other-runs]
 """
 from __future__ import annotations
 
@@ -76,29 +81,86 @@ def measured_traffic(kernel: str, workload: str, launches_per_step: float):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, budget_s: float):
-    """The oracle, as it stands, on whole frames of the workload until ~budget_s."""
-    import oracle
+def oracle_cores() -> int:
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:  # noqa: BLE001
-        cores = os.cpu_count() or 1
-    pairs = w.L * (w.L + 1) // 2 if w.causal else w.L * w.L
-    per_head = 4 * pairs * w.d
-    done, t0 = 0, time.perf_counter()
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    for b, h in heads:
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        oracle.attention(q[sl].float().numpy(), k[sl].float().numpy(), v[sl].float().numpy(),
-                         w.scale, w.causal)
-        done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
+        return os.cpu_count() or 1
+
+
+def oracle_check(w, q, k, v, out_gpu):
+    """The oracle, as it stands, on every head of the workload: its wall time on
+    the host cores, and the GPU output of the timed region against it."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from synth.metrics import REL_RMS_BAND, within_bar
+    f64 = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+    got = out_gpu.detach().to("cpu", torch.float64).numpy()
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    t0 = time.perf_counter()
+    ref = np.empty_like(got)
+    for b in range(w.B):  # head by head, as the oracle runs on its own
+        ref[b:b + 1] = oracle.attention(qf[b:b + 1], kf[b:b + 1], vf[b:b + 1], w.scale, w.causal)
     dt = time.perf_counter() - t0
-    return {"value": round(done * per_head / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{done} of {len(heads)} heads (L={w.L}, d={w.d}, all rows), {dt:.1f} s, float64"}
+    ok, a, r = within_bar(got, ref)
+    return {"oracle_s": round(dt, 3), "oracle_cores": oracle_cores(), "max_abs": float(f"{a:.4g}"),
+            "rel_rms": float(f"{r:.4g}"), "ok": bool(ok and r <= REL_RMS_BAND)}
+
+
+def time_calls(call, stream, steps: int):
+    """ms per call over `steps` back-to-back calls between two events on the
+    stream the kernels run on, then the per-call median and minimum over as
+    many more calls, each between its own pair of events."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    region = a.elapsed_time(b) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for x, y in ev:
+        x.record(stream)
+        call()
+        y.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(x.elapsed_time(y) for x, y in ev)
+    med = per[len(per) // 2] if len(per) % 2 else 0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2])
+    return region, med, per[0]
+
+
+def other_run(name: str, steps: int, warmup: int, dev):
+    """One of the other workloads: warm up, time, kernel averages, oracle parity."""
+    import torch
+
+    from exact_softmax_attention_bf16_amd import attention, kernel_timing
+    from synth import WORKLOADS, make_qkv
+    w = WORKLOADS[name]
+    q, k, v = make_qkv(w.B, w.H, w.L, w.d, w.seed)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(qd)
+    call = lambda: attention(qd, kd, vd, scale=w.scale, causal=w.causal, out=out)  # noqa: E731
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    kt = {}
+    with kernel_timing(kt):
+        region, med, mn = time_calls(call, torch.cuda.current_stream(), steps)
+    flops = w.flops()
+    rec = {"B": w.B, "H": w.H, "L": w.L, "d": w.d, "causal": w.causal, "flop": flops,
+           "steps": steps, "ms_per_call": round(region, 5),
+           "ms_per_call_median": round(med, 5), "ms_per_call_min": round(mn, 5),
+           "tflops": round(flops / (region * 1e-3) / 1e12, 3),
+           "pct_bf16_mfma_peak": round(100.0 * flops / (region * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 3),
+           "kernel_ms": {n: round(t / c, 5) for n, (t, c) in sorted(kt.items())}}
+    rec.update(oracle_check(w, q, k, v, out))
+    log(f"[bench] {name}: {rec}")
+    return rec
 
 
 def design_probe(args) -> int:
@@ -168,8 +230,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="wan_31frame")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle (its timing and the parity of the timed output)")
+    ap.add_argument("--no-other-runs", action="store_true",
+                    help="time only --workload, not the other five runs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 256 MiB device-to-device three times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
@@ -231,9 +295,6 @@ def main() -> int:
     log(f"[bench] {args.steps} steps: {ms:.4f} ms/call, {tflops:.1f} TFLOP/s")
     for name, (tot, cnt) in sorted(kt.items()):
         log(f"[bench]   kernel {name}: {tot / cnt:.4f} ms avg over {cnt} launches")
-    if not torch.isfinite(out.float()).all():
-        log("[bench] non-finite output")
-        return 1
 
     # Per-call spread, after the timed region: K more calls, each between two
     # events on the stream the kernels run on.
@@ -264,11 +325,27 @@ def main() -> int:
                 "flop_per_launch": flop_per_launch,
                 "avg_launch_ms": round(tot / cnt, 5)}
 
-    cpu = None
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline (oracle), ~{args.cpu_seconds:.0f} s")
-        cpu = cpu_baseline(w, q, k, v, args.cpu_seconds)
-        log(f"[bench] cpu baseline: {cpu}")
+        log("[bench] oracle on every head of the timed output")
+        chk = oracle_check(w, q, k, v, out)
+        parity = {key: chk[key] for key in ("max_abs", "rel_rms", "ok")}
+        pairs = w.L * (w.L + 1) // 2 if w.causal else w.L * w.L
+        cpu = {"value": round(4 * w.B * w.H * pairs * w.d / chk["oracle_s"] / 1e12, 6),
+               "unit": "TFLOP/s", "cores": chk["oracle_cores"], "kind": "oracle",
+               "sample": (f"all {w.B * w.H} heads (L={w.L}, d={w.d}, every row), "
+                          f"{chk['oracle_s']:.1f} s, float64 NumPy")}
+        log(f"[bench] cpu baseline: {cpu}; parity {parity}")
+
+    runs = None
+    if not args.no_other_runs:
+        runs = {}
+        for name in ("tiny_d256", "mha_d64", "mha_d64_causal", "wan_1frame", "wan_4frame",
+                     "wan_31frame"):
+            if name == w.name:
+                continue
+            small = WORKLOADS[name].flops() < 1e11
+            runs[name] = other_run(name, 200 if small else args.steps, max(args.warmup, 10), dev)
 
     vs = None
     if w.name == "wan_31frame":
@@ -299,8 +376,14 @@ def main() -> int:
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
+        "runs": runs,
     }
     print(json.dumps(line), flush=True)
+    checks = ([parity] if parity else []) + list((runs or {}).values())
+    if not all(c["ok"] for c in checks):
+        log("[bench] a timed output is outside the parity bar or the expected error band")
+        return 1
     return 0
 
 

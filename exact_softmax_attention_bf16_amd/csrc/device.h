@@ -77,9 +77,13 @@ __device__ __forceinline__ float add_bf16x2(unsigned w, float s) {
                                          __builtin_bit_cast(bf16x2, 0x3f803f80u), s, false);
 }
 
-// Multiply both bf16 halves of a word by 2^-s (s <= 255) exactly: a saturating
-// subtract on the exponent field; values that would drop below the smallest
-// normal become zero.  `s2` is s << 7 | s << 23.  Inputs must be >= 0.
+// Multiply both bf16 halves of a word by 2^-s (s <= 255): a saturating
+// subtract on the exponent field, exact while the result stays normal.  A
+// value whose exponent field would go below 0 becomes zero; one whose field
+// lands exactly on 0 keeps its 7 mantissa bits as a subnormal, i.e. m * 2^-133
+// instead of (1 + m / 128) * 2^-127 -- wrong, but below 2^-126 in magnitude
+// (the callers' values are at most 1 with row maxima above 2^-1, so such a
+// term is negligible).  `s2` is s << 7 | s << 23.  Inputs must be >= 0.
 __device__ __forceinline__ unsigned scale_pow2_down(unsigned w, unsigned s2) {
   u16x2 a = __builtin_bit_cast(u16x2, w);
   u16x2 b = __builtin_bit_cast(u16x2, s2);

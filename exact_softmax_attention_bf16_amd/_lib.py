@@ -24,6 +24,9 @@ ATTN_ERR_HIP = 8
 ATTN_ERR_TOO_LARGE = 9
 ATTN_ERR_BAD_STRIDE = 10
 ATTN_ERR_BAD_MASK = 11
+ATTN_ERR_SCRATCH_TOO_SMALL = 12
+
+ATTN_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 ATTN_MASK_NONE = 0
 ATTN_MASK_CAUSAL = 1
@@ -40,6 +43,10 @@ SIGNATURES = {
     "attn_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_float, ctypes.c_int, ctypes.c_void_p]),
+    "attn_forward_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                            ctypes.c_int, ctypes.c_void_p]),
     "attn_forward_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,

@@ -95,6 +95,29 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | 
     return (out, lse) if return_lse else out
 
 
+def attention_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                      scale: float | None = None, causal: bool = False) -> torch.Tensor:
+    """attention() for callers that cannot allocate device memory (HIP graph
+    capture, tight serving loops): contiguous bf16 [B, H, L, d] q, k, v and a
+    caller-provided ``out``; the library draws its scratch memory from a fixed
+    per-device array instead of allocating (attn_forward_noalloc).  Calls whose
+    work may overlap on one GPU race on that array.  Raises AttnError with
+    ATTN_ERR_SCRATCH_TOO_SMALL when one head needs more scratch than the array
+    holds (d > 128 with L above 7943)."""
+    _check(q, "q")
+    B, H, L, d = q.shape
+    for t, name in ((k, "k"), (v, "v"), (out, "out")):
+        _check(t, name, (B, H, L, d), q.device)
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _call(_lib.load().attn_forward_noalloc, q, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+          out.data_ptr(), B, H, L, d, float(scale), 1 if causal else 0)
+    return out
+
+
 def _window_args(window):
     if window is None:
         return -1, -1

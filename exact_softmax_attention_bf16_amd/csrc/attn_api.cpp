@@ -28,8 +28,8 @@ bool head_dim_supported(int64_t d) {
 // Heads per two-pass chunk: enough to fill the chip, capped near 2 GiB of workspace.
 constexpr int64_t kChunkBudget = int64_t(2) << 30;
 
-int64_t heads_per_chunk(int64_t BH, int64_t head_bytes) {
-  int64_t n = kChunkBudget / (head_bytes > 0 ? head_bytes : 1);
+int64_t heads_per_chunk(int64_t BH, int64_t head_bytes, int64_t budget = kChunkBudget) {
+  int64_t n = budget / (head_bytes > 0 ? head_bytes : 1);
   if (n < 1) n = 1;
   return n < BH ? n : BH;
 }
@@ -96,6 +96,68 @@ class WorkspaceLease {
   attn::WorkspaceCache<HipBackend>::Lease l_;
 };
 
+// ---- the no-allocation entry point's scratch memory: one array per device,
+// held from the library's first use on that device until the process ends.
+// Host code reaches it only through the address hipGetSymbolAddress gives for
+// the current device (the array's name is a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of `scratch` on device `dev`, looked up once per device with
+// that device current.
+hipError_t scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ScratchSlot& sl = g_scratch[dev];
+  std::call_once(sl.once, [&] {
+    int cur = -1;
+    sl.err = hipGetDevice(&cur);
+    if (sl.err == hipSuccess && cur != dev) sl.err = hipSetDevice(dev);
+    if (sl.err == hipSuccess) sl.err = hipGetSymbolAddress(&sl.ptr, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t e = hipSetDevice(cur);
+      if (sl.err == hipSuccess) sl.err = e;
+    }
+    if (sl.err != hipSuccess) sl.ptr = nullptr;
+  });
+  *out = sl.ptr;
+  return sl.err;
+}
+
+// Where one call's scratch memory comes from: the stream's leased workspace
+// (grown as needed), or -- for the no-allocation entry point -- the device's
+// fixed `scratch` array, whose capacity bounds what the call may use.  get()
+// is the first HIP call a forward call makes, after every host check.
+class Scratch {
+ public:
+  Scratch(hipStream_t s, bool fixed) : s_(s), fixed_(fixed), lease_(s) {}
+  bool fixed() const { return fixed_; }
+  static constexpr int64_t capacity() { return ATTN_NOALLOC_SCRATCH_BYTES; }
+  hipError_t get(size_t bytes, void** p) {
+    if (!fixed_) {
+      const hipError_t e = lease_.acquire(bytes);
+      *p = lease_.ptr();
+      return e;
+    }
+    if ((int64_t)bytes > capacity()) return hipErrorInvalidValue;  // callers size to capacity()
+    int dev = 0;
+    const hipError_t e = s_ ? hipStreamGetDevice(s_, &dev) : hipGetDevice(&dev);
+    return e != hipSuccess ? e : scratch_address(dev, p);
+  }
+  hipError_t release() { return fixed_ ? hipSuccess : lease_.release(); }
+
+ private:
+  hipStream_t s_;
+  bool fixed_;
+  WorkspaceLease lease_;
+};
+
 // ---- kernel timing (benchmarks only).
 struct TimingRecord {
   int id;
@@ -149,16 +211,19 @@ hipError_t timed(int id, hipStream_t s, bool on, F&& launch) {
 
 int run_two_pass(const void* q, const void* k, const void* v, void* out, float* lse,
                  attn::HeadMap hm, int64_t BH, int64_t L, int64_t d, float sl2,
-                 const attn::Band& band, hipStream_t stream) {
+                 const attn::Band& band, hipStream_t stream, Scratch& sc, bool on) {
   const attn::TwoPassDims t = attn::two_pass_dims(L, d);
   const int64_t per_head = attn::two_pass_head_bytes(t);
-  const int64_t chunk = heads_per_chunk(BH, per_head);
-  const bool on = timing_on();
+  // A fixed scratch array holds the chunk's staging (checked by the caller to
+  // fit one head); the values pass's key split is dropped for a chunk whose
+  // partial outputs would not fit next to it.
+  const int64_t chunk = sc.fixed() ? heads_per_chunk(BH, per_head, Scratch::capacity())
+                                   : heads_per_chunk(BH, per_head);
+  const int64_t need = sc.fixed() ? Scratch::capacity() : two_pass_workspace_bytes(BH, t, band);
 
-  WorkspaceLease ws(stream);
-  if (ws.acquire((size_t)two_pass_workspace_bytes(BH, t, band)) != hipSuccess)
-    return ATTN_ERR_WORKSPACE;
-  char* base = (char*)ws.ptr();
+  void* ws = nullptr;
+  if (sc.get((size_t)need, &ws) != hipSuccess) return ATTN_ERR_WORKSPACE;
+  char* base = (char*)ws;
 
   hipError_t err = hipSuccess;
   for (int64_t h0 = 0; h0 < BH && err == hipSuccess; h0 += chunk) {
@@ -171,7 +236,8 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, float* 
     float* mref = (float*)(base + e_bytes);
     float* psum = (float*)(base + e_bytes + st_bytes);
     float* part = (float*)(base + e_bytes + 2 * st_bytes);
-    const int split = attn::values_split(n, t, band);
+    int split = attn::values_split(n, t, band);
+    if (split > 1 && chunk_workspace_bytes(n, t, band) > need) split = 1;
     err = timed(ATTN_KERNEL_SCORES, stream, on, [&] {
       return attn::launch_scores(q, k, E, mref, psum, hm, n, t, sl2, band, stream);
     });
@@ -185,7 +251,7 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, float* 
         return attn::launch_values_reduce(part, out, split, hm, n, t, stream);
       });
   }
-  const hipError_t rerr = ws.release();
+  const hipError_t rerr = sc.release();
   if (err != hipSuccess || rerr != hipSuccess) return ATTN_ERR_HIP;
   return ATTN_OK;
 }
@@ -195,7 +261,7 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, float* 
 // ld_max: the largest row stride of q, k and v (elements).
 int forward(const void* q, const void* k, const void* v, void* out, float* lse,
             const attn::HeadMap& hm, int64_t bh, int64_t L, int64_t d, int64_t ld_max,
-            float scale, const attn::Band& band, hipStream_t stream) {
+            float scale, const attn::Band& band, hipStream_t stream, bool fixed_scratch = false) {
   // Kernels address one head with 32-bit byte offsets (rows up to L + 255 are
   // formed, past-the-end ones read as zero) and count heads in int.
   if ((L + 256) * ld_max * 2 >= ((int64_t)1 << 31) || bh >= ((int64_t)1 << 31) / 1024)
@@ -204,15 +270,18 @@ int forward(const void* q, const void* k, const void* v, void* out, float* lse,
 
   if (attn_path_for_head_dim(d) == ATTN_PATH_ONLINE) {
     const int64_t nqb = (L + 127) / 128;
-    const int nsplit = attn::online_split(bh, L, L);
+    int nsplit = attn::online_split(bh, L, L);
+    // A fixed scratch array: as many shares as fit (one share needs none).
+    auto share_bytes = [&](int n) { return round256((int64_t)n * bh * L * (d + 2) * 4); };
+    while (fixed_scratch && nsplit > 1 && share_bytes(nsplit) > Scratch::capacity()) --nsplit;
     if (nqb * bh * nsplit >= ((int64_t)1 << 31)) return ATTN_ERR_TOO_LARGE;
-    const bool on = timing_on();
+    const bool on = !fixed_scratch && timing_on();
     attn::KeySplit ks{nullptr, nullptr, 1, (int)bh};
-    WorkspaceLease ws(stream);
+    Scratch ws(stream, fixed_scratch);
     if (nsplit > 1) {  // few heads: the keys of each query block are split
-      if (ws.acquire((size_t)online_workspace_bytes(bh, L, d)) != hipSuccess)
-        return ATTN_ERR_WORKSPACE;
-      ks.part = (float*)ws.ptr();
+      void* p = nullptr;
+      if (ws.get((size_t)share_bytes(nsplit), &p) != hipSuccess) return ATTN_ERR_WORKSPACE;
+      ks.part = (float*)p;
       ks.stats = ks.part + (size_t)nsplit * bh * L * d;
       ks.n = nsplit;
     }
@@ -233,7 +302,11 @@ int forward(const void* q, const void* k, const void* v, void* out, float* lse,
   if (t.T > attn::kTwoPassMaxTiles || (int64_t)(t.L + 256) * t.Ls * 2 >= ((int64_t)1 << 32) - 1 ||
       (int64_t)t.T * t.T * bh >= ((int64_t)1 << 31))
     return ATTN_ERR_TOO_LARGE;
-  return run_two_pass(q, k, v, out, lse, hm, bh, L, d, sl2, band, stream);
+  if (fixed_scratch && attn::two_pass_head_bytes(t) > Scratch::capacity())
+    return ATTN_ERR_SCRATCH_TOO_SMALL;
+  Scratch sc(stream, fixed_scratch);
+  return run_two_pass(q, k, v, out, lse, hm, bh, L, d, sl2, band, stream, sc,
+                      !fixed_scratch && timing_on());
 }
 
 // One operand of attn_forward_ex: dims [B, heads, L, d] with element strides
@@ -286,6 +359,9 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_HIP: return "a HIP launch or runtime call failed";
     case ATTN_ERR_TOO_LARGE: return "problem too large: one head exceeds 32-bit byte offsets, or L > 31744 with d > 128";
     case ATTN_ERR_BAD_MASK: return "the compressed causal mask takes no window";
+    case ATTN_ERR_SCRATCH_TOO_SMALL:
+      return "attn_forward_noalloc: one head needs more scratch memory than its fixed "
+             "per-device array holds (ATTN_NOALLOC_SCRATCH_BYTES)";
     case ATTN_ERR_BAD_STRIDE:
       return "bad strides: negative, not a multiple of 8 elements, a row stride below d, or an "
              "output layout whose elements overlap";
@@ -308,8 +384,10 @@ int64_t attn_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t d, int cau
   return two_pass_workspace_bytes(B * H, t, attn::make_band(-1, -1, causal != 0, L));
 }
 
-int attn_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
-                 int64_t L, int64_t d, float scale, int causal, hipStream_t stream) {
+// attn_forward's and attn_forward_noalloc's argument checks; *bh = B * H.
+// Returns -1 when every check passed and there is work to do.
+static int check_forward_args(const void* q, const void* k, const void* v, const void* out, int64_t B,
+                       int64_t H, int64_t L, int64_t d, float scale, int64_t* bh_out) {
   if (B < 0 || H < 0 || L < 0 || d < 0) return ATTN_ERR_BAD_SHAPE;
   int64_t bh = 0, rows = 0, elems = 0, bytes = 0;
   if (__builtin_mul_overflow(B, H, &bh) || __builtin_mul_overflow(bh, L, &rows) ||
@@ -323,8 +401,27 @@ int attn_forward(const void* q, const void* k, const void* v, void* out, int64_t
   if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
     return ATTN_ERR_ALIAS;
   if (L > ((int64_t)1 << 30) || H > ((int64_t)1 << 30)) return ATTN_ERR_TOO_LARGE;
+  *bh_out = bh;
+  return -1;
+}
+
+int attn_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
+                 int64_t L, int64_t d, float scale, int causal, hipStream_t stream) {
+  int64_t bh = 0;
+  const int st = check_forward_args(q, k, v, out, B, H, L, d, scale, &bh);
+  if (st >= 0) return st;
   return forward(q, k, v, out, nullptr, attn::contiguous_heads((int)H, (int)L, (int)d), bh, L, d,
                  d, scale, attn::make_band(-1, -1, causal != 0, L), stream);
+}
+
+int attn_forward_noalloc(const void* q, const void* k, const void* v, void* out, int64_t B,
+                         int64_t H, int64_t L, int64_t d, float scale, int causal,
+                         hipStream_t stream) {
+  int64_t bh = 0;
+  const int st = check_forward_args(q, k, v, out, B, H, L, d, scale, &bh);
+  if (st >= 0) return st;
+  return forward(q, k, v, out, nullptr, attn::contiguous_heads((int)H, (int)L, (int)d), bh, L, d,
+                 d, scale, attn::make_band(-1, -1, causal != 0, L), stream, true);
 }
 
 int attn_forward_ex(const void* q, const void* k, const void* v, void* out, float* lse,

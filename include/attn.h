@@ -57,8 +57,10 @@ enum {
   ATTN_ERR_TOO_LARGE = 9,            /* one head exceeds the kernels' 32-bit byte offsets */
   ATTN_ERR_BAD_STRIDE = 10,          /* attn_forward_ex: a stride is negative or not a multiple
                                         of 8, a row stride is below d, or out's elements overlap */
-  ATTN_ERR_BAD_MASK = 11             /* attn_forward_varlen: the compressed causal mask
+  ATTN_ERR_BAD_MASK = 11,            /* attn_forward_varlen: the compressed causal mask
                                         combined with a window                   */
+  ATTN_ERR_SCRATCH_TOO_SMALL = 12    /* attn_forward_noalloc: one head needs more scratch
+                                        than ATTN_NOALLOC_SCRATCH_BYTES          */
 };
 
 /* Values of the `causal` argument.  attn_forward and attn_forward_ex treat
@@ -106,6 +108,35 @@ enum {
 int attn_forward(const void* q, const void* k, const void* v, void* out,
                  int64_t B, int64_t H, int64_t L, int64_t d,
                  float scale, int causal, hipStream_t stream);
+
+/*
+ * attn_forward_noalloc -- attn_forward for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments, checks, results and
+ * status codes as attn_forward; it calls no hipMalloc, hipFree, stream-ordered
+ * allocator or other allocating routine, and records no timing events.
+ *
+ * Scratch memory (the large-head-dim path's staged exponentials and
+ * statistics, the few-heads key splits' partial outputs) comes from one
+ * statically sized device array per GPU, ATTN_NOALLOC_SCRATCH_BYTES long, which
+ * each GPU the library runs on holds from the first such call until the
+ * process ends.  Heads are processed in chunks that fit it, and a key split is
+ * narrowed (or dropped) when its shares would not fit.  When one head of the
+ * large-head-dim path alone needs more than the array holds (about
+ * 2 * L * (256 * ceil(L / 256) + 128) + 8 * L * ceil(L / 256) bytes for
+ * d > 128, i.e. L above 7943) the call returns ATTN_ERR_SCRATCH_TOO_SMALL
+ * before any HIP call and queues nothing.  Nothing in the array has to start
+ * at zero: every call writes the scratch it reads.
+ *
+ * All calls on one GPU share that GPU's array: calls whose work may overlap on
+ * the device (different streams, or different host threads without ordering)
+ * race on it and give undefined results.  Serialise them (one stream, calls
+ * made in order) or use attn_forward.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (128u << 20)
+int attn_forward_noalloc(const void* q, const void* k, const void* v, void* out,
+                         int64_t B, int64_t H, int64_t L, int64_t d,
+                         float scale, int causal, hipStream_t stream);
 
 /*
  * attn_forward_ex -- the same operation on strided operands, with key/value

@@ -42,6 +42,7 @@ def fwd(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, B=1, H=1, L=16, d=
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["attn_forward", "attn_forward_ex", "attn_forward_varlen",
+                            "attn_forward_noalloc",
                             "attn_status_string",
                             "attn_path_for_head_dim", "attn_workspace_bytes",
                             "attn_timing_enable", "attn_timing_collect"])
@@ -58,7 +59,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(12):
+    for code in range(13):
         s = eab.status_string(code)
         assert s and s != "unknown status"
     assert eab.status_string(99) == "unknown status"
@@ -446,3 +447,47 @@ def test_varlen_without_key_tokens_takes_null_keys():
     assert fwd_var(k=None, v=None, **kw) == _lib.ATTN_ERR_TOO_LARGE
     kw.update(max_k=4, total_k=4)
     assert fwd_var(k=None, v=A + T, **kw) == _lib.ATTN_ERR_NULL_PTR
+
+
+# ---- attn_forward_noalloc: the same checks as attn_forward, plus its scratch limit
+
+def fwd_noalloc(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, B=1, H=1, L=16, d=64,
+                scale=0.125, causal=0):
+    return _lib.load().attn_forward_noalloc(q, k, v, out, B, H, L, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), _lib.ATTN_ERR_NULL_PTR), (dict(B=-1), _lib.ATTN_ERR_BAD_SHAPE),
+    (dict(d=96), _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM), (dict(scale=float("nan")), _lib.ATTN_ERR_BAD_SCALE),
+    (dict(k=A + 8), _lib.ATTN_ERR_MISALIGNED), (dict(out=A), _lib.ATTN_ERR_ALIAS),
+    (dict(B=0), _lib.ATTN_OK), (dict(L=0), _lib.ATTN_OK)])
+def test_noalloc_shares_the_checks_of_attn_forward(kw, code):
+    assert fwd_noalloc(**kw) == code
+    assert fwd(**kw) == code
+
+
+@pytest.mark.parametrize("L", [7944, 8000, 20000])
+def test_noalloc_rejects_a_head_beyond_its_scratch(L):
+    """d > 128: one head's staging, 2 L (256 T + 128) + 8 L T bytes (T = ceil(L / 256)),
+    must fit ATTN_NOALLOC_SCRATCH_BYTES; the call is refused before any HIP call."""
+    T = (L + 255) // 256
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert r(2 * L * (256 * T + 128)) + 2 * r(4 * T * L) > _lib.ATTN_NOALLOC_SCRATCH_BYTES
+    big = 4 * L * 1024 * 2
+    assert fwd_noalloc(q=A, k=A + big, v=A + 2 * big, out=A + 3 * big, L=L, d=1024) == \
+        _lib.ATTN_ERR_SCRATCH_TOO_SMALL
+
+
+def test_noalloc_largest_head_fits():
+    """L = 7943 is the longest head at d > 128 whose staging fits the array."""
+    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    T = (7943 + 255) // 256
+    assert r(2 * 7943 * (256 * T + 128)) + 2 * r(4 * T * 7943) <= _lib.ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_python_binding_needs_out():
+    import torch
+    with pytest.raises(TypeError):
+        eab.attention_noalloc(torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16),
+                              torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16),
+                              torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16))

@@ -230,8 +230,8 @@ int run_two_pass(const void* q, const void* k, const void* v, void* out, float* 
     const int n = (int)((BH - h0) < chunk ? (BH - h0) : chunk);
     hm.bh0 = (int)h0;  // the kernels find the chunk's heads through the map
     // This chunk's layout: E, the two statistics tables, the partial outputs.
-    const int64_t e_bytes = round256((int64_t)t.L * t.Ls * 2) * n;
-    const int64_t st_bytes = round256((int64_t)t.T * t.L * 4) * n;
+    const int64_t e_bytes = round256((int64_t)t.QB * t.EB * 1024) * n;
+    const int64_t st_bytes = round256((int64_t)t.TK * t.L * 4) * n;
     void* E = base;
     float* mref = (float*)(base + e_bytes);
     float* psum = (float*)(base + e_bytes + st_bytes);
@@ -298,9 +298,9 @@ int forward(const void* q, const void* k, const void* v, void* out, float* lse,
     return e == hipSuccess && rerr == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
   }
   const attn::TwoPassDims t = attn::two_pass_dims(L, d);
-  // E rows are addressed up to (L + 255) * Ls * 2 bytes inside a head.
-  if (t.T > attn::kTwoPassMaxTiles || (int64_t)(t.L + 256) * t.Ls * 2 >= ((int64_t)1 << 32) - 1 ||
-      (int64_t)t.T * t.T * bh >= ((int64_t)1 << 31))
+  // One head's E is addressed with 32-bit byte offsets.
+  if (t.TK > attn::kTwoPassMaxTiles || (int64_t)t.QB * t.EB * 1024 >= ((int64_t)1 << 32) - 1 ||
+      (int64_t)t.T * t.TK * bh >= ((int64_t)1 << 31))
     return ATTN_ERR_TOO_LARGE;
   if (fixed_scratch && attn::two_pass_head_bytes(t) > Scratch::capacity())
     return ATTN_ERR_SCRATCH_TOO_SMALL;
@@ -357,7 +357,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_ALIAS: return "out overlaps q, k or v";
     case ATTN_ERR_WORKSPACE: return "workspace allocation failed";
     case ATTN_ERR_HIP: return "a HIP launch or runtime call failed";
-    case ATTN_ERR_TOO_LARGE: return "problem too large: one head exceeds 32-bit byte offsets, or L > 31744 with d > 128";
+    case ATTN_ERR_TOO_LARGE: return "problem too large: one head exceeds 32-bit byte offsets, or L > 15872 with d > 128";
     case ATTN_ERR_BAD_MASK: return "the compressed causal mask takes no window";
     case ATTN_ERR_SCRATCH_TOO_SMALL:
       return "attn_forward_noalloc: one head needs more scratch memory than its fixed "

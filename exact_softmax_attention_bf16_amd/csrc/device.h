@@ -53,6 +53,38 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, void* ds
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// The four words of the buffer resource make_rsrc builds (read from lane 0),
+// for load16_to_lds_untracked.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xffffu,
+               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+
+// load16_to_lds issued from inline asm, so that the compiler does not track
+// it: it adds no wait for it before later LDS reads (it cannot tell which LDS
+// bytes a load writes when the destination stage is chosen at run time, and
+// would otherwise wait for every load in flight).  The caller must wait
+// (s_waitcnt vmcnt) for the load before any LDS read of the bytes it writes;
+// the load writes no register.  M0 holds the wave's LDS destination.
+__device__ __forceinline__ void load16_to_lds_untracked(const u32x4& r, void* dst, uint32_t voff) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dst);
+  // Re-read from lane 0 here so that the operand is formed in scalar registers
+  // (the values may have been kept in vector registers in between).
+  const u32x4 rs = {(uint32_t)__builtin_amdgcn_readfirstlane(r[0]),
+                    (uint32_t)__builtin_amdgcn_readfirstlane(r[1]),
+                    (uint32_t)__builtin_amdgcn_readfirstlane(r[2]),
+                    (uint32_t)__builtin_amdgcn_readfirstlane(r[3])};
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds),
+      "v"(voff), "s"(rs)
+      : "memory", "m0");
+}
+
 // D = A * B + C with A 32x16, B 16x32, C/D 32x32 fp32.  Lane l supplies
 // A[l % 32][8 * (l / 32) + e] and B[8 * (l / 32) + e][l % 32], e = 0..7, and
 // holds D[8 * (j / 4) + 4 * (l / 32) + j % 4][l % 32] in element j.

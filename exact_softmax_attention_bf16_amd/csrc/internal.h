@@ -71,33 +71,41 @@ __host__ __device__ inline bool band_is_full(const Band& b) {
 __host__ __device__ inline bool band_is_causal(const Band& b) {
   return b.left >= kNoLimit && b.right == 0;
 }
-// Score tiles (edge `tile` keys) that query tile qt meets: [*lo, *hi] within [0, T).
-__host__ __device__ inline void band_tiles(const Band& b, int qt, int T, int tile, int* lo,
-                                           int* hi) {
-  const int first_key = qt * tile - b.left;  // the tile's first query, leftmost key
-  *lo = (b.left >= kNoLimit || first_key <= 0) ? 0 : first_key / tile;
-  const int64_t last_key = (int64_t)qt * tile + tile - 1 + b.right;
-  *hi = (b.right >= kNoLimit || last_key >= (int64_t)T * tile) ? T - 1 : (int)(last_key / tile);
+// Key tiles (`ktile` keys each, TK of them) that the queries
+// [qt * qtile, qt * qtile + qtile) meet: [*lo, *hi] within [0, TK).
+__host__ __device__ inline void band_tiles(const Band& b, int qt, int qtile, int TK, int ktile,
+                                           int* lo, int* hi) {
+  const int first_key = qt * qtile - b.left;  // the tile's first query, leftmost key
+  *lo = (b.left >= kNoLimit || first_key <= 0) ? 0 : first_key / ktile;
+  const int64_t last_key = (int64_t)qt * qtile + qtile - 1 + b.right;
+  *hi = (b.right >= kNoLimit || last_key >= (int64_t)TK * ktile) ? TK - 1 : (int)(last_key / ktile);
+  if (*hi < *lo) *hi = *lo - 1;  // no key tile (cannot happen for bands that keep the diagonal)
 }
 
 // Sizes of the two-pass path's per-head staging, all in elements.
 struct TwoPassDims {
   int L;   // sequence length
   int d;   // head dimension
-  int T;   // number of 256-key score tiles: ceil(L / 256)
-  int Ls;  // row stride of E: 256 T + 128 (an odd multiple of 256 bytes, which
-           // spreads a tile's rows over the memory channels)
-  int Lk;  // keys the values pass iterates over: ceil(L / 64) * 64 (<= Ls)
+  int T;   // number of 256-query tiles: ceil(L / 256)
+  int TK;  // number of 128-key score tiles (the statistics' granularity): ceil(L / 128)
+  int QB;  // 32-query blocks of E: ceil(L / 32)
+  int EB;  // 16-key blocks of E per query block: 16 T (keys padded to 256 T)
+  int Lk;  // keys the values pass iterates over: ceil(L / 64) * 64 (<= 256 T)
 };
+// E, the bf16 exponentials, is stored in 1 KB blocks of 32 queries x 16 keys:
+// block (qb, kb) of a head holds, at element 8 * lane, keys 16 kb + 8 (lane / 32)
+// .. + 8 (in the scores pass's key order) of query 32 qb + lane % 32 -- the 16
+// bytes one lane of a register-direct store holds, and the 16 bytes one lane
+// of the values pass's MFMA operand needs.  Blocks are ordered [qb][kb].
 
 TwoPassDims two_pass_dims(int64_t L, int64_t d);
 
-// The values pass keeps one byte per (score tile, query) of its query tile in
-// LDS next to the 128 KB GEMM stages, which caps L at 124 * 256 = 31744 there.
+// The values pass keeps one byte per (128-key score tile, query) of its query
+// tile in LDS next to the 128 KB GEMM stages, which caps L at 124 * 128 = 15872.
 constexpr int kTwoPassMaxTiles = 124;
 
 // Bytes of workspace one head needs on the two-pass path: E and the
-// per-(tile, query) exponent reference and partial sum.
+// per-(128-key tile, query) exponent reference and partial sum.
 int64_t two_pass_head_bytes(const TwoPassDims& t);
 
 // A split of each query block's keys among n workgroups (n > 1): share s of
@@ -141,7 +149,7 @@ hipError_t launch_online_combine(const KeySplit& ks, void* out, float* lse, cons
 // compute units idle.  Shape only.
 int online_split(int64_t BH, int64_t Lq, int64_t Lk);
 
-// Scores pass: per 256x256 (key, query) tile, E = bf16(2^(y - m)) with
+// Scores pass: per 128-key x 256-query tile, E = bf16(2^(y - m)) with
 // y = sl2 * q.k, m = ceil(max over the tile's keys of y) per query, plus m and
 // the sum of the stored E per (tile, query).
 hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, float* psum,

@@ -45,7 +45,9 @@ TwoPassDims two_pass_dims(int64_t L, int64_t d) {
   t.L = (int)L;
   t.d = (int)d;
   t.T = (int)((L + kTile - 1) / kTile);
-  t.Ls = t.T * kTile + kTile / 2;
+  t.TK = (int)((L + 127) / 128);
+  t.QB = (int)((L + 31) / 32);
+  t.EB = 16 * t.T;
   t.Lk = (int)((L + 63) / 64 * 64);
   return t;
 }
@@ -53,7 +55,7 @@ TwoPassDims two_pass_dims(int64_t L, int64_t d) {
 static int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
 int64_t two_pass_head_bytes(const TwoPassDims& t) {
-  return round256((int64_t)t.L * t.Ls * 2) + 2 * round256((int64_t)t.T * t.L * 4);
+  return round256((int64_t)t.QB * t.EB * 1024) + 2 * round256((int64_t)t.TK * t.L * 4);
 }
 
 namespace {
@@ -69,21 +71,24 @@ __device__ __forceinline__ u32x4 unswap_halves(u32x4 x, int r) {
 // queries [256 qt, +256) on the N side, so each lane of the accumulator owns a
 // query and holds 4 runs of 4 consecutive keys per 32x32 block.
 //
-// E layout: row `query` of head bh holds the tile's keys in blocks of 32; inside
-// a block, key c sits at position kperm(c) (bits 2 and 3 of c exchanged).  A
-// lane's 16 values of one 32x32 accumulator block are then two runs of 8
-// consecutive positions, stored straight from registers as two 16-byte writes
-// (the lanes of the other half-wave fill the 16 bytes between).  The values
-// pass reads V rows in the same order.
+// E layout (internal.h): 1 KB blocks of 32 queries x 16 key positions.  Inside
+// each 32-key block of a tile, key c sits at position kperm(c) (bits 2 and 3 of
+// c exchanged), so that a lane's 16 values of one 32x32 accumulator block are
+// two runs of 8 consecutive positions, i.e. 16 bytes in each of two blocks: one
+// register-direct store instruction writes one whole block (8 full cache lines;
+// row-major E took 32 scattered 32-byte pieces per instruction and cost a fifth
+// of this pass).  The values pass reads V rows in the same key order.
 //
-// Epilogue, per query: m = ceil(max over the tile's keys of y), y = sl2 * s;
-// E = bf16(2^(y - m)) (so 1/2 < max E <= 1); psum = sum of the stored E.
-// MASK selects the edge-tile version (keys past L, keys after the query); it is
-// a template flag so that the per-element test compiles to selects, not branches.
+// Statistics per 128-key half of a tile (the keys one wave holds), so that
+// each wave's epilogue needs nothing from the others: per query,
+// m = ceil(max over the half's keys of y), y = sl2 * s; E = bf16(2^(y - m))
+// (so 1/2 < max E <= 1); psum = sum of the stored E.  Half h of tile kt is
+// statistics tile 2 kt + h.  MASK selects the edge-tile version (keys past L,
+// keys outside the band); it is a template flag so that the per-element test
+// compiles to selects, not branches.
+constexpr int kSK = 128;  // keys per statistics tile
 struct ScoresSmem {
   GemmSmem g;
-  float red[2][kTile];   // per-wave-row partial maxima
-  float red2[2][kTile];  // per-wave-row partial sums
 };
 
 struct ScoresTile {
@@ -128,7 +133,7 @@ __device__ __forceinline__ ScoresTile scores_tile(int idx, int T, const Band& ba
   } else {
     int qt = 0, lo = 0, hi = 0;
     for (;; ++qt) {  // r < per_head: ends at a query tile below T
-      band_tiles(band, qt, T, kTile, &lo, &hi);
+      band_tiles(band, qt, kTile, T, kTile, &lo, &hi);
       if (r <= hi - lo) break;
       r -= hi - lo + 1;
     }
@@ -160,29 +165,30 @@ __device__ __forceinline__ bool scores_wave_idle(const ScoresTile& t, int wave, 
 }
 
 template <bool MASK>
-__device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ], ScoresSmem& sm,
+__device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ],
                                                 uint16_t* __restrict__ E,
                                                 float* __restrict__ mref,
                                                 float* __restrict__ psum, const ScoresTile& t,
-                                                int L, int Ls, int T, float sl2, const Band& band) {
+                                                int L, int QB, int EB, int TK, float sl2,
+                                                const Band& band) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = scores_key_half(wave), c32 = lane & 31, h = lane >> 5;
   const int qbase = scores_query_base(wave);  // this wave's first query column in the tile
-  const int key0 = t.kt * kTile + wm * 128;
-  uint16_t* Eh = E + (size_t)t.bh * L * Ls;
-  float mt[kScoresNJ], ps[kScoresNJ];
+  const int key0 = t.kt * kTile + wm * kSK;
+  uint16_t* Eh = E + (size_t)t.bh * QB * EB * 512;
+  // This half's statistics (none for a half wholly past L: no such tile).
+  const bool stats = key0 < L;
+  float* mref_t = mref + ((size_t)t.bh * TK + (key0 / kSK)) * L;
+  float* psum_t = psum + ((size_t)t.bh * TK + (key0 / kSK)) * L;
 
-  // One column of accumulator blocks (32 queries) at a time: partial maximum
-  // over this wave's 128 keys, exchange with the wave holding the other 128
-  // keys, exponentials and stores.
 #pragma unroll
   for (int bj = 0; bj < kScoresNJ; ++bj) {
     const int ql = qbase + bj * 32 + c32;
     const int query = t.qt * kTile + ql;
     // Key key0 + 4h + c (c = 32 bi + 8 (j / 4) + j % 4, a constant) is allowed
     // for this query iff lo <= c < lim.
-    int lim = min(L, query + band.right + 1) - (key0 + 4 * h);
-    int lo = query - band.left - (key0 + 4 * h);
+    const int lim = min(L, query + band.right + 1) - (key0 + 4 * h);
+    const int lo = query - band.left - (key0 + 4 * h);
     auto masked = [&](int bi, int j) {
       const int c = bi * 32 + 8 * (j >> 2) + (j & 3);
       return c >= lim || c < lo;
@@ -190,41 +196,36 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ], Sco
 
     // Maximum of y (interior tiles: on the raw accumulator, then scaled; the
     // sign of sl2 picks max or min).
-    float wmax;
+    float tmax;
     if (!MASK && sl2 >= 0.f) {
       float hi = acc[0][bj][0];
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
         for (int j = 0; j < 16; ++j) hi = fmaxf(hi, acc[bi][bj][j]);
-      wmax = hi * sl2;
+      tmax = hi * sl2;
     } else if (!MASK) {
-      float lo = acc[0][bj][0];
+      float lo2 = acc[0][bj][0];
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) lo = fminf(lo, acc[bi][bj][j]);
-      wmax = lo * sl2;
+        for (int j = 0; j < 16; ++j) lo2 = fminf(lo2, acc[bi][bj][j]);
+      tmax = lo2 * sl2;
     } else {
       float mx = -INFINITY;
 #pragma unroll
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
         for (int j = 0; j < 16; ++j) mx = fmaxf(mx, masked(bi, j) ? -INFINITY : acc[bi][bj][j] * sl2);
-      wmax = mx;
+      tmax = mx;
     }
-    wmax = wave_swap32_max(wmax);
-    if (h == 0) sm.red[wm][ql] = wmax;
-    __syncthreads();  // both key halves' maxima for this column are in red
-    // Recompute the mask below instead of keeping 64 mask bits alive across the
-    // barrier (the compiler would otherwise hold them in scalar registers).
-    asm volatile("" : "+v"(lim), "+v"(lo));
-
-    const float tmax = fmaxf(sm.red[0][ql], sm.red[1][ql]);
+    tmax = wave_swap32_max(tmax);
     const float m2 = tmax == -INFINITY ? -INFINITY : ceilf(tmax);
     const float add = tmax == -INFINITY ? 0.f : -m2;
     float s = 0.f;
-    uint16_t* row = Eh + (size_t)min(query, L - 1) * Ls + key0 + 8 * h;
+    // This column's 32 queries are one query block; blocks 2 bi and 2 bi + 1 of
+    // the half's 16-key blocks take w[0] and w[1].
+    uint16_t* blk = Eh + ((size_t)(min(query, L - 1) >> 5) * EB + (key0 >> 4)) * 512 + lane * 8;
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
       u32x4 w[2];
@@ -244,31 +245,16 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ], Sco
         w[i >> 1][2 * (i & 1) + 1] = w1;
       }
       if (query < L) {
-        *(u32x4*)(row + 32 * bi) = w[0];
-        *(u32x4*)(row + 32 * bi + 16) = w[1];
+        *(u32x4*)(blk + (2 * bi) * 512) = w[0];
+        *(u32x4*)(blk + (2 * bi + 1) * 512) = w[1];
       }
     }
-    mt[bj] = m2;
-    ps[bj] = wave_swap32_sum(s);
+    s = wave_swap32_sum(s);
+    if (h == 0 && query < L && stats) {
+      mref_t[query] = m2;
+      psum_t[query] = s;
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep the next column's copies after this one's
-  }
-  if (h == 0) {
-#pragma unroll
-    for (int bj = 0; bj < kScoresNJ; ++bj) sm.red2[wm][qbase + bj * 32 + c32] = ps[bj];
-  }
-  __syncthreads();  // partial sums complete
-  if (wm == 0 && h == 0) {
-    float* mref_t = mref + ((size_t)t.bh * T + t.kt) * L;
-    float* psum_t = psum + ((size_t)t.bh * T + t.kt) * L;
-#pragma unroll
-    for (int bj = 0; bj < kScoresNJ; ++bj) {
-      const int ql = qbase + bj * 32 + c32;
-      const int query = t.qt * kTile + ql;
-      if (query < L) {
-        mref_t[query] = mt[bj];
-        psum_t[query] = sm.red2[0][ql] + sm.red2[1][ql];
-      }
-    }
   }
 }
 
@@ -280,8 +266,8 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ], Sco
 // One LDS object (see the GEMM loop's notes on the compiler's LDS-DMA waits).
 __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, uint16_t* __restrict__ E,
-    float* __restrict__ mref, float* __restrict__ psum, HeadMap hm, int L, int d, int T, int Ls,
-    float sl2, Band band, int per_head, int ntiles) {
+    float* __restrict__ mref, float* __restrict__ psum, HeadMap hm, int L, int d, int T, int TK,
+    int QB, int EB, float sl2, Band band, int per_head, int ntiles) {
   __shared__ ScoresSmem smem;
   GemmSmem& sm = smem.g;
 
@@ -431,9 +417,9 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
       for (int kk = 1; kk < nk; ++kk) step(std::false_type{}, s++);
     }
     if (!scores_tile_unmasked(t, band, L))
-      scores_epilogue<true>(acc, smem, E, mref, psum, t, L, Ls, T, sl2, band);
+      scores_epilogue<true>(acc, E, mref, psum, t, L, QB, EB, TK, sl2, band);
     else
-      scores_epilogue<false>(acc, smem, E, mref, psum, t, L, Ls, T, sl2, band);
+      scores_epilogue<false>(acc, E, mref, psum, t, L, QB, EB, TK, sl2, band);
     // The next step's first fragments: read again (its stage is not refilled
     // before that step's end) instead of holding them through the epilogue.
     read_frags(cur, la, lb, sm.a[s & 1], sm.b[s & 1], abase, bbase, lane, 0);
@@ -444,21 +430,21 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
 // ---------------------------------------------------------------------------
 // Values pass.  Tile (ct, qt): channels [256 ct, +256) on the M side (A = V^T),
 // queries [256 qt, +256) on the N side (B = E), K = keys in 64-wide steps.
-// Each lane owns four queries (one per 32-column block j); before each group
-// of four steps (one 256-key score tile t) it turns M - m_t into the exponent
-// shift for those queries, fetched one tile ahead.
+// Each lane owns four queries (one per 32-column block j); before each pair
+// of steps (one 128-key score tile t) it turns M - m_t into the exponent
+// shift for those queries.
 constexpr int kMaxTiles = kTwoPassMaxTiles;
 
 struct PowerOfTwoShift {
-  const uint8_t (*tab)[kTile];  // [t][query in tile]: M - m_t, capped at 255
+  const uint8_t (*tab)[kTile];  // [128-key tile t][query in tile]: M - m_t, capped at 255
   int col[4];                   // this lane's four query columns in the tile
   unsigned sw[4];               // current shift words (s << 7 | s << 23)
 
   __device__ __forceinline__ void step(int kt, bool first) {
-    if ((kt & 3) == 0 || first) {
+    if ((kt & 1) == 0 || first) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const unsigned s = tab[kt >> 2][col[j]];
+        const unsigned s = tab[kt >> 1][col[j]];
         sw[j] = (s << 7) | (s << 23);
       }
     }
@@ -477,19 +463,70 @@ struct ValuesSmem {
   float inv_l[kTile];
 };
 
+// Staging of the values pass, 8 waves: V read as V^T (64 key rows x 256
+// channels per stage, 512 bytes per row, 16-byte chunk c of row r at
+// c ^ 4 (r % 4), stage row r holding key k0 + kperm(r): the order the scores
+// pass gives the keys of each 32-key block of E) and E (the 8 x 4 blocks of
+// 32 queries x 16 keys the step covers, copied as they are: block (i, j) at
+// 1 KB x (4 i + j); a lane's MFMA operand is 16 contiguous bytes of a block).
+// Each wave issues 4 loads of each per step, through untracked direct loads:
+// the transpose reads of V carry no alias information, and the compiler would
+// otherwise wait for every load in flight before each of them.
+constexpr int kValuesWaves = 8;
+struct ValuesV {
+  uint32_t off[4];
+  uint32_t ld2;  // bytes per key row
+  __device__ __forceinline__ void init(uint32_t ld, int m0, int wave, int lane) {
+    ld2 = ld * 2u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int P = (wave * 4 + j) * 64 + lane;  // 16-byte chunk slot in the stage
+      const int row = P >> 5, pc = P & 31, lc = pc ^ ((row & 3) << 2);
+      off[j] = (uint32_t)kperm(row) * ld2 + (uint32_t)(m0 + lc * 8) * 2u;
+    }
+  }
+  __device__ __forceinline__ void issue(const u32x4& r, int k0, char* stage, int wave, int j) const {
+    load16_to_lds_untracked(r, stage + (wave * 4 + j) * 1024, off[j] + (uint32_t)k0 * ld2);
+  }
+};
+// Wave w copies query block w of the tile's 8, key blocks k0 / 16 .. + 4.
+struct ValuesE {
+  uint32_t off;
+  __device__ __forceinline__ void init(int EB, int wave, int lane) {
+    off = (uint32_t)wave * (uint32_t)EB * 1024u + (uint32_t)lane * 16u;
+  }
+  __device__ __forceinline__ void issue(const u32x4& r, int k0, char* stage, int wave, int j) const {
+    load16_to_lds_untracked(r, stage + (wave * 4 + j) * 1024, off + (uint32_t)((k0 >> 4) + j) * 1024u);
+  }
+};
+
+// One k16 sub-step's fragments of a values wave: 2 V^T blocks of 32 channels,
+// 4 E blocks of 32 queries.
+struct ValuesFrags {
+  bf16x8 a[2], b[4];
+};
+
 // SPLIT: the keys of each query tile are divided among `split` workgroups that
 // write fp32 shares of O to `part` (a separate instantiation, so that the
 // unsplit kernel carries none of it).
+//
+// 8 waves, two per SIMD: wave w owns channels [64 (w % 4), +64) x queries
+// [128 (w / 4), +128) of the tile, as 2 x 4 accumulator blocks.  Per k16
+// sub-step it reads 2 V^T fragments (two transpose reads each) and 4 E
+// fragments for 8 MFMAs; the next sub-step's fragments are read while the
+// current MFMAs run.  The next step's loads go out one per MFMA pair in the
+// step's first two sub-steps (into the stage the previous step drained).
 template <bool SPLIT>
-__global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict__ v,
+__global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_t* __restrict__ v,
                                                      const uint16_t* __restrict__ E,
                                                      const float* __restrict__ mref,
                                                      const float* __restrict__ psum,
                                                      uint16_t* __restrict__ out,
                                                      float* __restrict__ lse,
                                                      float* __restrict__ part, HeadMap hm, int L,
-                                                     int d, int T, int Ls, int Lk, Band band,
-                                                     int ncb, int split, int nheads) {
+                                                     int d, int T, int TK, int QB, int EB,
+                                                     int Lk, Band band, int ncb, int split,
+                                                     int nheads) {
   __shared__ ValuesSmem smem;
   GemmSmem& sm = smem.g;
   uint8_t(&shift_tab)[kMaxTiles][kTile] = smem.shift_tab;
@@ -502,25 +539,27 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
   const int r = lid % per_head;
   const int qt = r / (ncb * split), ct = (r / split) % ncb, sp = SPLIT ? r % split : 0;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, c32 = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cq = wave & 3, qh = wave >> 2, c32 = lane & 31, h = lane >> 5;
 
-  // Score tiles [tlo, thi] meet this query tile's band: keys [kbeg, kend).
+  // Score tiles [tlo, thi] (128 keys each) meet this query tile's band: keys
+  // [kbeg, kend).
   int tlo, thi;
-  band_tiles(band, qt, T, kTile, &tlo, &thi);
-  const int kbeg = tlo * kTile, kend = min(Lk, (thi + 1) * kTile);
+  band_tiles(band, qt, kTile, TK, kSK, &tlo, &thi);
+  const int kbeg = tlo * kSK, kend = min(Lk, (thi + 1) * kSK);
   // Split sp of `split` takes K steps [k_first, k_first + nk) (never empty:
   // the host keeps split <= the fewest steps of any query tile).
   const int nk_all = (kend - kbeg) / kStepK;
   const int k_first = kbeg / kStepK + (SPLIT ? nk_all * sp / split : 0);
   const int nk = SPLIT ? kbeg / kStepK + nk_all * (sp + 1) / split - k_first : nk_all;
 
-  // Thread tid owns query qt*256 + tid: M = max_t m_t, l = sum_t 2^(m_t - M) psum_t,
+  // Thread tid < 256 owns query qt*256 + tid: M = max_t m_t, l = sum_t 2^(m_t - M) psum_t,
   // and the shift M - m_t of each tile (a nonnegative integer; -inf tiles -> 255).
   // The stats are read in batches of 16 tiles so their latencies overlap.
-  {
-    const float* mh = mref + (size_t)bh * T * L;
-    const float* ph = psum + (size_t)bh * T * L;
+  if (tid < kTile) {
+    const float* mh = mref + (size_t)bh * TK * L;
+    const float* ph = psum + (size_t)bh * TK * L;
     const int qc = min(qt * kTile + tid, L - 1);
     float M = -INFINITY, l = 0.f;
     for (int t0 = tlo; t0 <= thi; t0 += 16) {
@@ -555,26 +594,86 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
     if (lse != nullptr && ct == 0 && sp == 0 && query < L)
       lse[(size_t)(hm.bh0 + bh) * L + query] = (M + log2f(l)) * 0.6931471805599453f;
   }
-  __syncthreads();
+
+  // V's resource ends after the head's row L - 1 (keys past L read as zero).
+  // Channels past d of a 256-channel tile read whatever lies there (zero past
+  // the end) and only feed accumulator rows that are never stored.
+  const int ldv = hm.v.ld;
+  const u32x4 rv = rsrc_words(v + hm.v_off(bh), ((uint32_t)(L - 1) * ldv + d) * 2u);
+  // E from the tile's first query block; blocks past the head's last read as zero.
+  const u32x4 re = rsrc_words(E + ((size_t)bh * QB + (size_t)qt * 8) * EB * 512,
+                              (uint32_t)(QB - qt * 8) * (uint32_t)EB * 1024u);
+  ValuesV la;
+  ValuesE lb;
+  la.init((uint32_t)ldv, ct * kTile, wave, lane);
+  lb.init(EB, wave, lane);
+  auto issue = [&](int k0, int st, int j) {  // load j (0..7) of the step at key k0
+    if (j < 4)
+      la.issue(rv, k0, sm.a[st], wave, j);
+    else
+      lb.issue(re, k0, sm.b[st], wave, j - 4);
+  };
+  const int kb = k_first * kStepK;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) issue(kb, 0, j);
+  wait_vmem();
+  __syncthreads();  // step 0 staged; the shift table and 1/l are complete
 
   PowerOfTwoShift sh;
   sh.tab = shift_tab;
   float invl[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    sh.col[j] = wn * 128 + j * 32 + c32;
+    sh.col[j] = qh * 128 + j * 32 + c32;
     invl[j] = inv_l[sh.col[j]];
   }
 
-  // V's resource ends after the head's row L - 1 (keys past L read as zero).
-  // Channels past d of a 256-channel tile read whatever lies there (zero past
-  // the end) and only feed accumulator rows that are never stored.
-  const int ldv = hm.v.ld;
-  const auto ra = make_rsrc(v + hm.v_off(bh), ((uint32_t)(L - 1) * ldv + d) * 2u);
-  const auto rb = make_rsrc(E + (size_t)bh * L * Ls, (uint32_t)L * Ls * 2);
-  f32x16 acc[4][4];
-  gemm_tile<KOuter>(acc, ra, (uint32_t)ldv, ct * kTile, rb, (uint32_t)Ls, qt * kTile, k_first, nk,
-                    sm, sh);
+  KOuter ka;  // fragment reads only (the loads go through ValuesV)
+  auto read = [&](ValuesFrags& f, const char* sa, const char* sb, int ss) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) f.a[i] = ka.frag(sa, cq * 64 + i * 32, ss, lane);
+    // E block (query block 4 qh + j, key block ss): 16 contiguous bytes per lane.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[j] = *(const bf16x8*)(sb + ((qh * 4 + j) * 4 + ss) * 1024 + lane * 16);
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  ValuesFrags cur, nxt;
+  read(cur, sm.a[0], sm.b[0], 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    const bool more = kt + 1 < nk;
+    // Past the last step: a reload of the last step into the stage no longer
+    // read, so that every step issues its loads unconditionally.
+    const int k1 = kb + (more ? kt + 1 : kt) * kStepK;
+    sh.step(k_first + kt, kt == 0);
+#pragma unroll
+    for (int ss = 0; ss < 4; ++ss) {
+      if (ss < 3) read(nxt, sm.a[st], sm.b[st], ss + 1);
+      bf16x8 bt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bt[j] = sh(cur.b[j], j);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int i = p >> 1, j0 = 2 * (p & 1);
+        acc[i][j0] = mfma32x32x16(cur.a[i], bt[j0], acc[i][j0]);
+        acc[i][j0 + 1] = mfma32x32x16(cur.a[i], bt[j0 + 1], acc[i][j0 + 1]);
+        if (ss < 2) issue(k1, st ^ 1, ss * 4 + p);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (ss < 3) cur = nxt;
+    }
+    // The next step is staged everywhere; this step's stage is no longer read.
+    wait_vmem();
+    __syncthreads();
+    if (more) read(cur, sm.a[st ^ 1], sm.b[st ^ 1], 0);
+  }
 
   if constexpr (SPLIT) {
     // This split's share of O = (its part of the sum) / l, in fp32, for the
@@ -582,13 +681,13 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
     float* ph = part + ((size_t)sp * nheads + bh) * L * d;
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
-      const int query = qt * kTile + wn * 128 + bj * 32 + c32;
+      const int query = qt * kTile + qh * 128 + bj * 32 + c32;
       if (query >= L) continue;
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi)
+      for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int ch = ct * kTile + wm * 128 + bi * 32 + 8 * i + 4 * h;
+          const int ch = ct * kTile + cq * 64 + bi * 32 + 8 * i + 4 * h;
           if (ch < d) {
             const f32x16& a = acc[bi][bj];
             f32x4 o = {a[4 * i] * invl[bj], a[4 * i + 1] * invl[bj], a[4 * i + 2] * invl[bj],
@@ -603,20 +702,19 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
   // O[query][ch] = acc / l, rounded once to bf16.  The tile goes through the
   // drained GEMM stages as [query][256 channels] rows (laid out like the E tile
   // of the scores pass) so that the global stores write whole row segments.
-  __syncthreads();  // every wave is past its GEMM: the stages are free
   char* stage = sm.a[0];
 #pragma unroll
   for (int bj = 0; bj < 4; ++bj) {
-    const int ql = wn * 128 + bj * 32 + c32;
+    const int ql = qh * 128 + bj * 32 + c32;
     char* row = stage + ql * 512 + 8 * (h ^ (c32 >> 4));
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
+    for (int bi = 0; bi < 2; ++bi) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f32x16& a = acc[bi][bj];
         const u32x2 w = {pack_bf16x2(a[4 * i] * invl[bj], a[4 * i + 1] * invl[bj]),
                          pack_bf16x2(a[4 * i + 2] * invl[bj], a[4 * i + 3] * invl[bj])};
-        const int chunk = wm * 16 + bi * 4 + i;
+        const int chunk = cq * 8 + bi * 4 + i;
         *(u32x2*)(row + ((chunk ^ c32) << 4)) = w;
       }
     }
@@ -629,10 +727,10 @@ __global__ __launch_bounds__(256) void values_kernel(const uint16_t* __restrict_
       const int ldo = hm.o.ld;
       uint16_t* oh = out + hm.o_off(bh) + (size_t)(qt * kTile) * ldo + ch;
 #pragma unroll 8
-      for (int j = 0; j < 32; ++j) {
-        const int r = (tid >> 5) + 8 * j;
-        if (qt * kTile + r < L)
-          *(u32x4*)(oh + (size_t)r * ldo) = unswap_halves(*(const u32x4*)(stage + r * 512 + ((c ^ (r & 31)) << 4)), r);
+      for (int j = 0; j < 16; ++j) {
+        const int rr = (tid >> 5) + 16 * j;
+        if (qt * kTile + rr < L)
+          *(u32x4*)(oh + (size_t)rr * ldo) = unswap_halves(*(const u32x4*)(stage + rr * 512 + ((c ^ (rr & 31)) << 4)), rr);
       }
     }
   }
@@ -684,7 +782,7 @@ int band_tiles_per_head(const Band& band, int T) {
   int n = 0;
   for (int qt = 0; qt < T; ++qt) {
     int lo, hi;
-    band_tiles(band, qt, T, kTile, &lo, &hi);
+    band_tiles(band, qt, kTile, T, kTile, &lo, &hi);
     n += hi - lo + 1;
   }
   return n;
@@ -696,13 +794,14 @@ hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, flo
   const uint16_t* qp = (const uint16_t*)q;
   const uint16_t* kp = (const uint16_t*)k;
   uint16_t* ep = (uint16_t*)E;
-  int L = t.L, d = t.d, T = t.T, Ls = t.Ls;
+  int L = t.L, d = t.d, T = t.T, TK = t.TK, QB = t.QB, EB = t.EB;
   int per_head = band_tiles_per_head(band, T);
   int ntiles = BH * per_head;
   const int grid = std::min(ntiles, device_cu_count());  // one workgroup per CU (LDS-bound)
   HeadMap m = hm;
   Band b = band;
-  void* args[] = {&qp, &kp, &ep, &mref, &psum, &m, &L, &d, &T, &Ls, &sl2, &b, &per_head, &ntiles};
+  void* args[] = {&qp, &kp, &ep, &mref, &psum, &m, &L, &d, &T, &TK, &QB, &EB, &sl2, &b, &per_head,
+                  &ntiles};
   return hipLaunchKernel((const void*)&scores_kernel, dim3((unsigned)grid),
                          dim3(64 * kScoresWaves), args, 0, s);
 }
@@ -713,8 +812,8 @@ int values_split(int64_t BH, const TwoPassDims& t, const Band& band) {
   int64_t fewest = t.Lk / kStepK;  // K steps of the narrowest query tile's band
   for (int qt = 0; qt < t.T; ++qt) {
     int lo, hi;
-    band_tiles(band, qt, t.T, kTile, &lo, &hi);
-    fewest = std::min<int64_t>(fewest, (std::min(t.Lk, (hi + 1) * kTile) - lo * kTile) / kStepK);
+    band_tiles(band, qt, kTile, t.TK, kSK, &lo, &hi);
+    fewest = std::min<int64_t>(fewest, (std::min(t.Lk, (hi + 1) * kSK) - lo * kSK) / kStepK);
   }
   // Each split keeps at least kValuesMinSplitSteps K steps: shorter loops are
   // dominated by the fixed cost of a workgroup, and the partials cost a pass.
@@ -729,15 +828,16 @@ hipError_t launch_values(const void* v, const void* E, const float* mref, const 
   const uint16_t* vtp = (const uint16_t*)v;
   const uint16_t* ep = (const uint16_t*)E;
   uint16_t* op = (uint16_t*)out;
-  int L = t.L, d = t.d, T = t.T, Ls = t.Ls, Lk = t.Lk;
+  int L = t.L, d = t.d, T = t.T, TK = t.TK, QB = t.QB, EB = t.EB, Lk = t.Lk;
   int ncb = (t.d + kTile - 1) / kTile;
   int nheads = BH;
   HeadMap m = hm;
   Band b = band;
-  void* args[] = {&vtp, &ep, &mref, &psum, &op, &lse, &part, &m, &L, &d, &T, &Ls, &Lk, &b, &ncb,
-                  &split, &nheads};
+  void* args[] = {&vtp, &ep, &mref, &psum, &op, &lse, &part, &m, &L, &d, &T, &TK, &QB, &EB, &Lk, &b,
+                  &ncb, &split, &nheads};
   const void* kern = split > 1 ? (const void*)&values_kernel<true> : (const void*)&values_kernel<false>;
-  return hipLaunchKernel(kern, dim3((unsigned)(BH * T * ncb * split)), dim3(256), args, 0, s);
+  return hipLaunchKernel(kern, dim3((unsigned)(BH * T * ncb * split)), dim3(64 * kValuesWaves), args,
+                         0, s);
 }
 
 hipError_t launch_values_reduce(const float* part, void* out, int split, const HeadMap& hm,

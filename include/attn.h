@@ -98,7 +98,7 @@ enum {
  * combine); that uses the workspace buffer below too (attn_workspace_bytes
  * gives its size).  For d > 128 the call uses the
  * workspace buffer the library keeps for (current device, stream), growing it
- * when needed (about 2*L*(256*ceil(L/256) + 128) + 8*L*ceil(L/256) bytes per
+ * when needed (about 16384*ceil(L/32)*ceil(L/256) + 8*L*ceil(L/128) bytes per
  * head, heads processed in chunks of at most 2 GiB; when so few heads would
  * leave most compute units idle, also up to 4 fp32 copies of the output for
  * a split over the keys -- attn_workspace_bytes gives the exact figure).
@@ -123,8 +123,8 @@ int attn_forward(const void* q, const void* k, const void* v, void* out,
  * process ends.  Heads are processed in chunks that fit it, and a key split is
  * narrowed (or dropped) when its shares would not fit.  When one head of the
  * large-head-dim path alone needs more than the array holds (about
- * 2 * L * (256 * ceil(L / 256) + 128) + 8 * L * ceil(L / 256) bytes for
- * d > 128, i.e. L above 7943) the call returns ATTN_ERR_SCRATCH_TOO_SMALL
+ * 16384 * ceil(L / 32) * ceil(L / 256) + 8 * L * ceil(L / 128) bytes for
+ * d > 128, i.e. L above 7936) the call returns ATTN_ERR_SCRATCH_TOO_SMALL
  * before any HIP call and queues nothing.  Nothing in the array has to start
  * at zero: every call writes the scratch it reads.
  *

@@ -88,20 +88,22 @@ def _values_split(n, L, d, causal):
 
 
 def test_workspace_bytes():
-    # per head: E (L rows of 256*T + 128 bf16, T = ceil(L/256)) and two fp32 [T, L] tables;
-    # plus split * n * L * d fp32 partial outputs when the values pass splits the keys
-    L, d, T = 3432, 1024, 14
-    ls = 256 * T + 128
+    # per head: E (1 KB blocks of 32 queries x 16 keys: ceil(L/32) x 16 T of them,
+    # T = ceil(L/256)) and two fp32 [TK, L] tables (TK = ceil(L/128) score tiles of
+    # 128 keys); plus split * n * L * d fp32 partial outputs when the values pass
+    # splits the keys
+    L, d, T, TK = 3432, 1024, 14, 27
     r = lambda x: (x + 255) // 256 * 256
-    per_head = r(L * ls * 2) + 2 * r(T * L * 4)
+    e_bytes = lambda n: ((n + 31) // 32) * 16 * ((n + 255) // 256) * 1024  # noqa: E731
+    per_head = r(e_bytes(L)) + 2 * r(TK * L * 4)
     assert _values_split(1, L, d, False) == 4 and _values_split(31, L, d, False) == 1
     assert _values_split(4, L, d, False) == 1
     assert eab.workspace_bytes(1, 1, L, d) == per_head + r(4 * L * d * 4)
     assert eab.workspace_bytes(4, 1, L, d) == 4 * per_head
     assert eab.workspace_bytes(31, 1, L, d) == 31 * per_head
     # tiny: L = 286, d = 256: 5 K steps -> too short to split
-    Lt, dt, Tt = 286, 256, 2
-    pt = r(Lt * (256 * Tt + 128) * 2) + 2 * r(Tt * Lt * 4)
+    Lt, dt = 286, 256
+    pt = r(e_bytes(Lt)) + 2 * r(3 * Lt * 4)
     assert _values_split(1, Lt, dt, False) == 1
     assert eab.workspace_bytes(1, 1, Lt, dt) == pt
     # causal: the first query tile has 4 K steps -> no split
@@ -110,7 +112,7 @@ def test_workspace_bytes():
     # L = 1100, d = 256: base 5, 18 K steps -> 2 splits
     assert _values_split(1, 1100, 256, False) == 2
     assert eab.workspace_bytes(1, 1, 1100, 256) == (
-        r(1100 * (256 * 5 + 128) * 2) + 2 * r(5 * 1100 * 4) + r(2 * 1100 * 256 * 4))
+        r(e_bytes(1100)) + 2 * r(9 * 1100 * 4) + r(2 * 1100 * 256 * 4))
     assert eab.workspace_bytes(4, 8, 1024, 64) == 0       # online path, 256 workgroups: none
     assert eab.workspace_bytes(0, 1, L, d) == 0
     big = eab.workspace_bytes(1000, 1, L, d)              # chunked under ~2 GiB
@@ -174,8 +176,8 @@ def test_too_large_two_pass_head():
 
 
 def test_two_pass_length_cap():
-    # the values pass keeps a byte per (256-key tile, query) in LDS: L <= 124 * 256 when d > 128
-    L, d = 124 * 256 + 1, 192
+    # the values pass keeps a byte per (128-key tile, query) in LDS: L <= 124 * 128 when d > 128
+    L, d = 124 * 128 + 1, 192
     n = L * d * 2
     assert fwd(q=A, k=A + n, v=A + 2 * n, out=A + 3 * n, L=L, d=d) == _lib.ATTN_ERR_TOO_LARGE
 
@@ -466,23 +468,26 @@ def test_noalloc_shares_the_checks_of_attn_forward(kw, code):
     assert fwd(**kw) == code
 
 
-@pytest.mark.parametrize("L", [7944, 8000, 20000])
-def test_noalloc_rejects_a_head_beyond_its_scratch(L):
-    """d > 128: one head's staging, 2 L (256 T + 128) + 8 L T bytes (T = ceil(L / 256)),
-    must fit ATTN_NOALLOC_SCRATCH_BYTES; the call is refused before any HIP call."""
-    T = (L + 255) // 256
+def _two_pass_head_bytes(L):
+    """E (ceil(L/32) x 16 ceil(L/256) blocks of 1 KB) and two fp32 [ceil(L/128), L] tables."""
     r = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert r(2 * L * (256 * T + 128)) + 2 * r(4 * T * L) > _lib.ATTN_NOALLOC_SCRATCH_BYTES
+    T, TK, QB = (L + 255) // 256, (L + 127) // 128, (L + 31) // 32
+    return r(QB * 16 * T * 1024) + 2 * r(4 * TK * L)
+
+
+@pytest.mark.parametrize("L", [7937, 8000, 15000])
+def test_noalloc_rejects_a_head_beyond_its_scratch(L):
+    """d > 128: one head's staging must fit ATTN_NOALLOC_SCRATCH_BYTES; the call is
+    refused before any HIP call."""
+    assert _two_pass_head_bytes(L) > _lib.ATTN_NOALLOC_SCRATCH_BYTES
     big = 4 * L * 1024 * 2
     assert fwd_noalloc(q=A, k=A + big, v=A + 2 * big, out=A + 3 * big, L=L, d=1024) == \
         _lib.ATTN_ERR_SCRATCH_TOO_SMALL
 
 
 def test_noalloc_largest_head_fits():
-    """L = 7943 is the longest head at d > 128 whose staging fits the array."""
-    r = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    T = (7943 + 255) // 256
-    assert r(2 * 7943 * (256 * T + 128)) + 2 * r(4 * T * 7943) <= _lib.ATTN_NOALLOC_SCRATCH_BYTES
+    """L = 7936 is the longest head at d > 128 whose staging fits the array."""
+    assert _two_pass_head_bytes(7936) <= _lib.ATTN_NOALLOC_SCRATCH_BYTES
 
 
 def test_noalloc_python_binding_needs_out():

@@ -103,7 +103,7 @@ def attention_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: to
     per-device array instead of allocating (attn_forward_noalloc).  Calls whose
     work may overlap on one GPU race on that array.  Raises AttnError with
     ATTN_ERR_SCRATCH_TOO_SMALL when one head needs more scratch than the array
-    holds (d > 128 with L above 7943)."""
+    holds (d > 128 with L above 7936)."""
     _check(q, "q")
     B, H, L, d = q.shape
     for t, name in ((k, "k"), (v, "v"), (out, "out")):

@@ -21,11 +21,14 @@
 //   * The S^T accumulator layout is, register for register, the B operand of
 //     O^T += V^T P^T once the 32 keys of a block are relabelled; so P goes from
 //     the softmax to the second MFMA without touching LDS.
-//   * K tiles go global -> LDS with direct buffer loads (XOR-swizzled 16-byte
-//     chunks, conflict-free fragment reads); V tiles are transposed in
-//     registers on the way into LDS so that V^T rows hold consecutive keys.
+//   * K and V tiles both go global -> LDS with direct buffer loads (XOR-swizzled
+//     16-byte chunks) and stay row-major; the V^T fragments of the second MFMA
+//     come from the gfx950 LDS transpose read (ds_read_b64_tr_b16), so no
+//     register passes through V on its way in.
 //   * K/V tiles are double-buffered: the next tile's loads are in flight while
 //     the current one is consumed.
+//   * Unmasked, the block maximum is a one-sided max3 chain on the raw scores
+//     (the maximum, or for a negative scale the minimum) scaled once.
 //   * Keys past L, and outside the query's band (after it when causal, or
 //     beyond a sliding window), are masked to -inf; a workgroup visits only
 //     the key blocks its queries' bands meet, a wave skips blocks its own
@@ -44,19 +47,15 @@
 namespace attn {
 namespace {
 
-constexpr int kQWaves = 4;            // query waves per group
-constexpr int kGroups = 2;            // groups taking alternate key blocks
-constexpr int kWaves = kQWaves * kGroups;
-constexpr int kBM = 32 * kQWaves;     // queries per workgroup
 constexpr int kBN = 64;           // keys per step
+constexpr int kBM = 128;          // queries per workgroup with 4 query waves per group
 constexpr float kLazy = 8.f;      // reference slack (log2 units) before O is rescaled
 
-template <int D>
+template <int D, int G>
 struct OnlineSmem {
-  static constexpr int KT_BYTES = 64 * D * 2;
-  static constexpr int VT_BYTES = D * (64 * 2 + 8);
-  char kbuf[kGroups][2][KT_BYTES];
-  char vbuf[kGroups][2][VT_BYTES];
+  static constexpr int TILE = kBN * D * 2;  // one 64-key K or V tile
+  char k[G][2][TILE];                      // per group, double-buffered
+  char v[G][2][TILE];
 };
 
 // LAYOUT: where head bh's rows are.  kPlain: q, k, v and out contiguous
@@ -76,34 +75,37 @@ enum { kPlain = 0, kStrided = 1, kVarlen = 2 };
 // of fmha.py's softmax, each key standing for cf consecutive queries.  Causal
 // has its own instantiation so that it carries no left-side tests.
 enum { kAllKeys = 0, kCausal = 1, kWindow = 2, kCompressed = 3 };
-template <int D, int MASK, int LAYOUT>
-__global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t* __restrict__ q,
-                                                          const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v,
-                                                          uint16_t* __restrict__ out,
-                                                          float* __restrict__ lse, HeadMap hm,
-                                                          int Lmax, int nqb, float sl2, Band band,
-                                                          VarSeqs vs, KeySplit ks) {
-  constexpr int CPR = D / 8;                       // 16-byte chunks per K row
-  constexpr int SWZ = (CPR >= 8 ? 8 : CPR) - 1;    // chunk-index bits that are swizzled
-  constexpr int VROW = kBN * 2 + 8;                // bytes per V^T row: 64 keys + pad
-  constexpr int K_LOADS = kBN * CPR / 256;         // direct loads per thread per K tile
-  constexpr int V_BLOCKS = 16 * CPR;               // 4-key x 8-channel blocks per V tile
+// QW: query waves per group (32 queries each); G: key-block groups, each
+// taking every G-th key block of the workgroup's band with its own tiles.
+template <int D, int MASK, int LAYOUT, int QW, int G>
+__global__ __launch_bounds__(64 * QW * G) void online_attn_kernel(const uint16_t* __restrict__ q,
+                                                    const uint16_t* __restrict__ k,
+                                                    const uint16_t* __restrict__ v,
+                                                    uint16_t* __restrict__ out,
+                                                    float* __restrict__ lse, HeadMap hm, int Lmax,
+                                                    int nqb, float sl2, Band band, VarSeqs vs,
+                                                    KeySplit ks) {
+  constexpr int BM = 32 * QW;                      // queries per workgroup
+  constexpr int GT = 64 * QW;                      // threads per group
+  constexpr int CPR = D / 8;                       // 16-byte chunks per K or V row
+  constexpr int SWZ = (CPR >= 8 ? 8 : CPR) - 1;    // chunk-index bits of K that are swizzled
+  constexpr int LOADS = kBN * CPR / GT;            // direct loads per thread per K (and V) tile
   constexpr int NS = D / 16;                       // k16 steps for S
   constexpr int NCB = D / 32;                      // 32-channel blocks of O
-  static_assert(K_LOADS >= 1 && V_BLOCKS <= 256, "tile shape");
+  constexpr int TILE = OnlineSmem<D, G>::TILE;
+  static_assert(LOADS >= 1 && LOADS * GT == kBN * CPR, "tile shape");
 
   // One LDS object (two would make the compiler wait on every direct load in
   // flight before each LDS read).
-  __shared__ OnlineSmem<D> smem;
+  __shared__ OnlineSmem<D, G> smem;
 
-  const int ltid = threadIdx.x & 255, lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63;
   // Wave-uniform, read from lane 0 so that the branches on them are scalar.
-  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);             // key-block group
-  const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);  // query wave in the group
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x / GT);              // key-block group
+  const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) % QW);  // query wave in the group
   const int c32 = lane & 31, h = lane >> 5;
-  auto& kbuf = smem.kbuf[g];
-  auto& vbuf = smem.vbuf[g];
+  char* const ktiles = &smem.k[g][0][0];
+  char* const vtiles = &smem.v[g][0][0];
 
   // Workgroup = (head, query block, key split); the splits of one block are
   // neighbours, so they run on one XCD and share its L2.
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
     const int qs = min(max(vs.cu_q[b], 0), vs.total_q);
     const int qe = min(max(vs.cu_q[b + 1], qs), vs.total_q);
     L = min(qe - qs, Lmax);
-    if (qb * kBM >= L) return;  // the whole workgroup, before any barrier
+    if (qb * BM >= L) return;  // the whole workgroup, before any barrier
     const int* cuk = vs.cu_k != nullptr ? vs.cu_k : vs.cu_q;
     const int tk = vs.cu_k != nullptr ? vs.total_k : vs.total_q;
     const int ks0 = min(max(cuk[b], 0), tk);
@@ -164,10 +166,10 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   // Rows past the end of each head read as zero: the resources end after its
   // last row (and are empty for a sequence without keys).
   const auto rq = make_rsrc(q + qoff, ((uint32_t)(L - 1) * ldq + D) * 2);
-  const auto rk = make_rsrc(k + koff, Lk > 0 ? ((uint32_t)(Lk - 1) * ldk + D) * 2 : 0u);
-  const auto rv = make_rsrc(v + voff, Lk > 0 ? ((uint32_t)(Lk - 1) * ldv + D) * 2 : 0u);
+  const u32x4 rk = rsrc_words(k + koff, Lk > 0 ? ((uint32_t)(Lk - 1) * ldk + D) * 2 : 0u);
+  const u32x4 rv = rsrc_words(v + voff, Lk > 0 ? ((uint32_t)(Lk - 1) * ldv + D) * 2 : 0u);
 
-  const int q0 = qb * kBM + wave * 32;  // first query of this wave
+  const int q0 = qb * BM + wave * 32;  // first query of this wave
   const int myq = q0 + c32;             // this lane's query
   // The last key query i may see (kNoLimit-sized when unbounded).
   auto last_key = [&](int i) { return MASK == kCompressed ? (i + 1) / cf - 1 : i + right; };
@@ -180,8 +182,8 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
     qf[s] = __builtin_bit_cast(bf16x8, load16(rq, (uint32_t)(myq * ldq + 16 * s + 8 * h) * 2));
 
   // Key blocks t0 .. t0 + ntiles - 1 meet the band of this workgroup's queries.
-  const int kstart = HAS_LEFT ? max(0, qb * kBM - left) : 0;
-  const int kend = BANDED ? min(Lk, last_key(qb * kBM + kBM - 1) + 1) : Lk;
+  const int kstart = HAS_LEFT ? max(0, qb * BM - left) : 0;
+  const int kend = BANDED ? min(Lk, last_key(qb * BM + BM - 1) + 1) : Lk;
   int t0 = kstart / kBN;
   int ntiles = max(0, (kend + kBN - 1) / kBN - t0);
   if (ks.n > 1) {  // this split's share of those blocks (possibly none)
@@ -190,38 +192,62 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
     ntiles = b - a;
   }
 
-  auto issue_k = [&](int t, int buf) {
+  // Both tiles are [64 keys][D channels] rows of 16-byte chunks, filled by
+  // direct loads (one 1 KB run of 64 chunks per load and wave), issued
+  // untracked: the wait for them is the explicit one before each barrier.  K chunk c of
+  // row r sits at c ^ (r & SWZ), so that the K fragment reads (16 bytes of one
+  // row per lane) are conflict-free; V chunk c at c ^ vswz(r), so that the four
+  // rows one transpose read gathers fall in distinct banks.
+  auto vswz = [](int r) { return CPR >= 8 ? 2 * (r & 3) : 2 * ((r >> 1) & 1); };
+  auto issue = [&](int t, int slot) {
 #pragma unroll
-    for (int j = 0; j < K_LOADS; ++j) {
-      const int P = (j * kQWaves + wave) * 64 + lane;
-      const int row = P / CPR, pc = P % CPR;
-      const int lc = pc ^ (row & SWZ);
-      const uint32_t voff = (uint32_t)((t * kBN + row) * ldk + lc * 8) * 2;
-      load16_to_lds(rk, &kbuf[buf][(j * kQWaves + wave) * 64 * 16], voff);
+    for (int j = 0; j < LOADS; ++j) {
+      const int P = (j * QW + wave) * 64 + lane;
+      const int row = P / CPR, lc = P % CPR;
+      const uint32_t key = (uint32_t)(t * kBN + row);
+      load16_to_lds_untracked(rk, ktiles + slot * TILE + (j * QW + wave) * 1024,
+                              (key * ldk + (uint32_t)(lc ^ (row & SWZ)) * 8) * 2);
+      load16_to_lds_untracked(rv, vtiles + slot * TILE + (j * QW + wave) * 1024,
+                              (key * ldv + (uint32_t)(lc ^ vswz(row)) * 8) * 2);
     }
   };
-  // Thread ltid of a group owns V block (vg = ltid % 16 -> keys 4vg..4vg+3,
-  // vc8 = ltid / 16 -> channels 8vc8..+7).
-  const bool vblk = ltid < V_BLOCKS;
-  const int vg = ltid & 15, vc8 = ltid >> 4;
-  auto load_v = [&](int t, u32x4 (&vr)[4]) {
-    if (vblk) {
+
+  // S^T block of 64 keys x 32 queries (two 32-key halves) from a K tile.  Every
+  // K fragment read is issued before the first MFMA, so that the MFMAs do not
+  // each wait out one read's latency.
+  auto compute_s = [&](const char* kt, f32x16 (&s)[2]) {
+    bf16x8 ka[NS][2];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        vr[kk] = load16(rv, (uint32_t)((t * kBN + 4 * vg + kk) * ldv + 8 * vc8) * 2);
-    }
-  };
-  auto store_vt = [&](int buf, const u32x4 (&vr)[4]) {
-    if (vblk) {
+    for (int ss = 0; ss < NS; ++ss)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const unsigned a0 = vr[0][w], a1 = vr[1][w], a2 = vr[2][w], a3 = vr[3][w];
-        u32x2 lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-        u32x2 hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-        *(u32x2*)&vbuf[buf][(8 * vc8 + 2 * w) * VROW + 8 * vg] = lo;
-        *(u32x2*)&vbuf[buf][(8 * vc8 + 2 * w + 1) * VROW + 8 * vg] = hi;
+      for (int kb = 0; kb < 2; ++kb) {
+        const int row = kb * 32 + c32;
+        const int pc = (2 * ss + h) ^ (row & SWZ);
+        ka[ss][kb] = *(const bf16x8*)&kt[(row * CPR + pc) * 16];
       }
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int ss = 0; ss < NS; ++ss)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(ka[ss][kb], qf[ss], s[kb]);
+  };
+
+  // V^T fragment of MFMA (c, kb, u) for O^T += V^T P^T: lane half h of channel
+  // 32c + c32 takes keys kb*32 + 16u + {4h..4h+3, 8+4h..8+4h+3}, the order in
+  // which the S^T registers hold them.  Two gfx950 transpose reads: in each
+  // 16-lane group, lane L addresses the 4 channels 4(L % 4).. of key row
+  // r0 + L / 4, and lane i receives the 4 keys r0.. of the group's channel i.
+  auto vfrag = [&](const char* vt, int c, int kb, int u) {
+    const int g16 = lane >> 4, L4 = lane & 15;
+    const int m = c * 32 + 16 * (g16 & 1) + 4 * (L4 & 3);
+    const int r0 = kb * 32 + 16 * u + 4 * (g16 >> 1) + (L4 >> 2);
+    const int off = r0 * (D * 2) + ((((m >> 3) ^ vswz(r0)) << 4) | ((m & 7) * 2));
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((short4_lds*)(vt + off));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((short4_lds*)(vt + off + 8 * D * 2));
+    const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, w);
   };
 
   f32x16 o[NCB];
@@ -229,182 +255,177 @@ __global__ __launch_bounds__(64 * kWaves) void online_attn_kernel(const uint16_t
   for (int c = 0; c < NCB; ++c) o[c] = f32x16{};
   float m = -INFINITY, lsum = 0.f;
 
-  // Group g takes key blocks t = t0 + g + kGroups * it.  Both groups run the
-  // same number of iterations (so that every wave meets every barrier); a
-  // block past the end is skipped.
-  const int niter = (ntiles + kGroups - 1) / kGroups;
-  const int tend = t0 + ntiles;
-  u32x4 vr[4];
-  if (g < ntiles) {
-    issue_k(t0 + g, 0);
-    load_v(t0 + g, vr);
-    wait_vmem();
-    store_vt(0, vr);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < niter; ++it) {
-    const int t = t0 + g + kGroups * it;
-    const int buf = it & 1;
-    const bool has_next = t + kGroups < tend;
-    if (has_next) {
-      issue_k(t + kGroups, buf ^ 1);
-      load_v(t + kGroups, vr);
-    }
+  // Softmax update of key block t from its S^T, then O^T += V^T P^T.
+  auto softmax_pv = [&](int t, f32x16 (&s)[2], const char* vt) {
     const int kbase = t * kBN;
-    // This wave's 32 queries see some key of the block.
-    const bool active = t < tend && (!BANDED || kbase <= last_key(q0 + 31)) &&
-                        (!HAS_LEFT || kbase + kBN - 1 >= q0 - left);
-    if (active) {
-      // S^T block: 64 keys x 32 queries, two 32-key halves.  Every K fragment
-      // read is issued before the first MFMA, so that the MFMAs do not each wait
-      // out one read's latency (measured: about -1% per call).
-      bf16x8 ka[NS][2];
+    // At D = 128 the V^T fragments are all read here, before the softmax (they
+    // do not depend on P), so that they have arrived when the MFMAs issue.
+    constexpr bool V_EARLY = D >= 128;
+    bf16x8 vf[V_EARLY ? NCB : 1][2][2];
+    if constexpr (V_EARLY) {
 #pragma unroll
-      for (int ss = 0; ss < NS; ++ss)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int row = kb * 32 + c32;
-          const int pc = (2 * ss + h) ^ (row & SWZ);
-          ka[ss][kb] = *(const bf16x8*)&kbuf[buf][(row * CPR + pc) * 16];
-        }
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int ss = 0; ss < NS; ++ss)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(ka[ss][kb], qf[ss], s[kb]);
-      // V^T fragment of MFMA (c, kb, u) for O^T += V^T P^T: keys
-      // kb*32 + 16u + {4h..4h+3, 8+4h..8+4h+3} in lane half h of channel c*32 + c32.
-      // At D = 128 they are all read here, before the softmax (they do not depend
-      // on P), so that they have arrived when the MFMAs issue (measured: -2% per
-      // call at D = 128, +2% at D = 64, where they are read next to each MFMA).
-      auto vfrag = [&](int c, int kb, int u) {
-        const char* base = &vbuf[buf][(c * 32 + c32) * VROW + (kb * 32 + 16 * u + 4 * h) * 2];
-        const u32x2 lo = *(const u32x2*)base;
-        const u32x2 hi = *(const u32x2*)(base + 16);
-        return u32x4{lo[0], lo[1], hi[0], hi[1]};
-      };
-      constexpr bool V_EARLY = D >= 128;
-      u32x4 vf[V_EARLY ? NCB : 1][2][2];
-      if constexpr (V_EARLY) {
-#pragma unroll
-        for (int c = 0; c < NCB; ++c)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) vf[c][kb][u] = vfrag(c, kb, u);
-      }
-      // Softmax update for this lane's query over its 32 of the 64 keys.  The
-      // maximum is taken on the raw scores (scaled afterwards; the sign of sl2
-      // picks max or min), and y - m is one FMA: p = 2^(s * sl2 - m).
-      const bool need_mask = (kbase + kBN > Lk) || (BANDED && kbase + kBN - 1 > last_key(q0)) ||
-                             (HAS_LEFT && kbase < q0 + 31 - left);
-      float tmax;
-      if (need_mask) {
-        tmax = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = kbase + kb * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
-            const bool off = key >= Lk || (BANDED && key > my_last) ||
-                             (HAS_LEFT && key < myq - left);
-            s[kb][j] = off ? -INFINITY : s[kb][j] * sl2;
-            tmax = fmaxf(tmax, s[kb][j]);
-          }
-        }
-      } else {
-        float hi = s[0][0], lo = s[0][0];
+      for (int c = 0; c < NCB; ++c)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            hi = fmaxf(hi, s[kb][j]);
-            lo = fminf(lo, s[kb][j]);
-          }
-        tmax = sl2 >= 0.f ? hi * sl2 : lo * sl2;
-      }
-      tmax = wave_swap32_max(tmax);
-      // Lazy reference: m moves only when this block's maximum exceeds it by more
-      // than kLazy (log2 units), so most blocks skip the rescale of O.  P and l
-      // always use the same reference, so the result is unchanged; p <= 2^kLazy.
-      const bool grow = tmax > m + kLazy;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float mnew = grow ? tmax : m;
-        const float alpha = m == -INFINITY ? 0.f : exp2_fast(m - mnew);
-        m = mnew;
-        lsum *= alpha;
-#pragma unroll
-        for (int c = 0; c < NCB; ++c)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) o[c][j] *= alpha;
-      }
-      const float muse = m == -INFINITY ? 0.f : m;
-      const float mul = need_mask ? 1.f : sl2;
-      unsigned pk[2][8];
+          for (int u = 0; u < 2; ++u) vf[c][kb][u] = vfrag(vt, c, kb, u);
+    }
+    // This lane's query over its 32 of the 64 keys.  Unmasked, the maximum is
+    // taken on the raw scores and scaled afterwards (the maximum when sl2 >= 0,
+    // else the minimum), and y - m is one FMA: p = 2^(s * sl2 - m).
+    const bool need_mask = (kbase + kBN > Lk) || (BANDED && kbase + kBN - 1 > last_key(q0)) ||
+                           (HAS_LEFT && kbase < q0 + 31 - left);
+    float tmax;
+    if (need_mask) {
+      tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-          const float p0 = exp2_fast(fmaf(s[kb][j], mul, -muse));
-          const float p1 = exp2_fast(fmaf(s[kb][j + 1], mul, -muse));
-          pk[kb][j >> 1] = pack_bf16x2(p0, p1);
-          lsum = add_bf16x2(pk[kb][j >> 1], lsum);  // sum of the rounded P actually used
+        for (int j = 0; j < 16; ++j) {
+          const int key = kbase + kb * 32 + 8 * (j >> 2) + 4 * h + (j & 3);
+          const bool off = key >= Lk || (BANDED && key > my_last) || (HAS_LEFT && key < myq - left);
+          s[kb][j] = off ? -INFINITY : s[kb][j] * sl2;
+          tmax = fmaxf(tmax, s[kb][j]);
         }
       }
-      // O^T += V^T P^T: the P of MFMA (kb, u) is exactly the S^T registers
-      // 8u..8u+7 of block kb.
+    } else if (sl2 >= 0.f) {
+      float hi = s[0][0];
 #pragma unroll
-      for (int c = 0; c < NCB; ++c) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int j = 0; j < 16; ++j) hi = fmaxf(hi, s[kb][j]);
+      tmax = hi * sl2;
+    } else {
+      float lo = s[0][0];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const u32x4 bv = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
-            const u32x4 av = V_EARLY ? vf[V_EARLY ? c : 0][kb][u] : vfrag(c, kb, u);
-            o[c] = mfma32x32x16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), o[c]);
-          }
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) lo = fminf(lo, s[kb][j]);
+      tmax = lo * sl2;
+    }
+    tmax = wave_swap32_max(tmax);
+    // Lazy reference: m moves only when this block's maximum exceeds it by more
+    // than kLazy (log2 units), so most blocks skip the rescale of O.  P and l
+    // always use the same reference, so the result is unchanged; p <= 2^kLazy.
+    const bool grow = tmax > m + kLazy;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mnew = grow ? tmax : m;
+      const float alpha = m == -INFINITY ? 0.f : exp2_fast(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[c][j] *= alpha;
+    }
+    const float muse = m == -INFINITY ? 0.f : m;
+    const float mul = need_mask ? 1.f : sl2;
+    unsigned pk[2][8];
+    float ps[2] = {0.f, 0.f};  // two partial sums of the rounded P, to shorten the chain
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        const float p0 = exp2_fast(fmaf(s[kb][j], mul, -muse));
+        const float p1 = exp2_fast(fmaf(s[kb][j + 1], mul, -muse));
+        pk[kb][j >> 1] = pack_bf16x2(p0, p1);
+        ps[kb] = add_bf16x2(pk[kb][j >> 1], ps[kb]);  // sum of the rounded P actually used
+      }
+    }
+    lsum += ps[0] + ps[1];
+    // The P of MFMA (kb, u) is exactly the S^T registers 8u..8u+7 of block kb.
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4 bv = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
+          const bf16x8 av = V_EARLY ? vf[V_EARLY ? c : 0][kb][u] : vfrag(vt, c, kb, u);
+          o[c] = mfma32x32x16(av, __builtin_bit_cast(bf16x8, bv), o[c]);
         }
       }
     }
-    if (has_next) {
-      wait_vmem();
-      store_vt(buf ^ 1, vr);
+  };
+
+  // Group g takes key blocks t = t0 + g + G * it, double-buffered: the loads
+  // of its next block are in flight while it works on this one.  All groups
+  // run the same number of iterations (so that every wave meets every
+  // barrier); a block past the end, or one this wave's queries do not see, is
+  // skipped.
+  const int niter = (ntiles + G - 1) / G;
+  const int tend = t0 + ntiles;
+  auto active = [&](int t) {
+    const int kbase = t * kBN;
+    return t < tend && (!BANDED || kbase <= last_key(q0 + 31)) &&
+           (!HAS_LEFT || kbase + kBN - 1 >= q0 - left);
+  };
+  if (g < ntiles) issue(t0 + g, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int it = 0; it < niter; ++it) {
+    const int t = t0 + g + G * it;
+    const int slot = it & 1;
+    if (t + G < tend) issue(t + G, slot ^ 1);
+    if (active(t)) {
+      f32x16 s[2];
+      compute_s(ktiles + slot * TILE, s);
+      softmax_pv(t, s, vtiles + slot * TILE);
     }
+    wait_vmem();
     __syncthreads();
   }
 
-  // Merge the two groups' partial results.  Group 1 leaves m, l and O (fp32) in
-  // the K/V tiles, which no wave reads any more; group 0 combines.  Lane holds
-  // channels 32c + 8i + 4h + r (r = 0..3) of query myq in o[c][4i + r].
+  // Merge the groups' partial results.  Groups 1 .. G-1 leave O (fp32), m
+  // and l in the tiles, which no wave reads any more; group 0 combines them
+  // exactly: O = sum_g 2^(m_g - M) O_g / sum_g 2^(m_g - M) l_g, M = max_g m_g.
+  // Lane holds channels 32c + 8i + 4h + r (r = 0..3) of query myq in o[c][4i + r].
   lsum = wave_swap32_sum(lsum);
-  float* xo = (float*)&smem;                      // [4 waves][NCB][16][64 lanes]
-  float* xm = xo + kQWaves * NCB * 16 * 64;       // [4 waves][64 lanes]
-  float* xl = xm + kQWaves * 64;
-  static_assert(sizeof(OnlineSmem<D>) >= (kQWaves * NCB * 16 * 64 + 2 * kQWaves * 64) * 4,
+  constexpr int XO = QW * NCB * 16 * 64;          // floats of O per group
+  float* xo = (float*)&smem;                       // [G-1][QW waves][NCB][16][64 lanes]
+  float* xm = xo + (G - 1) * XO;                   // [G-1][QW waves][64 lanes]
+  float* xl = xm + (G - 1) * QW * 64;
+  static_assert(((G - 1) * XO + 2 * (G - 1) * QW * 64) * 4 <= (int)sizeof(OnlineSmem<D, G>),
                 "exchange fits in the tiles");
-  if (g == 1) {
+  if (g > 0) {
+    float* po = xo + (g - 1) * XO;
 #pragma unroll
     for (int c = 0; c < NCB; ++c)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) xo[((wave * NCB + c) * 16 + j) * 64 + lane] = o[c][j];
-    xm[wave * 64 + lane] = m;
-    xl[wave * 64 + lane] = lsum;
+      for (int j = 0; j < 16; ++j) po[((wave * NCB + c) * 16 + j) * 64 + lane] = o[c][j];
+    xm[((g - 1) * QW + wave) * 64 + lane] = m;
+    xl[((g - 1) * QW + wave) * 64 + lane] = lsum;
   }
   __syncthreads();
-  if (g == 1) return;
+  if (g > 0) return;
   {
-    const float m1 = xm[wave * 64 + lane], l1 = xl[wave * 64 + lane];
-    const float M = fmaxf(m, m1);
-    const float a0 = m == -INFINITY ? 0.f : exp2_fast(m - M);
-    const float a1 = m1 == -INFINITY ? 0.f : exp2_fast(m1 - M);
-    lsum = a0 * lsum + a1 * l1;
+    float mg[G], lg[G];
+    mg[0] = m;
+    lg[0] = lsum;
+    float M = m;
+#pragma unroll
+    for (int gi = 1; gi < G; ++gi) {
+      mg[gi] = xm[((gi - 1) * QW + wave) * 64 + lane];
+      lg[gi] = xl[((gi - 1) * QW + wave) * 64 + lane];
+      M = fmaxf(M, mg[gi]);
+    }
+    float a[G];
+    lsum = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      a[gi] = mg[gi] == -INFINITY ? 0.f : exp2_fast(mg[gi] - M);
+      lsum += a[gi] * lg[gi];
+    }
 #pragma unroll
     for (int c = 0; c < NCB; ++c)
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        o[c][j] = a0 * o[c][j] + a1 * xo[((wave * NCB + c) * 16 + j) * 64 + lane];
+      for (int j = 0; j < 16; ++j) {
+        float acc = a[0] * o[c][j];
+#pragma unroll
+        for (int gi = 1; gi < G; ++gi)
+          acc += a[gi] * xo[(gi - 1) * XO + ((wave * NCB + c) * 16 + j) * 64 + lane];
+        o[c][j] = acc;
+      }
     m = M;
   }
   if (ks.n > 1) {
@@ -489,18 +510,28 @@ __global__ __launch_bounds__(256) void online_combine_kernel(KeySplit ks, uint16
   if (lse != nullptr && chunk == 0) lse[lrow] = (M + log2f(den)) * 0.6931471805599453f;
 }
 
-template <int D, int MASK, int LAYOUT>
+template <int D, int MASK, int LAYOUT, int QW, int G>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* out, float* lse,
                       HeadMap hm, int BH, int L, float sl2, Band band, VarSeqs vs,
                       KeySplit ks, hipStream_t s) {
-  const int nqb = (L + kBM - 1) / kBM;
-  const dim3 grid((unsigned)(nqb * BH * (ks.n > 1 ? ks.n : 1))), block(64 * kWaves);
+  const int nqb = (L + 32 * QW - 1) / (32 * QW);
+  const dim3 grid((unsigned)(nqb * BH * (ks.n > 1 ? ks.n : 1))), block(64 * QW * G);
   const uint16_t* qp = (const uint16_t*)q;
   const uint16_t* kp = (const uint16_t*)k;
   const uint16_t* vp = (const uint16_t*)v;
   uint16_t* op = (uint16_t*)out;
   void* args[] = {&qp, &kp, &vp, &op, &lse, &hm, &L, (void*)&nqb, &sl2, &band, &vs, &ks};
-  return hipLaunchKernel((const void*)&online_attn_kernel<D, MASK, LAYOUT>, grid, block, args, 0, s);
+  return hipLaunchKernel((const void*)&online_attn_kernel<D, MASK, LAYOUT, QW, G>, grid, block,
+                         args, 0, s);
+}
+
+// Four query waves by two key-block groups: 8 waves, 128 queries.  (Four
+// groups, and 64-query workgroups for causal masks, measured no faster.)
+template <int D, int MASK, int LAYOUT>
+hipError_t launch_l(const void* q, const void* k, const void* v, void* out, float* lse,
+                    HeadMap hm, int BH, int L, float sl2, Band band, VarSeqs vs,
+                    KeySplit ks, hipStream_t s) {
+  return launch_one<D, MASK, LAYOUT, 4, 2>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
 }
 
 template <int D, int MASK>
@@ -508,13 +539,13 @@ hipError_t launch_m(const void* q, const void* k, const void* v, void* out, floa
                     const HeadMap& hm, int BH, int L, float sl2, Band band,
                     const VarSeqs& vs, KeySplit ks, hipStream_t s) {
   if (vs.cu_q != nullptr)
-    return launch_one<D, MASK, kVarlen>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
+    return launch_l<D, MASK, kVarlen>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
   if constexpr (MASK == kCompressed) {
     return hipErrorInvalidValue;  // token-packed sequences only
   } else {
     if (is_plain(hm, L, D))
-      return launch_one<D, MASK, kPlain>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
-    return launch_one<D, MASK, kStrided>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
+      return launch_l<D, MASK, kPlain>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
+    return launch_l<D, MASK, kStrided>(q, k, v, out, lse, hm, BH, L, sl2, band, vs, ks, s);
   }
 }
 

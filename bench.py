@@ -134,23 +134,48 @@ def time_calls(call, stream, steps: int):
     return region, med, per[0]
 
 
-def other_run(name: str, steps: int, warmup: int, dev):
-    """One of the other workloads: warm up, time, kernel averages, oracle parity."""
+def abi_call(w, qd, kd, vd, out):
+    """A closure that calls attn_forward through the C ABI with its arguments
+    marshalled once, on the current stream: the per-call host cost is then the
+    library's own, not the Python binding's checks."""
+    import ctypes
+
     import torch
 
-    from exact_softmax_attention_bf16_amd import attention, kernel_timing
+    from exact_softmax_attention_bf16_amd._lib import AttnError, load
+    f = load().attn_forward
+    stream = ctypes.c_void_p(torch.cuda.current_stream(qd.device).cuda_stream)
+    args = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(), w.B, w.H, w.L, w.d,
+            ctypes.c_float(w.scale), int(w.causal), stream)
+
+    def call():
+        st = f(*args)
+        if st != 0:
+            raise AttnError(st)
+    return call
+
+
+def other_run(name: str, steps: int, warmup: int, dev):
+    """One of the other workloads: warm up, time (per-kernel timing off), then
+    the per-kernel averages over as many more calls, and oracle parity."""
+    import torch
+
+    from exact_softmax_attention_bf16_amd import kernel_timing
     from synth import WORKLOADS, make_qkv
     w = WORKLOADS[name]
     q, k, v = make_qkv(w.B, w.H, w.L, w.d, w.seed)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     out = torch.empty_like(qd)
-    call = lambda: attention(qd, kd, vd, scale=w.scale, causal=w.causal, out=out)  # noqa: E731
+    call = abi_call(w, qd, kd, vd, out)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
+    region, med, mn = time_calls(call, torch.cuda.current_stream(), steps)
     kt = {}
     with kernel_timing(kt):
-        region, med, mn = time_calls(call, torch.cuda.current_stream(), steps)
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
     flops = w.flops()
     rec = {"B": w.B, "H": w.H, "L": w.L, "d": w.d, "causal": w.causal, "flop": flops,
            "steps": steps, "ms_per_call": round(region, 5),
@@ -161,6 +186,66 @@ def other_run(name: str, steps: int, warmup: int, dev):
     rec.update(oracle_check(w, q, k, v, out))
     log(f"[bench] {name}: {rec}")
     return rec
+
+
+def split_columns_probe(args) -> int:
+    """The large-d alternative that splits the output columns across waves
+    (include/attn_probe.h), timed next to attn_forward on the same workload with
+    events on the same stream; its output is checked against the oracle on every
+    head.  The probe's L2->CU stream: per workgroup (64 rows) and 32-key block,
+    64 KB of K, 64 KB of V and 128 KB of Q."""
+    import ctypes
+
+    import torch
+
+    from synth import WORKLOADS, make_qkv
+
+    w = WORKLOADS[args.workload]
+    if w.causal or w.d != 1024:
+        log("[probe] the split-columns probe is written for d = 1024 without a mask")
+        return 2
+    path = os.path.join(ROOT, "exact_softmax_attention_bf16_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"probe library not built: {path}")
+    probe = ctypes.CDLL(path).attn_probe_split_columns
+    probe.restype = ctypes.c_int
+    probe.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 4 + [ctypes.c_float, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    q, k, v = make_qkv(w.B, w.H, w.L, w.d, w.seed)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out_a, out_p = torch.empty_like(qd), torch.empty_like(qd)
+    two_pass = abi_call(w, qd, kd, vd, out_a)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def split_cols():
+        st = probe(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out_p.data_ptr(), w.B, w.H, w.L,
+                   w.d, ctypes.c_float(w.scale), sp)
+        if st != 0:
+            raise RuntimeError(f"attn_probe_split_columns: status {st}")
+
+    steps = max(args.steps // 5, 3)
+    for _ in range(args.warmup):
+        two_pass()
+        split_cols()
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn in (("two_pass", two_pass), ("split_columns", split_cols)):
+        region, med, mn = time_calls(fn, stream, steps)
+        res[name] = {"ms_per_call": round(region, 4), "ms_median": round(med, 4),
+                     "tflops": round(w.flops() / (region * 1e-3) / 1e12, 1),
+                     "pct_bf16_mfma_peak": round(100.0 * w.flops() / (region * 1e-3) / 1e12 /
+                                                 PEAK_BF16_TFLOPS, 2)}
+    wgs = w.B * w.H * ((w.L + 63) // 64)
+    stream_bytes = wgs * ((w.L + 31) // 32) * (64 + 64 + 128) * 1024
+    res["split_columns"]["l2_to_cu_gb_per_call"] = round(stream_bytes / 1e9, 2)
+    res["split_columns"]["l2_to_cu_tb_per_s"] = round(
+        stream_bytes / (res["split_columns"]["ms_per_call"] * 1e-3) / 1e12, 2)
+    res["split_columns"]["vs_oracle"] = oracle_check(w, q, k, v, out_p)
+    rec = {"probe": "split_columns", "workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d,
+           "steps": steps, **res}
+    print(json.dumps(rec), flush=True)
+    return 0
 
 
 def design_probe(args) -> int:
@@ -237,6 +322,10 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 256 MiB device-to-device three times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against a known byte count)")
+    ap.add_argument("--split-columns-probe", action="store_true",
+                    help="time the one-kernel large-d alternative that splits the output columns "
+                         "across waves (libattn_probe.so) next to attn_forward, check it against "
+                         "the oracle, and print one JSON line")
     ap.add_argument("--design-probe", action="store_true",
                     help="time the materialised-S alternative for large d from library pieces "
                          "(hipBLASLt bmm for Q K^T and P V, torch softmax between them) next to "
@@ -245,6 +334,8 @@ def main() -> int:
 
     if args.design_probe:
         return design_probe(args)
+    if args.split_columns_probe:
+        return split_columns_probe(args)
 
     if args.copy_probe:
         import torch
@@ -266,7 +357,7 @@ def main() -> int:
 
     import torch
 
-    from exact_softmax_attention_bf16_amd import attention, kernel_timing
+    from exact_softmax_attention_bf16_amd import kernel_timing
     from synth import WORKLOADS, make_qkv
 
     w = WORKLOADS[args.workload]
@@ -275,9 +366,10 @@ def main() -> int:
     q, k, v = make_qkv(w.B, w.H, w.L, w.d, w.seed)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     out = torch.empty_like(qd)
+    call = abi_call(w, qd, kd, vd, out)
 
     for _ in range(args.warmup):
-        attention(qd, kd, vd, scale=w.scale, causal=w.causal, out=out)
+        call()
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done")
 
@@ -286,7 +378,7 @@ def main() -> int:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            attention(qd, kd, vd, scale=w.scale, causal=w.causal, out=out)
+            call()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
@@ -303,7 +395,7 @@ def main() -> int:
           for _ in range(args.steps)]
     for a, b in ev:
         a.record(stream)
-        attention(qd, kd, vd, scale=w.scale, causal=w.causal, out=out)
+        call()
         b.record(stream)
     torch.cuda.synchronize()
     per_call = sorted(a.elapsed_time(b) for a, b in ev)

@@ -19,6 +19,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["attn_api.cpp", "online_attn.hip", "two_pass_attn.hip"]
+# Design probes (include/attn_probe.h): a library of their own, not loaded by
+# the attention path.
+PROBE_SOURCES = ["probe/split_columns.hip"]
+PROBE_LIB_PATH = os.path.join(HERE, "libattn_probe.so")
 ARCH = "gfx950"
 
 
@@ -48,7 +52,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(obj_dir, exist_ok=True)
 
     def compile_one(src: str) -> str:
-        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0].replace("/", "_") + ".o")
         lang = ["-x", "hip"]
         cmd = [cc, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
@@ -62,14 +66,15 @@ def build(verbose: bool = False) -> str:
             print(msgs, flush=True)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    for path, group in ((LIB_PATH, objs[:len(SOURCES)]), (PROBE_LIB_PATH, objs[len(SOURCES):])):
+        tmp = path + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *group]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+        os.replace(tmp, path)
     return LIB_PATH
 
 

@@ -496,3 +496,22 @@ def test_noalloc_python_binding_needs_out():
         eab.attention_noalloc(torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16),
                               torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16),
                               torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16))
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "attn_probe.h")
+PROBE_LIB = os.path.join(ROOT, "exact_softmax_attention_bf16_amd", "libattn_probe.so")
+
+
+def test_probe_library_exports_its_header_and_checks_arguments():
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = set(re.findall(r"^\s*int\s+(attn_probe_[a-z_0-9]+)\s*\(", text, flags=re.M))
+    assert names == {"attn_probe_split_columns"}
+    out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True, text=True)
+    assert names <= set(re.findall(r"\sT\s(attn_probe_\w+)", out.stdout))
+    f = ctypes.CDLL(PROBE_LIB).attn_probe_split_columns
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64] * 4 + [ctypes.c_float, ctypes.c_void_p]
+    assert f(None, A, A, A, 1, 1, 64, 1024, 0.03125, None) == 1
+    assert f(A, A + 64 * MB, A + 128 * MB, A + 192 * MB, 1, 1, 64, 512, 0.03125, None) == 2
+    assert f(A, A + 64 * MB, A + 128 * MB, A + 192 * MB, 1, 1, 0, 1024, 0.03125, None) == 2
+    assert f(A, A + 64 * MB, A + 128 * MB, A + 192 * MB, 1, 1, 1 << 20, 1024, 0.03125, None) == 2

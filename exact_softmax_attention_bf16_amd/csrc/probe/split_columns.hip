@@ -88,13 +88,12 @@ __global__ __launch_bounds__(64 * kWaves) void split_columns_kernel(
                               (uint32_t)((key0 + row) * kD + c0 + (lc ^ vswz(row)) * 8) * 2);
     }
     // 1. Partial S^T over this wave's channels.  Step s, lane half h takes
-    // channels c0 + 64 h + 8 s .. + 8 for both K and Q (the order in which
-    // the 1024 products are summed does not matter), so that a lane's loads
-    // of one row are 128 contiguous bytes.
+    // channels c0 + 16 s + 8 h .. + 8 for both K and Q: the two lane halves of
+    // one row read 32 contiguous bytes in each load.
     f32x16 st[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const uint32_t ch = (uint32_t)(c0 + 64 * h + 8 * s);
+      const uint32_t ch = (uint32_t)(c0 + 16 * s + 8 * h);
       const bf16x8 kf = __builtin_bit_cast(bf16x8, load16(rk, ((uint32_t)(key0 + n) * kD + ch) * 2));
 #pragma unroll
       for (int a = 0; a < 2; ++a) {

@@ -67,7 +67,12 @@ bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
 struct HipBackend {
   using Stream = hipStream_t;
   using Event = hipEvent_t;
-  int create_event(hipEvent_t* e) { return hipEventCreateWithFlags(e, hipEventDisableTiming); }
+  // Only this device's streams wait on the event (hipStreamWaitEvent), so a
+  // device-scope release is enough; the default system-scope fence would write
+  // back and invalidate L2 at the end of every call.
+  int create_event(hipEvent_t* e) {
+    return hipEventCreateWithFlags(e, hipEventDisableTiming | hipEventReleaseToDevice);
+  }
   int record(hipEvent_t e, hipStream_t s) { return hipEventRecord(e, s); }
   int stream_wait(hipStream_t s, hipEvent_t e) { return hipStreamWaitEvent(s, e, 0); }
   int malloc_async(void** p, size_t n, hipStream_t s) { return hipMallocAsync(p, n, s); }
@@ -177,7 +182,9 @@ hipError_t take_event(hipEvent_t* ev) {
       return hipSuccess;
     }
   }
-  return hipEventCreate(ev);
+  // Timestamps only, read after the caller synchronises: no system-scope
+  // fence, which would write back and invalidate L2 between the kernels timed.
+  return hipEventCreateWithFlags(ev, hipEventDisableSystemFence);
 }
 
 void give_event(hipEvent_t ev) {

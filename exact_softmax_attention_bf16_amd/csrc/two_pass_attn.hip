@@ -7,10 +7,11 @@
 // file next to a useful query block, so the path stays two-pass like the
 // pages', but moves the softmax into the two GEMMs:
 //
-//   scores pass  for each 256-key x 256-query tile t of S^T = K Q^T (fp32):
-//                y = scale*log2(e) * s; per query m_t = ceil(max_keys y) (an
-//                integer); E = bf16(2^(y - m_t)); store E, m_t and
-//                psum_t = sum of the stored E over the tile's keys.
+//   scores pass  for each 256-key x 256-query tile of S^T = K Q^T (fp32):
+//                y = scale*log2(e) * s; per query and 128-key half t of the
+//                tile m_t = ceil(max over those keys of y) (an integer);
+//                E = bf16(2^(y - m_t)); store E, m_t and psum_t = sum of the
+//                stored E over those keys.
 //   values pass  per query M = max_t m_t, l = sum_t 2^(m_t - M) psum_t, and
 //                O = (sum_t 2^(m_t - M) E_t V_t) / l, with the factor applied
 //                to E exactly: m_t - M is an integer, so scaling bf16 E by it

@@ -114,17 +114,24 @@ __device__ __forceinline__ int scores_query_base(int wave) {
   return ((wave ^ (wave >> 2)) & 1) * 128 + ((wave >> 1) & 1) * 64;
 }
 
-// Tile idx of the pass: heads in order, then query tiles, then the key tiles
-// each query tile's band meets (band_tiles; per_head tiles per head).  Closed
-// forms for no mask (all T) and causal (kt <= qt); a walk over the query tiles
-// for a sliding window.
+// Tile idx of the pass: heads in order, then the tiles of a head.  No mask:
+// key tiles in blocks of kKeyBlock, and within a block query tiles, then key
+// tiles, so that the 32 tiles an XCD runs at a time share 4 key tiles and
+// about 8 query tiles (fewer K and Q slices fetched into its L2 per step than
+// with all of a query tile's key tiles in a row: -1.7% on this pass at 31
+// frames).  Causal (kt <= qt): query tiles, then their key tiles (closed
+// form).  A sliding window: query tiles, then the key tiles each one's band
+// meets (band_tiles), found by a walk.  per_head tiles per head.
+constexpr int kKeyBlock = 4;
 __device__ __forceinline__ ScoresTile scores_tile(int idx, int T, const Band& band, int per_head) {
   ScoresTile t;
   t.bh = idx / per_head;
   int r = idx - t.bh * per_head;
   if (band_is_full(band)) {
-    t.qt = r / T;
-    t.kt = r - t.qt * T;
+    const int b = r / (kKeyBlock * T), rb = r - b * kKeyBlock * T;
+    const int w = min(kKeyBlock, T - kKeyBlock * b);  // key tiles in this block
+    t.qt = rb / w;
+    t.kt = kKeyBlock * b + (rb - t.qt * w);
   } else if (band_is_causal(band)) {
     int qt = (int)((sqrtf(8.f * (float)r + 1.f) - 1.f) * 0.5f);
     while ((qt + 1) * (qt + 2) / 2 <= r) ++qt;

@@ -88,7 +88,10 @@ __global__ __launch_bounds__(64 * QW * G) void online_attn_kernel(const uint16_t
   constexpr int BM = 32 * QW;                      // queries per workgroup
   constexpr int GT = 64 * QW;                      // threads per group
   constexpr int CPR = D / 8;                       // 16-byte chunks per K or V row
-  constexpr int SWZ = (CPR >= 8 ? 8 : CPR) - 1;    // chunk-index bits of K that are swizzled
+  // K chunk c of row r sits at c ^ kswz(r): a 16-lane cycle of a 16-byte
+  // fragment read covers 16 consecutive rows, and kswz makes their chunks land
+  // in 16 distinct 16-byte bank groups (row r starts at bank group CPR r mod 16).
+  constexpr int KSH = CPR == 4 ? 2 : CPR == 8 ? 1 : 0;
   constexpr int LOADS = kBN * CPR / GT;            // direct loads per thread per K (and V) tile
   constexpr int NS = D / 16;                       // k16 steps for S
   constexpr int NCB = D / 32;                      // 32-channel blocks of O
@@ -194,10 +197,10 @@ __global__ __launch_bounds__(64 * QW * G) void online_attn_kernel(const uint16_t
 
   // Both tiles are [64 keys][D channels] rows of 16-byte chunks, filled by
   // direct loads (one 1 KB run of 64 chunks per load and wave), issued
-  // untracked: the wait for them is the explicit one before each barrier.  K chunk c of
-  // row r sits at c ^ (r & SWZ), so that the K fragment reads (16 bytes of one
-  // row per lane) are conflict-free; V chunk c at c ^ vswz(r), so that the four
-  // rows one transpose read gathers fall in distinct banks.
+  // untracked: the wait for them is the explicit one before each barrier.  K
+  // chunk c of row r sits at c ^ kswz(r) (above); V chunk c at c ^ vswz(r), so
+  // that the four rows one transpose read gathers fall in distinct banks.
+  auto kswz = [](int r) { return (r >> KSH) & (CPR - 1); };
   auto vswz = [](int r) { return CPR >= 8 ? 2 * (r & 3) : 2 * ((r >> 1) & 1); };
   auto issue = [&](int t, int slot) {
 #pragma unroll
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(64 * QW * G) void online_attn_kernel(const uint16_t
       const int row = P / CPR, lc = P % CPR;
       const uint32_t key = (uint32_t)(t * kBN + row);
       load16_to_lds_untracked(rk, ktiles + slot * TILE + (j * QW + wave) * 1024,
-                              (key * ldk + (uint32_t)(lc ^ (row & SWZ)) * 8) * 2);
+                              (key * ldk + (uint32_t)(lc ^ kswz(row)) * 8) * 2);
       load16_to_lds_untracked(rv, vtiles + slot * TILE + (j * QW + wave) * 1024,
                               (key * ldv + (uint32_t)(lc ^ vswz(row)) * 8) * 2);
     }
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(64 * QW * G) void online_attn_kernel(const uint16_t
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int row = kb * 32 + c32;
-        const int pc = (2 * ss + h) ^ (row & SWZ);
+        const int pc = (2 * ss + h) ^ kswz(row);
         ka[ss][kb] = *(const bf16x8*)&kt[(row * CPR + pc) * 16];
       }
     __builtin_amdgcn_sched_barrier(0);

@@ -13,6 +13,8 @@ that oracle.  Under "runs", the other five workloads (the tiny d = 256 head,
 4 x 8 heads at d = 64 with and without the causal mask, 1 and 4 Wan frames),
 each timed the same way (events on the kernels' stream around K calls, then
 per-call events) and checked against the oracle, with the oracle's time.
+Before each workload's W warm-up calls, 0.2 s of untimed calls (settle_s) let
+the clocks leave their idle state.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--no-other-runs]
@@ -157,6 +159,24 @@ def abi_call(w, qd, kd, vd, out):
     return call
 
 
+SETTLE_S = 0.2  # untimed calls before the warm-up steps, so the clocks have left idle
+
+
+def settle(call, seconds: float = SETTLE_S):
+    """Untimed calls for `seconds` of wall time (synchronising every 10 calls, so
+    the time is the GPU's, not the host's enqueue rate): the clocks ramp up from
+    their idle state over a fraction of a second."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        call()
+        n += 1
+        if n % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def other_run(name: str, steps: int, warmup: int, dev):
     """One of the other workloads: warm up, time (per-kernel timing off), then
     the per-kernel averages over as many more calls, and oracle parity."""
@@ -169,6 +189,7 @@ def other_run(name: str, steps: int, warmup: int, dev):
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     out = torch.empty_like(qd)
     call = abi_call(w, qd, kd, vd, out)
+    settle(call)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -370,10 +391,11 @@ def main() -> int:
     out = torch.empty_like(qd)
     call = abi_call(w, qd, kd, vd, out)
 
+    settle(call)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup} done")
+    log(f"[bench] settle {SETTLE_S} s and warmup {args.warmup} done")
 
     kt = {}
     with kernel_timing(kt):
@@ -452,6 +474,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": round(ms, 5),
         "ms_per_call_median": round(med, 5),
         "ms_per_call_min": round(per_call[0], 5),

@@ -33,6 +33,7 @@
 // are read in place.
 #include <algorithm>
 #include <atomic>
+#include <cstddef>
 #include <type_traits>
 
 #include "device.h"
@@ -88,8 +89,11 @@ __device__ __forceinline__ u32x4 unswap_halves(u32x4 x, int r) {
 // keys outside the band); it is a template flag so that the per-element test
 // compiles to selects, not branches.
 constexpr int kSK = 128;  // keys per statistics tile
-struct ScoresSmem {
-  GemmSmem g;
+// Three K stages and two Q stages (160 KB, all of a CU's LDS): the K loads of a
+// step go out two steps ahead, the Q loads a step and a quarter ahead.
+struct alignas(16) ScoresSmem {
+  char a[3][kStageBytes];  // K
+  char b[2][kStageBytes];  // Q
 };
 
 struct ScoresTile {
@@ -268,16 +272,21 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ],
 
 // Persistent: workgroup g takes tiles g, g + G, g + 2G, ... (G = grid size; g
 // after the XCD renumbering, so each XCD works through a contiguous range).
-// The K steps of all its tiles form one stream through the two LDS stages:
-// the loads run two steps ahead across tile boundaries, so the next tile's
-// first stages arrive while this tile's epilogue computes and stores E.
+// The K steps of all its tiles form one stream through the LDS stages: the
+// loads run two steps ahead across tile boundaries, so the next tile's first
+// stages arrive while this tile's epilogue computes and stores E.  Step s reads
+// K stage s % 3 and Q stage s % 2.  During step s the wave issues its K loads
+// of step s + 2 (in the first sub-step, into the K stage step s - 1 read) and,
+// after the barrier that ends step s, its Q loads of step s + 2 (into the Q
+// stage step s read).  So before that barrier it waits for everything but the
+// last K loads; after an epilogue (whose stores may complete out of order with
+// the loads) for everything.
 // One LDS object (see the GEMM loop's notes on the compiler's LDS-DMA waits).
 __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, uint16_t* __restrict__ E,
     float* __restrict__ mref, float* __restrict__ psum, HeadMap hm, int L, int d, int T, int TK,
     int QB, int EB, float sl2, Band band, int per_head, int ntiles) {
-  __shared__ ScoresSmem smem;
-  GemmSmem& sm = smem.g;
+  __shared__ ScoresSmem sm;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int abase = scores_key_half(wave) * 128;  // key rows of this wave
@@ -289,6 +298,7 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
   const int total = my_tiles * nk;
   const int ldk = hm.k.ld, ldq = hm.q.ld;
   constexpr int kLoads = KContiguousT<kScoresWaves>::kLoads;  // per wave and operand
+  static_assert(kLoads == 4, "one load per MFMA pair; the waits below count 4 loads");
 
   KContiguousT<kScoresWaves> la, lb;  // per-lane offsets within a tile; resources start at its first row
   la.init(make_rsrc(k, 0), (uint32_t)ldk, 0, wave, lane);
@@ -304,55 +314,56 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
     rk = make_rsrc(k + hm.k_off(t.bh) + (size_t)k0 * ldk, ((uint32_t)(L - 1 - k0) * ldk + d) * 2u);
     rq = make_rsrc(q + hm.q_off(t.bh) + (size_t)q0 * ldq, ((uint32_t)(L - 1 - q0) * ldq + d) * 2u);
   };
+  // Past the last step the cursor stays there: the loads of steps beyond the
+  // end reload it into stages no longer read.
   auto advance = [&]() {
+    if (li == my_tiles - 1 && lk == nk - 1) return;
     if (++lk == nk) {
       lk = 0;
-      if (++li < my_tiles) set_load_tile(li);
+      set_load_tile(++li);
     }
   };
-  auto issue_next = [&](char* sa, char* sb) {
-    la.issue_from(rk, lk * kStepK, sa, wave);
-    lb.issue_from(rq, lk * kStepK, sb, wave);
-    advance();
+  // Before the barrier ending a step: this wave's loads of the next step have
+  // landed (only the K loads of the step after it may still be in flight,
+  // unless stores were issued since).
+  auto wait_next = [&](bool after_stores) {
+    if (after_stores)
+      wait_vmem();
+    else
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   };
 
-  // The K loads of a load step go out one step after its Q loads, in the first
-  // sub-step of the next step (or at the start of an idle step); these hold
-  // the cursor of the last load step served.  At the start, and after a step
-  // whose wave issued both at once, they repeat loads already issued (same
-  // bytes into the same place).
-  __amdgpu_buffer_rsrc_t rk_pend;
-  int lk_pend;
-
   set_load_tile(0);
-  issue_next(sm.a[0], sm.b[0]);
+  la.issue_from(rk, 0, sm.a[0], wave);
+  lb.issue_from(rq, 0, sm.b[0], wave);
+  advance();
   wait_vmem();
   block_sync();
-  rk_pend = rk;
-  lk_pend = lk;
-  issue_next(sm.a[1], sm.b[1]);  // total >= nk >= 3
+  la.issue_from(rk, lk * kStepK, sm.a[1], wave);  // total >= nk >= 3
+  lb.issue_from(rq, lk * kStepK, sm.b[1], wave);
+  advance();  // the cursor is on step 2
 
   f32x16 acc[4][kScoresNJ];
   NoTransform nx;
   FragsT<kScoresNJ> cur, nxt;
   read_frags(cur, la, lb, sm.a[0], sm.b[0], abase, bbase, lane, 0);
 
-  // One K step s: sub-step 0 starts the accumulators when FIRST.
-  auto step = [&](auto first_step, int s) {
+  // One K step s (K stage ka = s % 3): sub-step 0 starts the accumulators
+  // when FIRST (the first step of a tile, which follows an epilogue).
+  auto step = [&](auto first_step, int s, int ka) {
     constexpr bool FIRST = decltype(first_step)::value;
+    const int kn = ka == 2 ? 0 : ka + 1, kf = kn == 2 ? 0 : kn + 1;  // stages of steps s + 1, s + 2
     const int st = s & 1;
-    const char* sa = sm.a[st];
+    const char* sa = sm.a[ka];
     const char* sb = sm.b[st];
-    // Sub-step 0: its MFMAs in pairs, each followed by one of the K loads the
-    // previous step deferred (the next step's, into the stage this step does
-    // not read).
+    // Sub-step 0: its MFMAs in pairs, each followed by one K load of step s + 2.
     read_frags(nxt, la, lb, sa, sb, abase, bbase, lane, 1);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       __builtin_amdgcn_sched_barrier(0);
       acc[p][0] = mfma32x32x16(cur.a[p], cur.b[0], FIRST ? f32x16{} : acc[p][0]);
       acc[p][1] = mfma32x32x16(cur.a[p], cur.b[1], FIRST ? f32x16{} : acc[p][1]);
-      la.issue_one(rk_pend, lk_pend * kStepK, sm.a[st ^ 1], wave, p);
+      la.issue_one(rk, lk * kStepK, sm.a[kf], wave, p);
     }
     __builtin_amdgcn_sched_barrier(0);
     cur = nxt;
@@ -364,53 +375,43 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
       cur = nxt;
     }
     // Last sub-step: next stage complete everywhere, this stage drained.
-    wait_vmem();
+    wait_next(FIRST);
     block_sync();
-    // This sub-step's MFMAs in pairs, each pair followed by one load of each
-    // operand for step s + 2 (past the end the cursor stays on the last tile: a
-    // reload into a stage no longer read), with the next step's first fragments
-    // read before the last pair.  Measured: loads as a burst right after the
-    // barrier, or those reads right after it, both cost a few percent.
+    // This sub-step's MFMAs in pairs, each pair followed by one Q load of step
+    // s + 2, with the next step's first fragments read before the last pair.
+    // Measured: loads as a burst right after the barrier, or those reads right
+    // after it, both cost a few percent.
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       if (p == 3) {
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(nxt, la, lb, sm.a[st ^ 1], sm.b[st ^ 1], abase, bbase, lane, 0);  // past the end: unused
+        read_frags(nxt, la, lb, sm.a[kn], sm.b[st ^ 1], abase, bbase, lane, 0);  // past the end: unused
       }
       __builtin_amdgcn_sched_barrier(0);
       acc[p][0] = mfma32x32x16(cur.a[p], cur.b[0], acc[p][0]);
       acc[p][1] = mfma32x32x16(cur.a[p], cur.b[1], acc[p][1]);
-      static_assert(kLoads == 4, "one load per MFMA pair");
       lb.issue_one(rq, lk * kStepK, sm.b[st], wave, p);
     }
     __builtin_amdgcn_sched_barrier(0);
     cur = nxt;
-    rk_pend = rk;
-    lk_pend = lk;
-    if (s + 2 < total) advance();
+    advance();
   };
 
   // A step of a wave whose block of the tile is discarded: its loads and the
   // barrier only.
-  auto idle_step = [&](int s) {
-    const int st = s & 1;
-    // The K loads the previous step deferred to this one (the next step reads
-    // them), then both operands of the step two ahead at once.
+  auto idle_step = [&](int s, int ka, bool after_stores) {
+    const int kf = ka == 0 ? 2 : ka - 1;  // (s + 2) % 3
 #pragma unroll
-    for (int p = 0; p < 4; ++p) la.issue_one(rk_pend, lk_pend * kStepK, sm.a[st ^ 1], wave, p);
-    wait_vmem();
+    for (int p = 0; p < 4; ++p) la.issue_one(rk, lk * kStepK, sm.a[kf], wave, p);
+    wait_next(after_stores);
     block_sync();
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      la.issue_one(rk, lk * kStepK, sm.a[st], wave, p);
-      lb.issue_one(rq, lk * kStepK, sm.b[st], wave, p);
-    }
-    rk_pend = rk;
-    lk_pend = lk;
-    if (s + 2 < total) advance();
+    for (int p = 0; p < 4; ++p) lb.issue_one(rq, lk * kStepK, sm.b[s & 1], wave, p);
+    advance();
   };
 
-  int s = 0;
+  int s = 0, ka = 0;  // ka = s % 3
+  auto next_ka = [&]() { ka = ka == 2 ? 0 : ka + 1; };
   for (int i = 0; i < my_tiles; ++i) {
     const ScoresTile t = scores_tile(first + i * G, T, band, per_head);
     if (__builtin_amdgcn_readfirstlane((int)scores_wave_idle(t, wave, L, band))) {
@@ -419,10 +420,17 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
       for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
         for (int bj = 0; bj < kScoresNJ; ++bj) acc[bi][bj] = f32x16{};
-      for (int kk = 0; kk < nk; ++kk) idle_step(s++);
+      for (int kk = 0; kk < nk; ++kk) {
+        idle_step(s++, ka, kk == 0);
+        next_ka();
+      }
     } else {
-      step(std::true_type{}, s++);
-      for (int kk = 1; kk < nk; ++kk) step(std::false_type{}, s++);
+      step(std::true_type{}, s++, ka);
+      next_ka();
+      for (int kk = 1; kk < nk; ++kk) {
+        step(std::false_type{}, s++, ka);
+        next_ka();
+      }
     }
     if (!scores_tile_unmasked(t, band, L))
       scores_epilogue<true>(acc, E, mref, psum, t, L, QB, EB, TK, sl2, band);
@@ -430,7 +438,7 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
       scores_epilogue<false>(acc, E, mref, psum, t, L, QB, EB, TK, sl2, band);
     // The next step's first fragments: read again (its stage is not refilled
     // before that step's end) instead of holding them through the epilogue.
-    read_frags(cur, la, lb, sm.a[s & 1], sm.b[s & 1], abase, bbase, lane, 0);
+    read_frags(cur, la, lb, sm.a[ka], sm.b[s & 1], abase, bbase, lane, 0);
   }
   wait_vmem();
 }
@@ -448,11 +456,12 @@ struct PowerOfTwoShift {
   int col[4];                   // this lane's four query columns in the tile
   unsigned sw[4];               // current shift words (s << 7 | s << 23)
 
+  // Before step kt (32 keys each; four per 128-key tile).
   __device__ __forceinline__ void step(int kt, bool first) {
-    if ((kt & 1) == 0 || first) {
+    if ((kt & 3) == 0 || first) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const unsigned s = tab[kt >> 1][col[j]];
+        const unsigned s = tab[kt >> 2][col[j]];
         sw[j] = (s << 7) | (s << 23);
       }
     }
@@ -465,46 +474,56 @@ struct PowerOfTwoShift {
   }
 };
 
-struct ValuesSmem {
-  GemmSmem g;
+// The values pass walks the keys in steps of 32 through four LDS stages of
+// 32 KB (V 16 KB, E 16 KB): the loads of step kt + 3 go out during step kt,
+// so a load has three steps to arrive (two 64-key stages gave it about half
+// of one 64-key step).
+constexpr int kVK = 32;      // keys per values step
+constexpr int kVStages = 4;  // stages in flight
+constexpr int kVStageBytes = kVK * kTile * 2;
+
+struct alignas(16) ValuesSmem {
+  char v[kVStages][kVStageBytes];  // V rows [32 keys][256 channels]
+  char e[kVStages][kVStageBytes];  // E blocks [8 query blocks][2 key blocks]
   uint8_t shift_tab[kMaxTiles][kTile];
   float inv_l[kTile];
 };
+static_assert(sizeof(ValuesSmem) <= 160 * 1024, "a CU's LDS");
 
-// Staging of the values pass, 8 waves: V read as V^T (64 key rows x 256
+// Staging of the values pass, 8 waves: V read as V^T (32 key rows x 256
 // channels per stage, 512 bytes per row, 16-byte chunk c of row r at
 // c ^ 4 (r % 4), stage row r holding key k0 + kperm(r): the order the scores
-// pass gives the keys of each 32-key block of E) and E (the 8 x 4 blocks of
+// pass gives the keys of each 32-key block of E) and E (the 8 x 2 blocks of
 // 32 queries x 16 keys the step covers, copied as they are: block (i, j) at
-// 1 KB x (4 i + j); a lane's MFMA operand is 16 contiguous bytes of a block).
-// Each wave issues 4 loads of each per step, through untracked direct loads:
+// 1 KB x (2 i + j); a lane's MFMA operand is 16 contiguous bytes of a block).
+// Each wave issues 2 loads of each per step, through untracked direct loads:
 // the transpose reads of V carry no alias information, and the compiler would
 // otherwise wait for every load in flight before each of them.
 constexpr int kValuesWaves = 8;
 struct ValuesV {
-  uint32_t off[4];
+  uint32_t off[2];
   uint32_t ld2;  // bytes per key row
   __device__ __forceinline__ void init(uint32_t ld, int m0, int wave, int lane) {
     ld2 = ld * 2u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int P = (wave * 4 + j) * 64 + lane;  // 16-byte chunk slot in the stage
+    for (int j = 0; j < 2; ++j) {
+      const int P = (wave * 2 + j) * 64 + lane;  // 16-byte chunk slot in the stage
       const int row = P >> 5, pc = P & 31, lc = pc ^ ((row & 3) << 2);
       off[j] = (uint32_t)kperm(row) * ld2 + (uint32_t)(m0 + lc * 8) * 2u;
     }
   }
   __device__ __forceinline__ void issue(const u32x4& r, int k0, char* stage, int wave, int j) const {
-    load16_to_lds_untracked(r, stage + (wave * 4 + j) * 1024, off[j] + (uint32_t)k0 * ld2);
+    load16_to_lds_untracked(r, stage + (wave * 2 + j) * 1024, off[j] + (uint32_t)k0 * ld2);
   }
 };
-// Wave w copies query block w of the tile's 8, key blocks k0 / 16 .. + 4.
+// Wave w copies query block w of the tile's 8, key blocks k0 / 16 and k0 / 16 + 1.
 struct ValuesE {
   uint32_t off;
   __device__ __forceinline__ void init(int EB, int wave, int lane) {
     off = (uint32_t)wave * (uint32_t)EB * 1024u + (uint32_t)lane * 16u;
   }
   __device__ __forceinline__ void issue(const u32x4& r, int k0, char* stage, int wave, int j) const {
-    load16_to_lds_untracked(r, stage + (wave * 4 + j) * 1024, off + (uint32_t)((k0 >> 4) + j) * 1024u);
+    load16_to_lds_untracked(r, stage + (wave * 2 + j) * 1024, off + (uint32_t)((k0 >> 4) + j) * 1024u);
   }
 };
 
@@ -522,8 +541,11 @@ struct ValuesFrags {
 // [128 (w / 4), +128) of the tile, as 2 x 4 accumulator blocks.  Per k16
 // sub-step it reads 2 V^T fragments (two transpose reads each) and 4 E
 // fragments for 8 MFMAs; the next sub-step's fragments are read while the
-// current MFMAs run.  The next step's loads go out one per MFMA pair in the
-// step's first two sub-steps (into the stage the previous step drained).
+// current MFMAs run.  Step kt (32 keys, two sub-steps): the loads of step
+// kt + 3 go out one per MFMA pair in the first sub-step (into the stage step
+// kt - 1 read); the wave then waits for its loads of step kt + 1, meets the
+// others at the barrier, and runs the second sub-step's MFMAs (fragments
+// already in registers) while it reads the first fragments of step kt + 1.
 template <bool SPLIT>
 __global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_t* __restrict__ v,
                                                      const uint16_t* __restrict__ E,
@@ -535,10 +557,9 @@ __global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_
                                                      int d, int T, int TK, int QB, int EB,
                                                      int Lk, Band band, int ncb, int split,
                                                      int nheads) {
-  __shared__ ValuesSmem smem;
-  GemmSmem& sm = smem.g;
-  uint8_t(&shift_tab)[kMaxTiles][kTile] = smem.shift_tab;
-  float(&inv_l)[kTile] = smem.inv_l;
+  __shared__ ValuesSmem sm;
+  uint8_t(&shift_tab)[kMaxTiles][kTile] = sm.shift_tab;
+  float(&inv_l)[kTile] = sm.inv_l;
 
   if (!SPLIT) split = 1;
   const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -556,11 +577,39 @@ __global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_
   int tlo, thi;
   band_tiles(band, qt, kTile, TK, kSK, &tlo, &thi);
   const int kbeg = tlo * kSK, kend = min(Lk, (thi + 1) * kSK);
-  // Split sp of `split` takes K steps [k_first, k_first + nk) (never empty:
-  // the host keeps split <= the fewest steps of any query tile).
-  const int nk_all = (kend - kbeg) / kStepK;
-  const int k_first = kbeg / kStepK + (SPLIT ? nk_all * sp / split : 0);
-  const int nk = SPLIT ? kbeg / kStepK + nk_all * (sp + 1) / split - k_first : nk_all;
+  // Split sp of `split` takes steps [k_first, k_first + nk) (never empty: the
+  // host keeps split <= the fewest 64-key steps of any query tile).
+  const int nk_all = (kend - kbeg) / kVK;
+  const int k_first = kbeg / kVK + (SPLIT ? nk_all * sp / split : 0);
+  const int nk = SPLIT ? kbeg / kVK + nk_all * (sp + 1) / split - k_first : nk_all;
+
+  // V's resource ends after the head's row L - 1 (keys past L read as zero).
+  // Channels past d of a 256-channel tile read whatever lies there (zero past
+  // the end) and only feed accumulator rows that are never stored.
+  const int ldv = hm.v.ld;
+  const u32x4 rv = rsrc_words(v + hm.v_off(bh), ((uint32_t)(L - 1) * ldv + d) * 2u);
+  // E from the tile's first query block; blocks past the head's last read as zero.
+  const u32x4 re = rsrc_words(E + ((size_t)bh * QB + (size_t)qt * 8) * EB * 512,
+                              (uint32_t)(QB - qt * 8) * (uint32_t)EB * 1024u);
+  ValuesV la;
+  ValuesE lb;
+  la.init((uint32_t)ldv, ct * kTile, wave, lane);
+  lb.init(EB, wave, lane);
+  // Load j (0..3) of step u into its stage; steps past the last reload the
+  // last (into a stage no longer read), so every step issues 4 loads.
+  const int kb = k_first * kVK;
+  auto issue = [&](int u, int j) {
+    const int k0 = kb + min(u, nk - 1) * kVK;
+    if (j < 2)
+      la.issue(rv, k0, sm.v[u & 3], wave, j);
+    else
+      lb.issue(re, k0, sm.e[u & 3], wave, j - 2);
+  };
+  // Steps 0, 1 and 2 go out first, and arrive while the statistics are read.
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) issue(u, j);
 
   // Thread tid < 256 owns query qt*256 + tid: M = max_t m_t, l = sum_t 2^(m_t - M) psum_t,
   // and the shift M - m_t of each tile (a nonnegative integer; -inf tiles -> 255).
@@ -602,30 +651,10 @@ __global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_
     if (lse != nullptr && ct == 0 && sp == 0 && query < L)
       lse[(size_t)(hm.bh0 + bh) * L + query] = (M + log2f(l)) * 0.6931471805599453f;
   }
-
-  // V's resource ends after the head's row L - 1 (keys past L read as zero).
-  // Channels past d of a 256-channel tile read whatever lies there (zero past
-  // the end) and only feed accumulator rows that are never stored.
-  const int ldv = hm.v.ld;
-  const u32x4 rv = rsrc_words(v + hm.v_off(bh), ((uint32_t)(L - 1) * ldv + d) * 2u);
-  // E from the tile's first query block; blocks past the head's last read as zero.
-  const u32x4 re = rsrc_words(E + ((size_t)bh * QB + (size_t)qt * 8) * EB * 512,
-                              (uint32_t)(QB - qt * 8) * (uint32_t)EB * 1024u);
-  ValuesV la;
-  ValuesE lb;
-  la.init((uint32_t)ldv, ct * kTile, wave, lane);
-  lb.init(EB, wave, lane);
-  auto issue = [&](int k0, int st, int j) {  // load j (0..7) of the step at key k0
-    if (j < 4)
-      la.issue(rv, k0, sm.a[st], wave, j);
-    else
-      lb.issue(re, k0, sm.b[st], wave, j - 4);
-  };
-  const int kb = k_first * kStepK;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) issue(kb, 0, j);
-  wait_vmem();
-  __syncthreads();  // step 0 staged; the shift table and 1/l are complete
+  // Step 0 staged (only steps 1 and 2 may be in flight); the shift table and
+  // 1/l complete.
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  block_sync();
 
   PowerOfTwoShift sh;
   sh.tab = shift_tab;
@@ -637,12 +666,13 @@ __global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_
   }
 
   KOuter ka;  // fragment reads only (the loads go through ValuesV)
-  auto read = [&](ValuesFrags& f, const char* sa, const char* sb, int ss) {
+  auto read = [&](ValuesFrags& f, int st, int ss) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) f.a[i] = ka.frag(sa, cq * 64 + i * 32, ss, lane);
+    for (int i = 0; i < 2; ++i) f.a[i] = ka.frag(sm.v[st], cq * 64 + i * 32, ss, lane);
     // E block (query block 4 qh + j, key block ss): 16 contiguous bytes per lane.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[j] = *(const bf16x8*)(sb + ((qh * 4 + j) * 4 + ss) * 1024 + lane * 16);
+    for (int j = 0; j < 4; ++j)
+      f.b[j] = *(const bf16x8*)(sm.e[st] + ((qh * 4 + j) * 2 + ss) * 1024 + lane * 16);
   };
 
   f32x16 acc[2][4];
@@ -652,17 +682,13 @@ __global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
   ValuesFrags cur, nxt;
-  read(cur, sm.a[0], sm.b[0], 0);
+  read(cur, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    const bool more = kt + 1 < nk;
-    // Past the last step: a reload of the last step into the stage no longer
-    // read, so that every step issues its loads unconditionally.
-    const int k1 = kb + (more ? kt + 1 : kt) * kStepK;
+    const int st = kt & 3;
     sh.step(k_first + kt, kt == 0);
-#pragma unroll
-    for (int ss = 0; ss < 4; ++ss) {
-      if (ss < 3) read(nxt, sm.a[st], sm.b[st], ss + 1);
+    // Sub-step 0, with the loads of step kt + 3.
+    read(nxt, st, 1);
+    {
       bf16x8 bt[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) bt[j] = sh(cur.b[j], j);
@@ -672,16 +698,35 @@ __global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_
         const int i = p >> 1, j0 = 2 * (p & 1);
         acc[i][j0] = mfma32x32x16(cur.a[i], bt[j0], acc[i][j0]);
         acc[i][j0 + 1] = mfma32x32x16(cur.a[i], bt[j0 + 1], acc[i][j0 + 1]);
-        if (ss < 2) issue(k1, st ^ 1, ss * 4 + p);
+        issue(kt + 3, p);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (ss < 3) cur = nxt;
     }
-    // The next step is staged everywhere; this step's stage is no longer read.
-    wait_vmem();
-    __syncthreads();
-    if (more) read(cur, sm.a[st ^ 1], sm.b[st ^ 1], 0);
+    cur = nxt;
+    // Step kt + 1 staged everywhere (this wave's loads of steps kt + 2 and
+    // kt + 3 may still be in flight); stage st is read no more after this
+    // barrier (sub-step 1's fragments are in registers).
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    block_sync();
+    {
+      bf16x8 bt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bt[j] = sh(cur.b[j], j);
+      read(nxt, (kt + 1) & 3, 0);  // past the last step: unused
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int i = p >> 1, j0 = 2 * (p & 1);
+        acc[i][j0] = mfma32x32x16(cur.a[i], bt[j0], acc[i][j0]);
+        acc[i][j0 + 1] = mfma32x32x16(cur.a[i], bt[j0 + 1], acc[i][j0 + 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    cur = nxt;
   }
+  // No load in flight into the stages (the O tile below reuses them).
+  wait_vmem();
+  block_sync();
 
   if constexpr (SPLIT) {
     // This split's share of O = (its part of the sum) / l, in fp32, for the
@@ -708,9 +753,13 @@ __global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_
   }
 
   // O[query][ch] = acc / l, rounded once to bf16.  The tile goes through the
-  // drained GEMM stages as [query][256 channels] rows (laid out like the E tile
-  // of the scores pass) so that the global stores write whole row segments.
-  char* stage = sm.a[0];
+  // drained stages (128 KB from sm.v[0] on) as [query][256 channels] rows
+  // (laid out like the E tile of the scores pass) so that the global stores
+  // write whole row segments.
+  static_assert(offsetof(ValuesSmem, e) == kVStages * kVStageBytes &&
+                    2 * kVStages * kVStageBytes >= kTile * kTile * 2,
+                "the O tile fits the stages");
+  char* stage = sm.v[0];
 #pragma unroll
   for (int bj = 0; bj < 4; ++bj) {
     const int ql = qh * 128 + bj * 32 + c32;

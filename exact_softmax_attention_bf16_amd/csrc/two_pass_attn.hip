@@ -279,8 +279,8 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ],
 // of step s + 2 (in the first sub-step, into the K stage step s - 1 read) and,
 // after the barrier that ends step s, its Q loads of step s + 2 (into the Q
 // stage step s read).  So before that barrier it waits for everything but the
-// last K loads; after an epilogue (whose stores may complete out of order with
-// the loads) for everything.
+// last four loads it issued (loads complete in order; a store issued between
+// them, such as the epilogue's, only makes the wait longer).
 // One LDS object (see the GEMM loop's notes on the compiler's LDS-DMA waits).
 __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, uint16_t* __restrict__ E,
@@ -295,7 +295,6 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
   const int first = (int)xcd_logical_id(blockIdx.x, gridDim.x);
   const int my_tiles = (ntiles - 1 - first) / G + 1;  // first < ntiles
   const int nk = d / kStepK;                          // >= 3 on this path
-  const int total = my_tiles * nk;
   const int ldk = hm.k.ld, ldq = hm.q.ld;
   constexpr int kLoads = KContiguousT<kScoresWaves>::kLoads;  // per wave and operand
   static_assert(kLoads == 4, "one load per MFMA pair; the waits below count 4 loads");
@@ -324,14 +323,8 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
     }
   };
   // Before the barrier ending a step: this wave's loads of the next step have
-  // landed (only the K loads of the step after it may still be in flight,
-  // unless stores were issued since).
-  auto wait_next = [&](bool after_stores) {
-    if (after_stores)
-      wait_vmem();
-    else
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  };
+  // landed (only the K loads of the step after it may still be in flight).
+  auto wait_next = [&]() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); };
 
   set_load_tile(0);
   la.issue_from(rk, 0, sm.a[0], wave);
@@ -339,7 +332,7 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
   advance();
   wait_vmem();
   block_sync();
-  la.issue_from(rk, lk * kStepK, sm.a[1], wave);  // total >= nk >= 3
+  la.issue_from(rk, lk * kStepK, sm.a[1], wave);  // nk >= 3: a step of the first tile
   lb.issue_from(rq, lk * kStepK, sm.b[1], wave);
   advance();  // the cursor is on step 2
 
@@ -349,7 +342,7 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
   read_frags(cur, la, lb, sm.a[0], sm.b[0], abase, bbase, lane, 0);
 
   // One K step s (K stage ka = s % 3): sub-step 0 starts the accumulators
-  // when FIRST (the first step of a tile, which follows an epilogue).
+  // when FIRST (the first step of a tile).
   auto step = [&](auto first_step, int s, int ka) {
     constexpr bool FIRST = decltype(first_step)::value;
     const int kn = ka == 2 ? 0 : ka + 1, kf = kn == 2 ? 0 : kn + 1;  // stages of steps s + 1, s + 2
@@ -375,7 +368,7 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
       cur = nxt;
     }
     // Last sub-step: next stage complete everywhere, this stage drained.
-    wait_next(FIRST);
+    wait_next();
     block_sync();
     // This sub-step's MFMAs in pairs, each pair followed by one Q load of step
     // s + 2, with the next step's first fragments read before the last pair.
@@ -399,11 +392,11 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
 
   // A step of a wave whose block of the tile is discarded: its loads and the
   // barrier only.
-  auto idle_step = [&](int s, int ka, bool after_stores) {
+  auto idle_step = [&](int s, int ka) {
     const int kf = ka == 0 ? 2 : ka - 1;  // (s + 2) % 3
 #pragma unroll
     for (int p = 0; p < 4; ++p) la.issue_one(rk, lk * kStepK, sm.a[kf], wave, p);
-    wait_next(after_stores);
+    wait_next();
     block_sync();
 #pragma unroll
     for (int p = 0; p < 4; ++p) lb.issue_one(rq, lk * kStepK, sm.b[s & 1], wave, p);
@@ -421,7 +414,7 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
 #pragma unroll
         for (int bj = 0; bj < kScoresNJ; ++bj) acc[bi][bj] = f32x16{};
       for (int kk = 0; kk < nk; ++kk) {
-        idle_step(s++, ka, kk == 0);
+        idle_step(s++, ka);
         next_ka();
       }
     } else {
@@ -452,19 +445,18 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
 constexpr int kMaxTiles = kTwoPassMaxTiles;
 
 struct PowerOfTwoShift {
-  const uint8_t (*tab)[kTile];  // [128-key tile t][query in tile]: M - m_t, capped at 255
-  int col[4];                   // this lane's four query columns in the tile
-  unsigned sw[4];               // current shift words (s << 7 | s << 23)
+  int col[4];      // this lane's four query columns in the tile
+  unsigned sw[4];  // shift words (s << 7 | s << 23) of the current 128-key tile
 
-  // Before step kt (32 keys each; four per 128-key tile).
-  __device__ __forceinline__ void step(int kt, bool first) {
-    if ((kt & 3) == 0 || first) {
+  // The shifts of 128-key tile t (from [t][query in tile]: M - m_t), and the
+  // shift words made from them.
+  __device__ __forceinline__ void load(const uint8_t (*tab)[kTile], int t, unsigned (&s)[4]) const {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const unsigned s = tab[kt >> 2][col[j]];
-        sw[j] = (s << 7) | (s << 23);
-      }
-    }
+    for (int j = 0; j < 4; ++j) s[j] = tab[t][col[j]];
+  }
+  __device__ __forceinline__ void set(const unsigned (&s)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sw[j] = (s[j] << 7) | (s[j] << 23);
   }
   __device__ __forceinline__ bf16x8 operator()(bf16x8 f, int j) const {
     u32x4 w = __builtin_bit_cast(u32x4, f);
@@ -657,7 +649,6 @@ __global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_
   block_sync();
 
   PowerOfTwoShift sh;
-  sh.tab = shift_tab;
   float invl[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -681,47 +672,58 @@ __global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
+  // The E fragments are scaled as soon as they arrive, in the second half of
+  // the sub-step that reads them, so that the MFMAs after a barrier start at
+  // once.  The shift words of a step are read during the step before.
+  // 8 MFMAs of one sub-step in pairs; after pair p, load p of step kt + 3
+  // (LOADS) and, in pairs 2 and 3, the scaling of two fragments of `f`.
+  auto mfma_pairs = [&](const ValuesFrags& c, ValuesFrags& f, int kt, bool loads) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int i = p >> 1, j0 = 2 * (p & 1);
+      acc[i][j0] = mfma32x32x16(c.a[i], c.b[j0], acc[i][j0]);
+      acc[i][j0 + 1] = mfma32x32x16(c.a[i], c.b[j0 + 1], acc[i][j0 + 1]);
+      if (loads) issue(kt + 3, p);
+      if (p >= 2) {
+        // Scaled here (the empty asm keeps the compiler from sinking the
+        // scaling past the barrier to its first use).
+        const int j = 2 * (p - 2);
+        f.b[j] = sh(f.b[j], j);
+        f.b[j + 1] = sh(f.b[j + 1], j + 1);
+        asm volatile("" : "+v"(f.b[j]), "+v"(f.b[j + 1]));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   ValuesFrags cur, nxt;
+  {
+    unsigned s0[4];
+    sh.load(shift_tab, k_first >> 2, s0);
+    sh.set(s0);
+  }
   read(cur, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cur.b[j] = sh(cur.b[j], j);
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 3;
-    sh.step(k_first + kt, kt == 0);
+    // The shifts of step kt + 1 (past the end: unused), turned into shift
+    // words after this sub-step's MFMAs.
+    unsigned sn[4];
+    sh.load(shift_tab, min((k_first + kt + 1) >> 2, thi), sn);
     // Sub-step 0, with the loads of step kt + 3.
     read(nxt, st, 1);
-    {
-      bf16x8 bt[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bt[j] = sh(cur.b[j], j);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        __builtin_amdgcn_sched_barrier(0);
-        const int i = p >> 1, j0 = 2 * (p & 1);
-        acc[i][j0] = mfma32x32x16(cur.a[i], bt[j0], acc[i][j0]);
-        acc[i][j0 + 1] = mfma32x32x16(cur.a[i], bt[j0 + 1], acc[i][j0 + 1]);
-        issue(kt + 3, p);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    mfma_pairs(cur, nxt, kt, true);
     cur = nxt;
     // Step kt + 1 staged everywhere (this wave's loads of steps kt + 2 and
     // kt + 3 may still be in flight); stage st is read no more after this
     // barrier (sub-step 1's fragments are in registers).
     asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     block_sync();
-    {
-      bf16x8 bt[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bt[j] = sh(cur.b[j], j);
-      read(nxt, (kt + 1) & 3, 0);  // past the last step: unused
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        __builtin_amdgcn_sched_barrier(0);
-        const int i = p >> 1, j0 = 2 * (p & 1);
-        acc[i][j0] = mfma32x32x16(cur.a[i], bt[j0], acc[i][j0]);
-        acc[i][j0 + 1] = mfma32x32x16(cur.a[i], bt[j0 + 1], acc[i][j0 + 1]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    read(nxt, (kt + 1) & 3, 0);  // past the last step: unused
+    sh.set(sn);
+    mfma_pairs(cur, nxt, kt, false);
     cur = nxt;
   }
   // No load in flight into the stages (the O tile below reuses them).

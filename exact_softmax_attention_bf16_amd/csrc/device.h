@@ -45,10 +45,14 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t voff)
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
 }
 
-// 16 bytes from byte offset `voff` straight into LDS.  `dst` is wave-uniform;
-// lane i's 16 bytes land at dst + 16 * i.
-__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)dst, 16, (int)voff, 0, 0, 0);
+// 16 bytes from byte offset `voff` + `soff` straight into LDS.  `dst` and
+// `soff` are wave-uniform (soff, a scalar operand, saves a vector add per
+// load; callers keep it below the row length, so that whether a row lies
+// past the end of the resource is decided by `voff` alone); lane i's 16 bytes
+// land at dst + 16 * i.
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff,
+                                              uint32_t soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)dst, 16, (int)voff, (int)soff, 0, 0);
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

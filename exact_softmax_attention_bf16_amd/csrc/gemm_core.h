@@ -60,7 +60,7 @@ struct KContiguousT {
   // Load j of this wave's kLoads.
   __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int k0, char* stage,
                                             int wave, int j) const {
-    load16_to_lds(rs, stage + (wave * kLoads + j) * 1024, off[j] + (uint32_t)k0 * 2u);
+    load16_to_lds(rs, stage + (wave * kLoads + j) * 1024, off[j], (uint32_t)k0 * 2u);
   }
   // MFMA fragment: lane supplies row rbase + lane % 32, K values 16 ss + 8 (lane / 32) .. + 8.
   __device__ __forceinline__ bf16x8 frag(const char* stage, int rbase, int ss, int lane) const {

@@ -288,7 +288,8 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
     int QB, int EB, float sl2, Band band, int per_head, int ntiles) {
   __shared__ ScoresSmem sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: stage addresses in scalar registers
   const int abase = scores_key_half(wave) * 128;  // key rows of this wave
   const int bbase = scores_query_base(wave);  // query rows of this wave
   const int G = (int)gridDim.x;

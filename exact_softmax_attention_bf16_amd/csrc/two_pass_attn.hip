@@ -606,37 +606,48 @@ __global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_
 
   // Thread tid < 256 owns query qt*256 + tid: M = max_t m_t, l = sum_t 2^(m_t - M) psum_t,
   // and the shift M - m_t of each tile (a nonnegative integer; -inf tiles -> 255).
-  // The stats are read in batches of 16 tiles so their latencies overlap.
+  // The stats of up to 32 tiles are read at once, so that their latencies
+  // overlap and, for query tiles that meet at most 32 score tiles (L <= 4096
+  // without a band), the shifts come from the same registers: one round of
+  // loads instead of four (batches of 16 and a second pass).
   if (tid < kTile) {
     const float* mh = mref + (size_t)bh * TK * L;
     const float* ph = psum + (size_t)bh * TK * L;
     const int qc = min(qt * kTile + tid, L - 1);
+    constexpr int kB = 32;
     float M = -INFINITY, l = 0.f;
-    for (int t0 = tlo; t0 <= thi; t0 += 16) {
-      float mt[16], pt[16];
+    float mt[kB];
+    for (int t0 = tlo; t0 <= thi; t0 += kB) {
+      float pt[kB];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < kB; ++u) {
         const int t = min(t0 + u, thi);
         mt[u] = mh[(size_t)t * L + qc];
         pt[u] = ph[(size_t)t * L + qc];
       }
       float Mn = M;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) Mn = fmaxf(Mn, mt[u]);
+      for (int u = 0; u < kB; ++u) Mn = fmaxf(Mn, mt[u]);
       l = M == -INFINITY ? 0.f : l * exp2_fast(M - Mn);
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
+      for (int u = 0; u < kB; ++u)
         if (t0 + u <= thi && mt[u] != -INFINITY) l += pt[u] * exp2_fast(mt[u] - Mn);
       M = Mn;
     }
-    // The shifts need the final M: a second pass over the (now cached) stats.
-    for (int t0 = tlo; t0 <= thi; t0 += 16) {
-      float mt[16];
+    // The shifts need the final M: from the registers when one batch held
+    // every tile, else a second pass over the (now cached) stats.
+    if (thi - tlo < kB) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) mt[u] = mh[(size_t)min(t0 + u, thi) * L + qc];
+      for (int u = 0; u < kB; ++u)
+        if (tlo + u <= thi) shift_tab[tlo + u][tid] = (uint8_t)fminf(M - mt[u], 255.f);
+    } else {
+      for (int t0 = tlo; t0 <= thi; t0 += kB) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
-        if (t0 + u <= thi) shift_tab[t0 + u][tid] = (uint8_t)fminf(M - mt[u], 255.f);
+        for (int u = 0; u < kB; ++u) mt[u] = mh[(size_t)min(t0 + u, thi) * L + qc];
+#pragma unroll
+        for (int u = 0; u < kB; ++u)
+          if (t0 + u <= thi) shift_tab[t0 + u][tid] = (uint8_t)fminf(M - mt[u], 255.f);
+      }
     }
     inv_l[tid] = 1.f / l;
     // The row's softmax denominator is sum_j 2^(y_j) = 2^M l (y in log2 units).

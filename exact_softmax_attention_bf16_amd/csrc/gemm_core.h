@@ -33,12 +33,9 @@ __device__ __forceinline__ int kc_swz(int row) { return (row & 7) ^ ((row >> 3) 
 template <int NW>
 struct KContiguousT {
   static constexpr int kLoads = 32 / NW;
-  __amdgpu_buffer_rsrc_t r;
   uint32_t off[kLoads];
 
-  __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t rsrc, uint32_t ld, int r0, int wave,
-                                       int lane) {
-    r = rsrc;
+  __device__ __forceinline__ void init(uint32_t ld, int r0, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       const int P = (wave * kLoads + j) * 64 + lane;  // 16-byte chunk slot in the stage
@@ -46,12 +43,8 @@ struct KContiguousT {
       off[j] = ((uint32_t)(r0 + row) * ld + (uint32_t)(lc * 8)) * 2u;
     }
   }
-  // Rows [r0, r0 + 256) x columns [k0, k0 + 64) into `stage`.
-  __device__ __forceinline__ void issue(int k0, char* stage, int wave) const {
-    issue_from(r, k0, stage, wave);
-  }
-  // The same from another tensor of the same row stride (offsets as for r0 = 0
-  // when the resource starts at the tile's first row).
+  // Rows [r0, r0 + 256) x columns [k0, k0 + 64) of the tensor behind `rs` into
+  // `stage` (r0 = 0 when the resource starts at the tile's first row).
   __device__ __forceinline__ void issue_from(__amdgpu_buffer_rsrc_t rs, int k0, char* stage,
                                              int wave) const {
 #pragma unroll

@@ -301,8 +301,8 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
   static_assert(kLoads == 4, "one load per MFMA pair; the waits below count 4 loads");
 
   KContiguousT<kScoresWaves> la, lb;  // per-lane offsets within a tile; resources start at its first row
-  la.init(make_rsrc(k, 0), (uint32_t)ldk, 0, wave, lane);
-  lb.init(make_rsrc(q, 0), (uint32_t)ldq, 0, wave, lane);
+  la.init((uint32_t)ldk, 0, wave, lane);
+  lb.init((uint32_t)ldq, 0, wave, lane);
 
   // Load cursor: the step (tile li, K step lk) whose loads go out next.
   int li = 0, lk = 0;

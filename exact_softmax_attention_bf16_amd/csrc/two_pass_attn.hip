@@ -709,34 +709,46 @@ __global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  ValuesFrags cur, nxt;
-  {
-    unsigned s0[4];
-    sh.load(shift_tab, k_first >> 2, s0);
-    sh.set(s0);
-  }
-  read(cur, 0, 0);
+  // A wave whose 128 queries all lie past L (the far half of a head's last
+  // query tile when L mod 256 <= 128) only issues its loads and meets the
+  // barriers: its accumulators stay zero and none of its rows is stored.
+  if (__builtin_amdgcn_readfirstlane((int)(qt * kTile + qh * 128 >= L))) {
+    for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cur.b[j] = sh(cur.b[j], j);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 3;
-    // The shifts of step kt + 1 (past the end: unused), turned into shift
-    // words after this sub-step's MFMAs.
-    unsigned sn[4];
-    sh.load(shift_tab, min((k_first + kt + 1) >> 2, thi), sn);
-    // Sub-step 0, with the loads of step kt + 3.
-    read(nxt, st, 1);
-    mfma_pairs(cur, nxt, kt, true);
-    cur = nxt;
-    // Step kt + 1 staged everywhere (this wave's loads of steps kt + 2 and
-    // kt + 3 may still be in flight); stage st is read no more after this
-    // barrier (sub-step 1's fragments are in registers).
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    block_sync();
-    read(nxt, (kt + 1) & 3, 0);  // past the last step: unused
-    sh.set(sn);
-    mfma_pairs(cur, nxt, kt, false);
-    cur = nxt;
+      for (int p = 0; p < 4; ++p) issue(kt + 3, p);
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      block_sync();
+    }
+  } else {
+    ValuesFrags cur, nxt;
+    {
+      unsigned s0[4];
+      sh.load(shift_tab, k_first >> 2, s0);
+      sh.set(s0);
+    }
+    read(cur, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cur.b[j] = sh(cur.b[j], j);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & 3;
+      // The shifts of step kt + 1 (past the end: unused), turned into shift
+      // words after this sub-step's MFMAs.
+      unsigned sn[4];
+      sh.load(shift_tab, min((k_first + kt + 1) >> 2, thi), sn);
+      // Sub-step 0, with the loads of step kt + 3.
+      read(nxt, st, 1);
+      mfma_pairs(cur, nxt, kt, true);
+      cur = nxt;
+      // Step kt + 1 staged everywhere (this wave's loads of steps kt + 2 and
+      // kt + 3 may still be in flight); stage st is read no more after this
+      // barrier (sub-step 1's fragments are in registers).
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      block_sync();
+      read(nxt, (kt + 1) & 3, 0);  // past the last step: unused
+      sh.set(sn);
+      mfma_pairs(cur, nxt, kt, false);
+      cur = nxt;
+    }
   }
   // No load in flight into the stages (the O tile below reuses them).
   wait_vmem();

@@ -281,7 +281,8 @@ __device__ __forceinline__ void scores_epilogue(f32x16 (&acc)[4][kScoresNJ],
 // stage step s read).  So before that barrier it waits for everything but the
 // last four loads it issued (loads complete in order; a store issued between
 // them, such as the epilogue's, only makes the wait longer).
-// One LDS object (see the GEMM loop's notes on the compiler's LDS-DMA waits).
+// One LDS object, so that the compiler puts no wait for the direct loads in
+// flight before the fragment reads (gemm_core.h, header).
 __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, uint16_t* __restrict__ E,
     float* __restrict__ mref, float* __restrict__ psum, HeadMap hm, int L, int d, int T, int TK,

@@ -54,7 +54,9 @@ enum {
   ATTN_ERR_ALIAS = 6,                /* out overlaps q, k or v                    */
   ATTN_ERR_WORKSPACE = 7,            /* the stream-ordered workspace allocation failed */
   ATTN_ERR_HIP = 8,                  /* a HIP launch or runtime call failed       */
-  ATTN_ERR_TOO_LARGE = 9,            /* one head exceeds the kernels' 32-bit byte offsets */
+  ATTN_ERR_TOO_LARGE = 9,            /* one head exceeds the kernels' 32-bit byte offsets,
+                                        or L > 15872 with d > 128 (the values pass keeps a
+                                        byte per 128 keys and query of its tile in LDS) */
   ATTN_ERR_BAD_STRIDE = 10,          /* attn_forward_ex: a stride is negative or not a multiple
                                         of 8, a row stride is below d, or out's elements overlap */
   ATTN_ERR_BAD_MASK = 11,            /* attn_forward_varlen: the compressed causal mask

@@ -63,8 +63,8 @@ struct KContiguousT {
 };
 
 // Operand A stored with K as the outer index (A[m][k] at k * ld + m), e.g. V read
-// as the A operand of O^T = V^T E^T.  Its stage holds K rows of 256 m values
-// (512 bytes per row, 16-byte chunk c at c ^ 4 (row % 4)).  Stage row r holds K
+// as the A operand of O^T = V^T E^T.  Its stage holds K rows of 256 or 128 m
+// values (512 or 256 bytes per row, 16-byte chunk c at c ^ 4 (row % 4)).  Stage row r holds K
 // row k0 + kperm(r), kperm exchanging bits 2 and 3 of the index: the order the
 // scores pass gives the keys of each 32-key block of E, so that the B operand
 // (E, K-contiguous) and this one agree.  Fragments are built with two
@@ -73,7 +73,10 @@ struct KContiguousT {
 // of column m0 + i.
 __device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
-struct KOuter {
+// PITCH: bytes per stage row.  In either width the 32 lanes of a half-wave
+// read 4 rows x 4 chunks that the swizzle puts on distinct banks.
+template <int PITCH>
+struct KOuterT {
   // Sub-step ss (K rows 16 ss .. 16 ss + 15 of the stage), columns mbase ..
   // mbase + 31.
   __device__ __forceinline__ bf16x8 frag(const char* stage, int mbase, int ss, int lane) const {
@@ -81,7 +84,7 @@ struct KOuter {
     const int m = mbase + (g & 1) * 16 + 4 * (L & 3);
     const int row = 16 * ss + 8 * (g >> 1) + (L >> 2);
     auto at = [&](int rr) {
-      return (short4_lds*)(stage + rr * 512 + (((m >> 3) ^ ((rr & 3) << 2)) << 4) + (m & 7) * 2);
+      return (short4_lds*)(stage + rr * PITCH + (((m >> 3) ^ ((rr & 3) << 2)) << 4) + (m & 7) * 2);
     };
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(row));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(row + 4));
@@ -89,6 +92,7 @@ struct KOuter {
     return __builtin_bit_cast(bf16x8, v);
   }
 };
+using KOuter = KOuterT<512>;
 
 struct NoTransform {
   __device__ __forceinline__ void step(int, bool) {}

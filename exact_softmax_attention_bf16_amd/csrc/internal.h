@@ -163,8 +163,13 @@ hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, flo
 constexpr int kValuesTargetWorkgroups = 256;  // MI355X compute units
 constexpr int kValuesMaxSplit = 4;
 constexpr int kValuesMinSplitSteps = 8;  // K steps (64 keys each) per split at least
+// Whether the values pass runs on 128 x 128 tiles (no split): when the
+// 256 x 256 grid would leave at least half of the compute units idle and the
+// narrow grid fits on them in one round.  Depends on the shape only.
+bool values_narrow(int64_t BH, const TwoPassDims& t);
 // Splits used for BH heads: 1 unless the unsplit grid would leave at least half
-// of the compute units idle.  Depends on the shape only.
+// of the compute units idle and the narrow tiles do not apply.  Depends on the
+// shape only.
 int values_split(int64_t BH, const TwoPassDims& t, const Band& band);
 // lse as for launch_online.
 hipError_t launch_values(const void* v, const void* E, const float* mref, const float* psum,

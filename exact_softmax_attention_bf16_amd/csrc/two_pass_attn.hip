@@ -446,19 +446,22 @@ __global__ __launch_bounds__(64 * kScoresWaves) void scores_kernel(
 // shift for those queries.
 constexpr int kMaxTiles = kTwoPassMaxTiles;
 
+// NQ: query columns per lane (one per 32-query block of the wave).
+template <int NQ>
 struct PowerOfTwoShift {
-  int col[4];      // this lane's four query columns in the tile
-  unsigned sw[4];  // shift words (s << 7 | s << 23) of the current 128-key tile
+  int col[NQ];      // this lane's query columns in the tile
+  unsigned sw[NQ];  // shift words (s << 7 | s << 23) of the current 128-key tile
 
   // The shifts of 128-key tile t (from [t][query in tile]: M - m_t), and the
   // shift words made from them.
-  __device__ __forceinline__ void load(const uint8_t (*tab)[kTile], int t, unsigned (&s)[4]) const {
+  template <int QT>
+  __device__ __forceinline__ void load(const uint8_t (*tab)[QT], int t, unsigned (&s)[NQ]) const {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s[j] = tab[t][col[j]];
+    for (int j = 0; j < NQ; ++j) s[j] = tab[t][col[j]];
   }
-  __device__ __forceinline__ void set(const unsigned (&s)[4]) {
+  __device__ __forceinline__ void set(const unsigned (&s)[NQ]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sw[j] = (s[j] << 7) | (s[j] << 23);
+    for (int j = 0; j < NQ; ++j) sw[j] = (s[j] << 7) | (s[j] << 23);
   }
   __device__ __forceinline__ bf16x8 operator()(bf16x8 f, int j) const {
     u32x4 w = __builtin_bit_cast(u32x4, f);
@@ -467,6 +470,66 @@ struct PowerOfTwoShift {
     return __builtin_bit_cast(bf16x8, w);
   }
 };
+
+// The statistics of query q0 + tid of head bh over score tiles [tlo, thi]:
+// M = max_t m_t, l = sum_t 2^(m_t - M) psum_t, the shift M - m_t of each tile
+// (a nonnegative integer; -inf tiles -> 255) into shift_tab[t][tid], 1/l into
+// inv_l[tid], and when write_lse the log-sum-exp into lse.
+// The stats of up to 32 tiles are read at once, so that their latencies
+// overlap and, for query tiles that meet at most 32 score tiles (L <= 4096
+// without a band), the shifts come from the same registers: one round of
+// loads instead of four (batches of 16 and a second pass).
+template <int QT>
+__device__ __forceinline__ void values_stats(const float* __restrict__ mref,
+                                             const float* __restrict__ psum,
+                                             float* __restrict__ lse, bool write_lse, int bh,
+                                             int bh0, int TK, int L, int q0, int tlo, int thi,
+                                             uint8_t (*shift_tab)[QT], float* inv_l, int tid) {
+  const float* mh = mref + (size_t)bh * TK * L;
+  const float* ph = psum + (size_t)bh * TK * L;
+  const int qc = min(q0 + tid, L - 1);
+  constexpr int kB = 32;
+  float M = -INFINITY, l = 0.f;
+  float mt[kB];
+  for (int t0 = tlo; t0 <= thi; t0 += kB) {
+    float pt[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int t = min(t0 + u, thi);
+      mt[u] = mh[(size_t)t * L + qc];
+      pt[u] = ph[(size_t)t * L + qc];
+    }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < kB; ++u) Mn = fmaxf(Mn, mt[u]);
+    l = M == -INFINITY ? 0.f : l * exp2_fast(M - Mn);
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      if (t0 + u <= thi && mt[u] != -INFINITY) l += pt[u] * exp2_fast(mt[u] - Mn);
+    M = Mn;
+  }
+  // The shifts need the final M: from the registers when one batch held
+  // every tile, else a second pass over the (now cached) stats.
+  if (thi - tlo < kB) {
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      if (tlo + u <= thi) shift_tab[tlo + u][tid] = (uint8_t)fminf(M - mt[u], 255.f);
+  } else {
+    // Every load is consumed (entries past thi rewrite thi's), so that none
+    // is left in flight for the compiler to wait on later.
+    for (int t0 = tlo; t0 <= thi; t0 += kB) {
+#pragma unroll
+      for (int u = 0; u < kB; ++u) mt[u] = mh[(size_t)min(t0 + u, thi) * L + qc];
+#pragma unroll
+      for (int u = 0; u < kB; ++u) shift_tab[min(t0 + u, thi)][tid] = (uint8_t)fminf(M - mt[u], 255.f);
+    }
+  }
+  inv_l[tid] = 1.f / l;
+  // The row's softmax denominator is sum_j 2^(y_j) = 2^M l (y in log2 units).
+  const int query = q0 + tid;
+  if (lse != nullptr && write_lse && query < L)
+    lse[(size_t)(bh0 + bh) * L + query] = (M + log2f(l)) * 0.6931471805599453f;
+}
 
 // The values pass walks the keys in steps of 32 through four LDS stages of
 // 32 KB (V 16 KB, E 16 KB): the loads of step kt + 3 go out during step kt,
@@ -605,63 +668,16 @@ __global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_
 #pragma unroll
     for (int j = 0; j < 4; ++j) issue(u, j);
 
-  // Thread tid < 256 owns query qt*256 + tid: M = max_t m_t, l = sum_t 2^(m_t - M) psum_t,
-  // and the shift M - m_t of each tile (a nonnegative integer; -inf tiles -> 255).
-  // The stats of up to 32 tiles are read at once, so that their latencies
-  // overlap and, for query tiles that meet at most 32 score tiles (L <= 4096
-  // without a band), the shifts come from the same registers: one round of
-  // loads instead of four (batches of 16 and a second pass).
-  if (tid < kTile) {
-    const float* mh = mref + (size_t)bh * TK * L;
-    const float* ph = psum + (size_t)bh * TK * L;
-    const int qc = min(qt * kTile + tid, L - 1);
-    constexpr int kB = 32;
-    float M = -INFINITY, l = 0.f;
-    float mt[kB];
-    for (int t0 = tlo; t0 <= thi; t0 += kB) {
-      float pt[kB];
-#pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        const int t = min(t0 + u, thi);
-        mt[u] = mh[(size_t)t * L + qc];
-        pt[u] = ph[(size_t)t * L + qc];
-      }
-      float Mn = M;
-#pragma unroll
-      for (int u = 0; u < kB; ++u) Mn = fmaxf(Mn, mt[u]);
-      l = M == -INFINITY ? 0.f : l * exp2_fast(M - Mn);
-#pragma unroll
-      for (int u = 0; u < kB; ++u)
-        if (t0 + u <= thi && mt[u] != -INFINITY) l += pt[u] * exp2_fast(mt[u] - Mn);
-      M = Mn;
-    }
-    // The shifts need the final M: from the registers when one batch held
-    // every tile, else a second pass over the (now cached) stats.
-    if (thi - tlo < kB) {
-#pragma unroll
-      for (int u = 0; u < kB; ++u)
-        if (tlo + u <= thi) shift_tab[tlo + u][tid] = (uint8_t)fminf(M - mt[u], 255.f);
-    } else {
-      for (int t0 = tlo; t0 <= thi; t0 += kB) {
-#pragma unroll
-        for (int u = 0; u < kB; ++u) mt[u] = mh[(size_t)min(t0 + u, thi) * L + qc];
-#pragma unroll
-        for (int u = 0; u < kB; ++u)
-          if (t0 + u <= thi) shift_tab[t0 + u][tid] = (uint8_t)fminf(M - mt[u], 255.f);
-      }
-    }
-    inv_l[tid] = 1.f / l;
-    // The row's softmax denominator is sum_j 2^(y_j) = 2^M l (y in log2 units).
-    const int query = qt * kTile + tid;
-    if (lse != nullptr && ct == 0 && sp == 0 && query < L)
-      lse[(size_t)(hm.bh0 + bh) * L + query] = (M + log2f(l)) * 0.6931471805599453f;
-  }
+  // Thread tid < 256 owns query qt*256 + tid.
+  if (tid < kTile)
+    values_stats<kTile>(mref, psum, lse, ct == 0 && sp == 0, bh, hm.bh0, TK, L, qt * kTile, tlo,
+                        thi, shift_tab, inv_l, tid);
   // Step 0 staged (only steps 1 and 2 may be in flight); the shift table and
   // 1/l complete.
   asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   block_sync();
 
-  PowerOfTwoShift sh;
+  PowerOfTwoShift<4> sh;
   float invl[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -820,6 +836,253 @@ __global__ __launch_bounds__(64 * kValuesWaves) void values_kernel(const uint16_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Values pass on 128 x 128 tiles, for calls whose 256 x 256 tiles would fill
+// at most half of the compute units (one head at L = 3432: 56 of them against
+// 216 narrow ones).  It needs no key split, so no fp32 partial outputs and no
+// reduction pass.  Tile (ct, qt): channels [128 ct, +128) on the M side,
+// queries [128 qt, +128) on the N side, keys in steps of 64 through four LDS
+// stages of 32 KB (V 16 KB, E 16 KB); the loads of step kt + 3 go out during
+// step kt, as in the wide kernel.
+constexpr int kNT = 128;                     // narrow tile edge
+constexpr int kNK = 64;                      // keys per step
+constexpr int kNStages = 4;
+constexpr int kNStageBytes = kNK * kNT * 2;  // per operand
+
+struct alignas(16) NarrowSmem {
+  char v[kNStages][kNStageBytes];  // V rows [64 keys][128 channels], 256 bytes each
+  char e[kNStages][kNStageBytes];  // E blocks [4 query blocks][4 key blocks]
+  uint8_t shift_tab[kMaxTiles][kNT];
+  float inv_l[kNT];
+};
+static_assert(sizeof(NarrowSmem) <= 160 * 1024, "a CU's LDS");
+
+// V rows as V^T: 64 key rows x 128 channels per stage, 16-byte chunk c of row
+// r at c ^ 4 (r % 4), stage row r holding key k0 + kperm(r) (as in ValuesV).
+// Each of the 8 waves issues 2 of the 16 loads of 1 KB.
+struct NarrowV {
+  uint32_t off[2];
+  uint32_t ld2;  // bytes per key row
+  __device__ __forceinline__ void init(uint32_t ld, int m0, int wave, int lane) {
+    ld2 = ld * 2u;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int P = (wave * 2 + j) * 64 + lane;  // 16-byte chunk slot in the stage
+      const int row = P >> 4, pc = P & 15, lc = pc ^ ((row & 3) << 2);
+      off[j] = (uint32_t)kperm(row) * ld2 + (uint32_t)(m0 + lc * 8) * 2u;
+    }
+  }
+  __device__ __forceinline__ void issue(const u32x4& r, int k0, char* stage, int wave, int j) const {
+    load16_to_lds_untracked(r, stage + (wave * 2 + j) * 1024, off[j] + (uint32_t)k0 * ld2);
+  }
+};
+// E: the 4 x 4 blocks of 32 queries x 16 keys a step covers, block (i, j) at
+// 1 KB x (4 i + j); wave w copies query block w / 2, key blocks 2 (w % 2) and
+// 2 (w % 2) + 1 of the step.
+struct NarrowE {
+  uint32_t off;
+  int kb0;  // first key block of this wave within a step
+  __device__ __forceinline__ void init(int EB, int wave, int lane) {
+    off = (uint32_t)(wave >> 1) * (uint32_t)EB * 1024u + (uint32_t)lane * 16u;
+    kb0 = 2 * (wave & 1);
+  }
+  __device__ __forceinline__ void issue(const u32x4& r, int k0, char* stage, int wave, int j) const {
+    load16_to_lds_untracked(r, stage + (wave * 2 + j) * 1024,
+                            off + (uint32_t)((k0 >> 4) + kb0 + j) * 1024u);
+  }
+};
+
+struct NarrowFrags {
+  bf16x8 a, b[2];
+};
+
+// 8 waves, two per SIMD: wave w owns channels [32 (w % 4), +32) x queries
+// [64 (w / 4), +64) of the tile, as 1 x 2 accumulator blocks.  Per k16
+// sub-step it reads one V^T fragment (two transpose reads) and two E
+// fragments for 2 MFMAs, two sub-steps ahead (one sub-step's 128 cycles of
+// MFMAs per SIMD do not cover an LDS read).  Step kt (64 keys, four
+// sub-steps): the loads of step kt + 3 go out one per MFMA in the first two
+// sub-steps, whose reads finish the stage; the wave then waits for its loads
+// of step kt + 1 and meets the others at the barrier, and runs the last two
+// sub-steps' MFMAs while it reads the first two of step kt + 1.
+__global__ __launch_bounds__(64 * kValuesWaves) void values_narrow_kernel(
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ E, const float* __restrict__ mref,
+    const float* __restrict__ psum, uint16_t* __restrict__ out, float* __restrict__ lse,
+    HeadMap hm, int L, int d, int T2, int TK, int QB, int EB, int Lk, Band band, int ncb2) {
+  __shared__ NarrowSmem sm;
+
+  const uint32_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int per_head = T2 * ncb2;
+  const int bh = lid / per_head;
+  const int r = lid % per_head;
+  const int qt = r / ncb2, ct = r % ncb2;  // a query tile's channel tiles are neighbours (one XCD)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cq = wave & 3, qh = wave >> 2, c32 = lane & 31, h = lane >> 5;
+
+  // Score tiles [tlo, thi] (128 keys each) meet this query tile's band: keys
+  // [kbeg, kend), a whole number of steps (Lk is a multiple of 64), at least
+  // one (the tile holds a query below L, whose band keeps its diagonal).
+  int tlo, thi;
+  band_tiles(band, qt, kNT, TK, kSK, &tlo, &thi);
+  const int kbeg = tlo * kSK, kend = min(Lk, (thi + 1) * kSK);
+  const int nk = (kend - kbeg) / kNK;
+  const int k_first = kbeg / kNK;
+
+  const int ldv = hm.v.ld;
+  const u32x4 rv = rsrc_words(v + hm.v_off(bh), ((uint32_t)(L - 1) * ldv + d) * 2u);
+  const u32x4 re = rsrc_words(E + ((size_t)bh * QB + (size_t)qt * 4) * EB * 512,
+                              (uint32_t)(QB - qt * 4) * (uint32_t)EB * 1024u);
+  NarrowV la;
+  NarrowE lb;
+  la.init((uint32_t)ldv, ct * kNT, wave, lane);
+  lb.init(EB, wave, lane);
+  // Load j (0..3) of step u; steps past the last reload the last.
+  auto issue = [&](int u, int j) {
+    const int k0 = kbeg + min(u, nk - 1) * kNK;
+    if (j < 2)
+      la.issue(rv, k0, sm.v[u & 3], wave, j);
+    else
+      lb.issue(re, k0, sm.e[u & 3], wave, j - 2);
+  };
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) issue(u, j);
+
+  // Thread tid < 128 owns query qt*128 + tid.
+  if (tid < kNT)
+    values_stats<kNT>(mref, psum, lse, ct == 0, bh, hm.bh0, TK, L, qt * kNT, tlo, thi,
+                      sm.shift_tab, sm.inv_l, tid);
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  block_sync();
+
+  PowerOfTwoShift<2> sh;
+  float invl[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    sh.col[j] = qh * 64 + j * 32 + c32;
+    invl[j] = sm.inv_l[sh.col[j]];
+  }
+  KOuterT<kNT * 2> ka;
+  auto read = [&](NarrowFrags& f, int st, int ss) {
+    f.a = ka.frag(sm.v[st], cq * 32, ss, lane);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      f.b[j] = *(const bf16x8*)(sm.e[st] + ((qh * 2 + j) * 4 + ss) * 1024 + lane * 16);
+  };
+  // E fragments are scaled once read (the empty asm keeps the compiler from
+  // sinking the scaling to their first use after the barrier).
+  auto scale = [&](NarrowFrags& f) {
+    f.b[0] = sh(f.b[0], 0);
+    f.b[1] = sh(f.b[1], 1);
+    asm volatile("" : "+v"(f.b[0]), "+v"(f.b[1]));
+  };
+
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  // A wave whose 64 queries all lie past L only issues its loads and meets
+  // the barriers.
+  if (__builtin_amdgcn_readfirstlane((int)(qt * kNT + qh * 64 >= L))) {
+    for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) issue(kt + 3, p);
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      block_sync();
+    }
+  } else {
+    // f0: this sub-step's fragments (scaled), f1: the next (read, to be
+    // scaled), f2: the one after (being read).
+    NarrowFrags f0, f1, f2;
+    auto mfmas = [&](const NarrowFrags& f, int kt, int ss) {
+      __builtin_amdgcn_sched_barrier(0);
+      acc[0] = mfma32x32x16(f.a, f.b[0], acc[0]);
+      if (ss < 2) issue(kt + 3, 2 * ss);
+      acc[1] = mfma32x32x16(f.a, f.b[1], acc[1]);
+      if (ss < 2) issue(kt + 3, 2 * ss + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    {
+      unsigned s0[2];
+      sh.load(sm.shift_tab, k_first >> 1, s0);
+      sh.set(s0);
+    }
+    read(f0, 0, 0);
+    read(f1, 0, 1);
+    scale(f0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & 3;
+      unsigned sn[2];  // shifts of step kt + 1 (past the end: unused)
+      sh.load(sm.shift_tab, min((k_first + kt + 1) >> 1, thi), sn);
+      // Sub-steps 0 and 1, each with two loads of step kt + 3.
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+        read(f2, st, ss + 2);
+        mfmas(f0, kt, ss);
+        scale(f1);
+        f0 = f1;
+        f1 = f2;
+      }
+      // Step kt + 1 staged everywhere (steps kt + 2 and kt + 3 may be in
+      // flight); every read of stage st issued (and done at the barrier).
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      block_sync();
+      // Sub-steps 2 and 3, reading the first two of step kt + 1.
+      read(f2, (kt + 1) & 3, 0);
+      mfmas(f0, kt, 2);
+      scale(f1);  // sub-step 3: this step's shifts
+      sh.set(sn);
+      f0 = f1;
+      f1 = f2;
+      read(f2, (kt + 1) & 3, 1);
+      mfmas(f0, kt, 3);
+      scale(f1);  // step kt + 1, sub-step 0
+      f0 = f1;
+      f1 = f2;
+    }
+  }
+  // No load in flight into the stages (the O tile below reuses them).
+  wait_vmem();
+  block_sync();
+
+  // O[query][ch] = acc / l, rounded once to bf16, staged as [query][128
+  // channels] rows of 256 bytes (chunk c of row r at c ^ (r % 16), 8-byte
+  // halves swapped when r % 32 >= 16) so that the stores write whole rows.
+  static_assert(offsetof(NarrowSmem, e) == kNStages * kNStageBytes &&
+                    kNStages * kNStageBytes >= kNT * kNT * 2,
+                "the O tile fits the V stages");
+  char* stage = sm.v[0];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int ql = qh * 64 + j * 32 + c32;
+    char* row = stage + ql * 256 + 8 * (h ^ (c32 >> 4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x16& a = acc[j];
+      const u32x2 w = {pack_bf16x2(a[4 * i] * invl[j], a[4 * i + 1] * invl[j]),
+                       pack_bf16x2(a[4 * i + 2] * invl[j], a[4 * i + 3] * invl[j])};
+      const int chunk = cq * 4 + i;
+      *(u32x2*)(row + ((chunk ^ (c32 & 15)) << 4)) = w;
+    }
+  }
+  __syncthreads();
+  {
+    const int c = tid & 15;
+    const int ch = ct * kNT + 8 * c;
+    if (ch < d) {
+      const int ldo = hm.o.ld;
+      uint16_t* oh = out + hm.o_off(bh) + (size_t)(qt * kNT) * ldo + ch;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = (tid >> 4) + 32 * j;
+        if (qt * kNT + rr < L)
+          *(u32x4*)(oh + (size_t)rr * ldo) =
+              unswap_halves(*(const u32x4*)(stage + rr * 256 + ((c ^ (rr & 15)) << 4)), rr);
+      }
+    }
+  }
+}
+
 // out = bf16(sum over the splits of part), 8 elements per thread.  part is
 // [split][head][L][d] contiguous; out is addressed through the head map.
 __global__ __launch_bounds__(256) void values_reduce_kernel(const float* __restrict__ part,
@@ -890,9 +1153,15 @@ hipError_t launch_scores(const void* q, const void* k, void* E, float* mref, flo
                          dim3(64 * kScoresWaves), args, 0, s);
 }
 
+bool values_narrow(int64_t BH, const TwoPassDims& t) {
+  const int64_t wide = BH * t.T * ((t.d + kTile - 1) / kTile);
+  const int64_t narrow = BH * ((t.L + kNT - 1) / kNT) * ((t.d + kNT - 1) / kNT);
+  return wide * 2 <= kValuesTargetWorkgroups && narrow <= kValuesTargetWorkgroups;
+}
+
 int values_split(int64_t BH, const TwoPassDims& t, const Band& band) {
   const int64_t base = BH * t.T * ((t.d + kTile - 1) / kTile);  // workgroups without a split
-  if (base * 2 > kValuesTargetWorkgroups) return 1;
+  if (base * 2 > kValuesTargetWorkgroups || values_narrow(BH, t)) return 1;
   int64_t fewest = t.Lk / kStepK;  // K steps of the narrowest query tile's band
   for (int qt = 0; qt < t.T; ++qt) {
     int lo, hi;
@@ -919,6 +1188,13 @@ hipError_t launch_values(const void* v, const void* E, const float* mref, const 
   Band b = band;
   void* args[] = {&vtp, &ep, &mref, &psum, &op, &lse, &part, &m, &L, &d, &T, &TK, &QB, &EB, &Lk, &b,
                   &ncb, &split, &nheads};
+  if (split == 1 && values_narrow(BH, t)) {
+    int T2 = (t.L + kNT - 1) / kNT, ncb2 = (t.d + kNT - 1) / kNT;
+    void* nargs[] = {&vtp, &ep, &mref, &psum, &op, &lse, &m, &L, &d, &T2, &TK, &QB, &EB, &Lk, &b,
+                     &ncb2};
+    return hipLaunchKernel((const void*)&values_narrow_kernel, dim3((unsigned)(BH * T2 * ncb2)),
+                           dim3(64 * kValuesWaves), nargs, 0, s);
+  }
   const void* kern = split > 1 ? (const void*)&values_kernel<true> : (const void*)&values_kernel<false>;
   return hipLaunchKernel(kern, dim3((unsigned)(BH * T * ncb * split)), dim3(64 * kValuesWaves), args,
                          0, s);

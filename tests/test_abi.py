@@ -72,19 +72,41 @@ def test_path_for_head_dim(d, path):
     assert eab.path_for_head_dim(d) == path
 
 
+def _values_narrow(n, L, d):
+    """The values pass runs on 128 x 128 tiles when its 256 x 256 grid
+    (n * T * ceil(d/256) workgroups) would fill at most half of 256 CUs and the
+    narrow grid (n * ceil(L/128) * ceil(d/128)) fits on them in one round."""
+    base = n * -(-L // 256) * -(-d // 256)
+    return 2 * base <= 256 and n * -(-L // 128) * -(-d // 128) <= 256
+
+
 def _values_split(n, L, d, causal):
     """Key splits of the values pass for n heads: 1 unless the unsplit grid
-    (n * T * ceil(d/256) workgroups) would fill at most half of 256 CUs; then as
+    would fill at most half of 256 CUs and the narrow tiles do not apply; then as
     many as fit in 256, at most 4, with at least 8 K steps (64 keys) per split in
     the query tile with the fewest; below 2, no split."""
     T = -(-L // 256)
     base = n * T * (-(-d // 256))
-    if 2 * base > 256:
+    if 2 * base > 256 or _values_narrow(n, L, d):
         return 1
     steps = -(-L // 64)
     fewest = min(4, steps) if causal else steps
     s = min(256 // base, 4, fewest // 8)
     return s if s >= 2 else 1
+
+
+def test_values_tiles_choice():
+    # one frame of 3432 x 1024: 56 wide tiles, 216 narrow ones -> narrow, no split
+    assert _values_narrow(1, 3432, 1024) and _values_split(1, 3432, 1024, False) == 1
+    # two frames: 112 wide tiles, 432 narrow ones -> wide, two splits
+    assert not _values_narrow(2, 3432, 1024) and _values_split(2, 3432, 1024, False) == 2
+    # 4096 x 1024: exactly 256 narrow tiles
+    assert _values_narrow(1, 4096, 1024)
+    assert not _values_narrow(1, 4097, 1024) and _values_split(1, 4097, 1024, False) == 3
+    # 12 heads of 2048 x 256 (96 wide, 384 narrow) -> 2 splits; 10 of 1600 x 256 -> 3
+    assert _values_split(12, 2048, 256, False) == 2 and _values_split(10, 1600, 256, False) == 3
+    # enough heads: neither
+    assert not _values_narrow(31, 3432, 1024) and _values_split(31, 3432, 1024, False) == 1
 
 
 def test_workspace_bytes():
@@ -96,23 +118,24 @@ def test_workspace_bytes():
     r = lambda x: (x + 255) // 256 * 256
     e_bytes = lambda n: ((n + 31) // 32) * 16 * ((n + 255) // 256) * 1024  # noqa: E731
     per_head = r(e_bytes(L)) + 2 * r(TK * L * 4)
-    assert _values_split(1, L, d, False) == 4 and _values_split(31, L, d, False) == 1
-    assert _values_split(4, L, d, False) == 1
-    assert eab.workspace_bytes(1, 1, L, d) == per_head + r(4 * L * d * 4)
+    assert eab.workspace_bytes(1, 1, L, d) == per_head  # narrow tiles: no partials
+    assert eab.workspace_bytes(2, 1, L, d) == 2 * per_head + r(2 * 2 * L * d * 4)
     assert eab.workspace_bytes(4, 1, L, d) == 4 * per_head
     assert eab.workspace_bytes(31, 1, L, d) == 31 * per_head
-    # tiny: L = 286, d = 256: 5 K steps -> too short to split
+    # tiny: L = 286, d = 256
     Lt, dt = 286, 256
     pt = r(e_bytes(Lt)) + 2 * r(3 * Lt * 4)
     assert _values_split(1, Lt, dt, False) == 1
     assert eab.workspace_bytes(1, 1, Lt, dt) == pt
-    # causal: the first query tile has 4 K steps -> no split
-    assert _values_split(1, 3432, 1024, True) == 1
     assert eab.workspace_bytes(1, 1, 3432, 1024, True) == per_head
-    # L = 1100, d = 256: base 5, 18 K steps -> 2 splits
-    assert _values_split(1, 1100, 256, False) == 2
-    assert eab.workspace_bytes(1, 1, 1100, 256) == (
-        r(e_bytes(1100)) + 2 * r(9 * 1100 * 4) + r(2 * 1100 * 256 * 4))
+    # one head of L = 4097, d = 1024: 264 narrow tiles -> 3 splits of the 68 wide ones
+    L4 = 4097
+    T4, TK4 = 17, 33
+    p4 = r(((L4 + 31) // 32) * 16 * T4 * 1024) + 2 * r(TK4 * L4 * 4)
+    assert eab.workspace_bytes(1, 1, L4, 1024) == p4 + r(3 * L4 * 1024 * 4)
+    # 12 heads of L = 2048, d = 256: 2 splits
+    p12 = r(e_bytes(2048)) + 2 * r(16 * 2048 * 4)
+    assert eab.workspace_bytes(12, 1, 2048, 256) == 12 * p12 + r(2 * 12 * 2048 * 256 * 4)
     assert eab.workspace_bytes(4, 8, 1024, 64) == 0       # online path, 256 workgroups: none
     assert eab.workspace_bytes(0, 1, L, d) == 0
     big = eab.workspace_bytes(1000, 1, L, d)              # chunked under ~2 GiB

@@ -154,24 +154,26 @@ def test_lse_scale_zero_is_log_count():
     assert ok, err
 
 
-@pytest.mark.parametrize("L,d", [(1100, 256), (2100, 512)])
-def test_key_split_with_strided_out_and_lse(L, d):
-    """One head: the values pass splits its keys; the reduction writes a strided
-    out (row stride 2d) and the first split writes the LSE."""
+@pytest.mark.parametrize("B,L,d,split", [(1, 1100, 256, False), (1, 2100, 512, False),
+                                         (12, 2048, 256, True), (10, 1600, 256, True)])
+def test_few_heads_with_strided_out_and_lse(B, L, d, split):
+    """Few heads: the values pass either runs on 128 x 128 tiles (one head) or
+    splits its keys, whose reduction then writes the strided out (row stride
+    2d) while the first split writes the LSE."""
     from exact_softmax_attention_bf16_amd import attention, kernel_timing
-    q, k, v = make_qkv(1, 1, L, d, 160 + L)
+    q, k, v = make_qkv(B, 1, L, d, 160 + L)
     s = 1.0 / math.sqrt(d)
-    big = torch.full((1, 1, L, 2 * d), 7.0, dtype=torch.bfloat16, device=DEV)
+    big = torch.full((B, 1, L, 2 * d), 7.0, dtype=torch.bfloat16, device=DEV)
     out = big[..., :d]
     res = {}
     with kernel_timing(res):
         o, lse = attention(q.to(DEV), k.to(DEV), v.to(DEV), scale=s, out=out, return_lse=True)
     torch.cuda.synchronize()
-    assert "values_reduce" in res
+    assert ("values_reduce" in res) == split
     assert bool((big[..., d:] == 7.0).all())  # the gaps between rows are untouched
     ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), s, False)
     ok, a, r = within_bar(to_f64(o), ref)
-    _report(f"split + strided out L={L} d={d}", a, r)
+    _report(f"few heads + strided out B={B} L={L} d={d}", a, r)
     assert ok, (a, r)
     ok, err = lse_ok(lse, oracle.log_sum_exp(to_f64(q), to_f64(k), s, False))
     assert ok, err
@@ -242,18 +244,25 @@ def test_window_limits_equal_unwindowed_and_causal_bitwise(d):
     assert torch.equal(left_only, causal)
 
 
-@pytest.mark.parametrize("L,d,window", [(2100, 512, (300, 200)), (1100, 256, (None, 0)),
-                                        (1500, 256, (600, None))])
-def test_window_with_key_split(L, d, window):
-    """One head: the values pass splits each query tile's band among workgroups."""
-    from exact_softmax_attention_bf16_amd import attention
-    q, k, v = make_qkv(1, 1, L, d, 192 + L)
+@pytest.mark.parametrize("B,L,d,window,split", [(1, 2100, 512, (300, 200), False),
+                                                 (1, 1100, 256, (None, 0), False),
+                                                 (1, 1500, 256, (600, None), False),
+                                                 (12, 2048, 256, (1200, 1200), True),
+                                                 (10, 1600, 256, (900, None), True)])
+def test_window_with_few_heads(B, L, d, window, split):
+    """Few heads: each query tile's band on the 128 x 128 tiles, or divided
+    among the workgroups of a key split."""
+    from exact_softmax_attention_bf16_amd import attention, kernel_timing
+    q, k, v = make_qkv(B, 1, L, d, 192 + L)
     s = 1.0 / math.sqrt(d)
-    o, lse = attention(q.to(DEV), k.to(DEV), v.to(DEV), scale=s, window=window, return_lse=True)
+    res = {}
+    with kernel_timing(res):
+        o, lse = attention(q.to(DEV), k.to(DEV), v.to(DEV), scale=s, window=window, return_lse=True)
     torch.cuda.synchronize()
+    assert ("values_reduce" in res) == split
     ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), s, False, window)
     ok, a, r = within_bar(to_f64(o), ref)
-    _report(f"split window {window} L={L} d={d}", a, r)
+    _report(f"few heads window {window} B={B} L={L} d={d}", a, r)
     assert ok, (a, r)
     ok, err = lse_ok(lse, oracle.log_sum_exp(to_f64(q), to_f64(k), s, False, window))
     assert ok, err

@@ -142,12 +142,12 @@ def test_empty_problem():
 
 def test_kernel_timing_records_each_kernel():
     from exact_softmax_attention_bf16_amd import attention, kernel_timing
-    q, k, v = (t.cuda() for t in make_qkv(1, 1, 1100, 1024, 14))
+    q, k, v = (t.cuda() for t in make_qkv(12, 1, 2048, 256, 14))
     res = {}
     with kernel_timing(res):
         attention(q, k, v)
         attention(q, k, v)
-    # one head of L=1100, d=1024 leaves most CUs idle: the values pass splits its keys
+    # 12 heads of L=2048, d=256: 96 wide tiles, 384 narrow ones; the values pass splits its keys
     assert set(res) == {"scores", "values", "values_reduce"}
     assert all(c == 2 and ms > 0 for ms, c in res.values())
 
@@ -161,18 +161,50 @@ def test_kernel_timing_without_split():
     assert set(res) == {"scores", "values"}
 
 
-@pytest.mark.parametrize("L,d,splits", [(1100, 256, 2), (1500, 256, 3), (2100, 512, 4),
-                                         (2100, 512, 1)])
-def test_values_key_split(L, d, splits):
-    """Few heads: the values pass divides the keys among 2-4 workgroups and sums
-    their fp32 shares (splits == 1: the same shape with enough heads not to)."""
-    B = 1 if splits > 1 else 32
+@pytest.mark.parametrize("B,L,d,splits", [(12, 2048, 256, 2), (10, 1600, 256, 3),
+                                           (32, 2100, 512, 1)])
+def test_values_key_split(B, L, d, splits):
+    """Heads too few for the 256 x 256 grid and too many for one round of
+    128 x 128 tiles: the values pass divides the keys among 2-3 workgroups and
+    sums their fp32 shares (splits == 1: enough heads not to)."""
+    from exact_softmax_attention_bf16_amd import attention, kernel_timing
     q, k, v = make_qkv(B, 1, L, d, 30 + splits)
-    o = run_gpu(q, k, v, 1.0 / math.sqrt(d), False)
-    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), 1.0 / math.sqrt(d), False)
+    s = 1.0 / math.sqrt(d)
+    res = {}
+    with kernel_timing(res):
+        o = attention(q.cuda(), k.cuda(), v.cuda(), scale=s)
+    torch.cuda.synchronize()
+    assert ("values_reduce" in res) == (splits > 1)
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), s, False)
     ok, a, r = within_bar(to_f64(o), ref)
-    _report(f"key split x{splits} L={L} d={d}", a, r)
-    assert ok
+    _report(f"key split x{splits} B={B} L={L} d={d}", a, r)
+    assert ok and r <= REL_RMS_BAND, (a, r)
+
+
+@pytest.mark.parametrize("H,L,d,causal", [(1, 1100, 256, False), (1, 1000, 320, False),
+                                           (1, 2100, 512, False), (2, 700, 192, False),
+                                           (1, 1300, 448, True), (1, 129, 192, False),
+                                           (1, 64, 1024, False), (1, 4096, 1024, False),
+                                           (3, 600, 1024, True)])
+def test_values_narrow_tiles(H, L, d, causal):
+    """Few heads: the values pass runs on 128 x 128 tiles, one round, no key
+    split (ragged query tiles whose far half is idle, channel tiles half past d,
+    one partial tile, exactly 256 tiles), with the LSE."""
+    from exact_softmax_attention_bf16_amd import attention, kernel_timing
+    q, k, v = make_qkv(1, H, L, d, 40 + L + d)
+    s = 1.0 / math.sqrt(d)
+    res = {}
+    with kernel_timing(res):
+        o, lse = attention(q.cuda(), k.cuda(), v.cuda(), scale=s, causal=causal, return_lse=True)
+    torch.cuda.synchronize()
+    assert set(res) == {"scores", "values"}
+    ref = oracle.attention(to_f64(q), to_f64(k), to_f64(v), s, causal)
+    ok, a, r = within_bar(to_f64(o), ref)
+    _report(f"narrow tiles H={H} L={L} d={d} causal={causal}", a, r)
+    assert ok and r <= REL_RMS_BAND, (a, r)
+    lref = oracle.log_sum_exp(to_f64(q), to_f64(k), s, causal)
+    err = np.abs(to_f64(lse) - lref)
+    assert bool((err <= 4e-3 + 1e-5 * np.abs(lref)).all()), float(err.max())
 
 
 def test_workspace_grows_and_is_reused_on_one_stream():

@@ -3,7 +3,8 @@ attn_forward's (the entry point it is a variant of) and the oracle, on two calls
 in a row with the second smaller, for each path that draws scratch memory:
 the large-head-dim two passes (exponentials and statistics; several chunks of
 heads when they do not fit the fixed array at once; the values pass's key
-split, dropped when its shares do not fit) and the online path's key split.
+split, dropped when its shares do not fit; its 128 x 128 tiles for one head)
+and the online path's key split.
 """
 import ctypes
 import math
@@ -36,7 +37,8 @@ def call(fn, q, k, v, out, scale, causal):
 # (B, H, L, d, causal): first call, then a smaller second call
 PAIRS = [
     ((6, 1, 3432, 1024, False), (1, 1, 1000, 512, False)),   # 6 frames: two chunks of heads
-    ((1, 1, 3432, 1024, False), (1, 1, 700, 256, True)),     # one frame: split needs 82 MB
+    ((1, 1, 3432, 1024, False), (1, 1, 700, 256, True)),     # one frame: 128 x 128 values tiles
+    ((2, 1, 3432, 1024, False), (1, 1, 1000, 512, False)),   # two frames: split shares 56 MB
     ((1, 1, 4096, 64, False), (1, 1, 1000, 128, True)),      # online key split
     ((2, 1, 2000, 768, True), (1, 2, 300, 192, False)),
     ((1, 1, 6500, 1024, False), (1, 1, 3000, 1024, False)),  # split's shares do not fit: dropped

@@ -101,9 +101,11 @@ enum {
  * gives its size).  For d > 128 the call uses the
  * workspace buffer the library keeps for (current device, stream), growing it
  * when needed (about 16384*ceil(L/32)*ceil(L/256) + 8*L*ceil(L/128) bytes per
- * head, heads processed in chunks of at most 2 GiB; when so few heads would
- * leave most compute units idle, also up to 4 fp32 copies of the output for
- * a split over the keys -- attn_workspace_bytes gives the exact figure).
+ * head, heads processed in chunks of at most 2 GiB).  When so few heads would
+ * leave most compute units idle, the values pass runs on 128 x 128 tiles if
+ * they fit the compute units in one round, and otherwise splits the keys,
+ * adding up to 3 fp32 copies of the output to the workspace
+ * (attn_workspace_bytes gives the exact figure).
  * Neither growing nor reusing the buffer waits on the host (see the thread
  * safety note above).
  */

@@ -30,7 +30,8 @@
 // Masks are bands of keys per query (causal, or a sliding window): both passes
 // visit only the tiles a query tile's band meets.  Operands are found through
 // a head map (strides, key/value head groups), so packed and strided layouts
-// are read in place.
+// are read in place.  For few heads the values pass runs on 128 x 128 tiles,
+// or splits the keys and sums fp32 shares in a third kernel.
 #include <algorithm>
 #include <atomic>
 #include <cstddef>

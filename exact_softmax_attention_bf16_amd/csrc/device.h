@@ -56,6 +56,10 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, void* ds
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) as an immediate for __builtin_amdgcn_s_waitcnt (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the other
+// two at their maxima): a wait the compiler's own wait tracking sees.
+constexpr int kWaitVmem0 = 0x0f70;
 
 // The four words of the buffer resource make_rsrc builds (read from lane 0),
 // for load16_to_lds_untracked.

@@ -364,7 +364,11 @@ __global__ __launch_bounds__(64 * QW * G) void online_attn_kernel(const uint16_t
            (!HAS_LEFT || kbase + kBN - 1 >= q0 - left);
   };
   if (g < ntiles) issue(t0 + g, 0);
-  wait_vmem();
+  // A wait the compiler sees (not an asm one), so that it knows the Q
+  // fragments have arrived: otherwise it waits for them again before each
+  // block's first MFMAs, and that wait also holds for the next block's loads,
+  // which are counted alongside.
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   __syncthreads();
   for (int it = 0; it < niter; ++it) {
     const int t = t0 + g + G * it;
